@@ -1,0 +1,181 @@
+/*
+ * Float64 CPU oracle for biased, windowed paged attention.
+ *
+ * TEST INFRASTRUCTURE ONLY: used by the tests, the smoke check and the
+ * benchmark's CPU baseline, never by the product path. It shares no code,
+ * header or table with the HIP library. Semantics and layouts are documented
+ * in oracle.h.
+ *
+ * Every row is computed the slow, obvious way: walk the visible keys in
+ * ascending logical position, fetch each key and value through the block
+ * table, form the score (q.k + a) * scale in float64, then take the softmax
+ * weighted average of the values. No blocking, no online softmax, no reuse.
+ * Build: gcc -O2 -fopenmp (never -ffast-math).
+ */
+#include "oracle.h"
+
+#include <math.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+/* Element i of an fp32 (dtype 0) or bf16 (dtype 1) array, widened exactly to
+ * float64. A bf16 value is the upper half of the fp32 bit pattern. */
+static double elem(const void* base, int64_t i, int32_t dtype) {
+  if (dtype == 0) return (double)((const float*)base)[i];
+  uint32_t bits = (uint32_t)((const uint16_t*)base)[i] << 16;
+  float f;
+  memcpy(&f, &bits, sizeof f);
+  return (double)f;
+}
+
+/* Offset of element (token j, dim 0) of head h in a paged cache, found
+ * through the block table row `table` (logical block j / block_size). */
+static int64_t kv_offset(const int32_t* table, int32_t j, int32_t h, int32_t num_heads,
+                         int32_t block_size, int32_t head_dim) {
+  int64_t phys = table[j / block_size];
+  int64_t slot = j % block_size;
+  return ((phys * num_heads + h) * block_size + slot) * head_dim;
+}
+
+/* Whether key j is visible to a query at logical position p: the key must be
+ * one of the L cached tokens; with a window W >= 1 it must satisfy
+ * |p - j| < W; a causal query also needs j <= p. */
+static int visible(int32_t p, int32_t j, int32_t L, int32_t window, int32_t causal) {
+  if (j < 0 || j >= L) return 0;
+  if (causal && j > p) return 0;
+  if (window > 0) {
+    int32_t d = p > j ? p - j : j - p;
+    if (d >= window) return 0;
+  }
+  return 1;
+}
+
+/* One attention row: query vector q_row (offset q_off into q), keys of the
+ * sequence whose block-table row is `table`, bias row `bias_row` indexed by
+ * key position (NULL = no bias). Writes head_dim values to out_row.
+ * `s` is scratch for L scores. */
+static void attend_row(double* out_row, const void* q, int64_t q_off, const void* k_cache,
+                       const void* v_cache, const int32_t* table, const float* bias_row,
+                       int32_t p, int32_t L, int32_t window, int32_t causal, double scale,
+                       int32_t h, int32_t num_heads, int32_t head_dim, int32_t block_size,
+                       int32_t dtype, double* s) {
+  for (int32_t d = 0; d < head_dim; ++d) out_row[d] = 0.0;
+  double m = -INFINITY;
+  for (int32_t j = 0; j < L; ++j) {
+    s[j] = -INFINITY;
+    if (!visible(p, j, L, window, causal)) continue;
+    int64_t ko = kv_offset(table, j, h, num_heads, block_size, head_dim);
+    double dot = 0.0;
+    for (int32_t d = 0; d < head_dim; ++d)
+      dot += elem(q, q_off + d, dtype) * elem(k_cache, ko + d, dtype);
+    double a = bias_row ? (double)bias_row[j] : 0.0;
+    s[j] = (dot + a) * scale;
+    if (s[j] > m) m = s[j];
+  }
+  if (L <= 0 || m == -INFINITY) return; /* empty or fully masked row: 0 */
+  double z = 0.0;
+  for (int32_t j = 0; j < L; ++j) {
+    if (s[j] == -INFINITY) continue;
+    double w = exp(s[j] - m);
+    z += w;
+    int64_t vo = kv_offset(table, j, h, num_heads, block_size, head_dim);
+    for (int32_t d = 0; d < head_dim; ++d) out_row[d] += w * elem(v_cache, vo + d, dtype);
+  }
+  for (int32_t d = 0; d < head_dim; ++d) out_row[d] /= z;
+}
+
+static int bad_scalars(int32_t num_seqs, int32_t num_heads, int32_t head_dim,
+                       int32_t block_size, int32_t max_blocks_per_seq, int32_t max_seq_len,
+                       int32_t sliding_window, int32_t dtype) {
+  if (num_seqs < 0 || num_heads < 1 || head_dim < 1 || block_size < 1) return 1;
+  if (max_blocks_per_seq < 0 || max_seq_len < 0) return 1;
+  if (sliding_window == 0 || sliding_window < -1) return 1;
+  if (dtype != 0 && dtype != 1) return 1;
+  if ((int64_t)max_blocks_per_seq * block_size < max_seq_len) return 1;
+  return 0;
+}
+
+int oracle_decode_f64(double* out, const void* q, const void* k_cache, const void* v_cache,
+                      const int32_t* block_tables, const int32_t* context_lens,
+                      const float* attn_bias, int32_t sliding_window, double scale,
+                      int32_t num_seqs, int32_t num_heads, int32_t head_dim,
+                      int32_t block_size, int32_t max_blocks_per_seq, int32_t max_seq_len,
+                      int32_t dtype) {
+  if (bad_scalars(num_seqs, num_heads, head_dim, block_size, max_blocks_per_seq, max_seq_len,
+                  sliding_window, dtype))
+    return -1;
+  for (int32_t b = 0; b < num_seqs; ++b)
+    if (context_lens[b] < 0 || context_lens[b] > max_seq_len) return -1;
+  int64_t pairs = (int64_t)num_seqs * num_heads;
+#pragma omp parallel
+  {
+    double* s = (double*)malloc(sizeof(double) * (size_t)(max_seq_len > 0 ? max_seq_len : 1));
+#pragma omp for schedule(dynamic, 1)
+    for (int64_t bh = 0; bh < pairs; ++bh) {
+      int32_t b = (int32_t)(bh / num_heads), h = (int32_t)(bh % num_heads);
+      int32_t L = context_lens[b];
+      const float* bias_row =
+          attn_bias ? attn_bias + ((int64_t)b * num_heads + h) * max_seq_len : NULL;
+      /* the decode query is the newest token, at position L - 1 */
+      attend_row(out + bh * head_dim, q, bh * head_dim, k_cache, v_cache,
+                 block_tables + (int64_t)b * max_blocks_per_seq, bias_row, L - 1, L,
+                 sliding_window, 0, scale, h, num_heads, head_dim, block_size, dtype, s);
+    }
+    free(s);
+  }
+  return 0;
+}
+
+int oracle_prefill_f64(double* out, const void* q, const void* k_cache, const void* v_cache,
+                       const int32_t* block_tables, const int32_t* context_lens,
+                       const int32_t* query_start_loc, const float* attn_bias,
+                       int32_t sliding_window, int32_t causal, double scale,
+                       int32_t num_seqs, int32_t num_heads, int32_t head_dim,
+                       int32_t block_size, int32_t max_blocks_per_seq, int32_t max_seq_len,
+                       int32_t dtype) {
+  if (bad_scalars(num_seqs, num_heads, head_dim, block_size, max_blocks_per_seq, max_seq_len,
+                  sliding_window, dtype))
+    return -1;
+  if (causal != 0 && causal != 1) return -1;
+  for (int32_t b = 0; b < num_seqs; ++b) {
+    int32_t nq = query_start_loc[b + 1] - query_start_loc[b];
+    if (context_lens[b] < 0 || context_lens[b] > max_seq_len || nq < 0 || nq > context_lens[b])
+      return -1;
+  }
+  int64_t pairs = (int64_t)num_seqs * num_heads;
+#pragma omp parallel
+  {
+    double* s = (double*)malloc(sizeof(double) * (size_t)(max_seq_len > 0 ? max_seq_len : 1));
+#pragma omp for schedule(dynamic, 1)
+    for (int64_t bh = 0; bh < pairs; ++bh) {
+      int32_t b = (int32_t)(bh / num_heads), h = (int32_t)(bh % num_heads);
+      int32_t L = context_lens[b];
+      int32_t q0 = query_start_loc[b];
+      int32_t nq = query_start_loc[b + 1] - q0;
+      for (int32_t t = 0; t < nq; ++t) {
+        int32_t p = L - nq + t; /* queries are the last nq positions */
+        int64_t row = ((int64_t)(q0 + t) * num_heads + h) * head_dim;
+        const float* bias_row =
+            attn_bias
+                ? attn_bias + (((int64_t)b * num_heads + h) * max_seq_len + p) * max_seq_len
+                : NULL;
+        attend_row(out + row, q, row, k_cache, v_cache,
+                   block_tables + (int64_t)b * max_blocks_per_seq, bias_row, p, L,
+                   sliding_window, causal, scale, h, num_heads, head_dim, block_size, dtype, s);
+      }
+    }
+    free(s);
+  }
+  return 0;
+}
+
+int oracle_num_threads(void) {
+#ifdef _OPENMP
+  return omp_get_max_threads();
+#else
+  return 1;
+#endif
+}

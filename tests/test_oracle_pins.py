@@ -1,0 +1,347 @@
+"""Pins for the float64 oracle (CPU only).
+
+The oracle is trusted only because these checks tie it to things it does not
+compute itself:
+
+* PyTorch's float64 ``scaled_dot_product_attention`` applied to K/V that the
+  test un-pages with plain tensor indexing, with the additive mask
+  ``scale * A + M`` (M = 0 or -inf from the window / causal definition). This
+  pins the whole formula of "PagedAttention: Support custom attention bias for
+  T5 model" (attention equation in the PR description), the gather through
+  the block table, bias indexing, windows and query positions.
+* Hand-worked closed forms whose expected value is derived in the comments.
+* Special cases: L = 1, W = 1, W >= L, empty and fully masked rows, a null
+  bias equal to a zero bias, a constant bias equal to none, relabelled
+  physical blocks, and a bias "probe" that isolates one key.
+
+Each check is chosen so that a plausible slip in the oracle (dropping the bias,
+adding it after the scale, a wrong block/slot/head index, a transposed bias
+index, an off-by-one window edge, a reversed causal mask, a wrong prefill
+query position) fails at least one of them.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+import torch.nn.functional as F
+
+import oracle
+import workloads
+
+BS = workloads.BLOCK_SIZE
+
+
+# ----------------------------------------------------------------------------
+# helpers (test side, independent of the oracle)
+# ----------------------------------------------------------------------------
+def unpage(cache, table, L):
+    """Dense [H, L, D] float64 tensor of one sequence's cache rows."""
+    j = torch.arange(L)
+    phys = table[j // BS].long()
+    slot = j % BS
+    return cache[phys, :, slot, :].permute(1, 0, 2).double()
+
+
+def window_mask(pos, L, window, causal):
+    """Additive mask [len(pos), L]: 0 where key j is visible to position p."""
+    p = torch.as_tensor(pos, dtype=torch.long)[:, None]
+    j = torch.arange(L)[None, :]
+    ok = torch.ones(p.shape[0], L, dtype=torch.bool)
+    if causal:
+        ok &= j <= p
+    if window > 0:
+        ok &= (p - j).abs() < window
+    m = torch.zeros(ok.shape, dtype=torch.float64)
+    m[~ok] = float("-inf")
+    return m
+
+
+def sdpa_decode(case):
+    """Library cross-check of decode: SDPA(q, K, V, mask = scale*A + M)."""
+    B, H, D = case.q.shape
+    out = torch.zeros(B, H, D, dtype=torch.float64)
+    for b in range(B):
+        L = int(case.lens[b])
+        if L == 0:
+            continue
+        K = unpage(case.k_cache, case.block_tables[b], L)
+        V = unpage(case.v_cache, case.block_tables[b], L)
+        M = window_mask([L - 1], L, case.sliding_window, False)          # [1, L]
+        mask = M.expand(H, 1, L).clone()
+        if case.attn_bias is not None:
+            mask = mask + case.scale * case.attn_bias[b, :, :L].double()[:, None, :]
+        qb = case.q[b].double()[:, None, :]                                  # [H,1,D]
+        out[b] = F.scaled_dot_product_attention(qb, K, V, attn_mask=mask,
+                                                scale=case.scale)[:, 0, :]
+    return out.numpy()
+
+
+def sdpa_prefill(case):
+    TQ, H, D = case.q.shape
+    out = torch.zeros(TQ, H, D, dtype=torch.float64)
+    qsl = case.query_start_loc
+    for b in range(case.num_seqs):
+        L = int(case.lens[b])
+        q0, q1 = int(qsl[b]), int(qsl[b + 1])
+        nq = q1 - q0
+        if nq == 0:
+            continue
+        pos = list(range(L - nq, L))
+        K = unpage(case.k_cache, case.block_tables[b], L)
+        V = unpage(case.v_cache, case.block_tables[b], L)
+        M = window_mask(pos, L, case.sliding_window, case.causal)           # [nq, L]
+        mask = M[None].expand(H, nq, L).clone()
+        if case.attn_bias is not None:
+            mask = mask + case.scale * case.attn_bias[b][:, pos, :L].double()
+        qb = case.q[q0:q1].double().permute(1, 0, 2)                        # [H,nq,D]
+        out[q0:q1] = F.scaled_dot_product_attention(qb, K, V, attn_mask=mask,
+                                                    scale=case.scale).permute(1, 0, 2)
+    return out.numpy()
+
+
+def run_decode(case, bias="case", window=None):
+    return oracle.decode(case.q, case.k_cache, case.v_cache, case.block_tables,
+                         case.context_lens, case.attn_bias if bias == "case" else bias,
+                         case.sliding_window if window is None else window, case.scale,
+                         case.max_seq_len)
+
+
+def run_prefill(case, bias="case", window=None):
+    return oracle.prefill(case.q, case.k_cache, case.v_cache, case.block_tables,
+                          case.context_lens, case.query_start_loc,
+                          case.attn_bias if bias == "case" else bias,
+                          case.sliding_window if window is None else window,
+                          int(case.causal), case.scale, case.max_seq_len)
+
+
+def small_decode(seed, dtype=torch.float32, bias="normal", window=-1, lens=(1, 40), H=3,
+                 D=8, B=4, max_seq_len=48, scale=None):
+    return workloads.decode_case(seed, num_seqs=B, num_heads=H, head_dim=D, lens=lens,
+                                 max_seq_len=max_seq_len, dtype=dtype, bias=bias,
+                                 sliding_window=window, scale=scale)
+
+
+def small_prefill(seed, dtype=torch.float32, bias="normal", window=-1, causal=False,
+                  lens=(1, 40), q_lens=None, H=2, D=8, B=3, max_seq_len=48):
+    return workloads.prefill_case(seed, num_seqs=B, num_heads=H, head_dim=D, lens=lens,
+                                  max_seq_len=max_seq_len, dtype=dtype, bias=bias,
+                                  sliding_window=window, causal=causal, q_lens=q_lens)
+
+
+# ----------------------------------------------------------------------------
+# library cross-check
+# ----------------------------------------------------------------------------
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+@pytest.mark.parametrize("bias", ["normal", None, "t5"])
+@pytest.mark.parametrize("window", [-1, 1, 5, 16, 17, 100])
+def test_decode_equals_sdpa(dtype, bias, window):
+    case = small_decode(11 + window, dtype=dtype, bias=bias, window=window, lens=(1, 45),
+                        scale=0.3)
+    np.testing.assert_allclose(run_decode(case), sdpa_decode(case), rtol=0, atol=1e-12)
+
+
+def test_decode_equals_sdpa_d64_fixed_pool():
+    case = workloads.tiny_decode_f32()
+    np.testing.assert_allclose(run_decode(case), sdpa_decode(case), rtol=0, atol=1e-12)
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("window", [-1, 1, 3, 16, 33])
+@pytest.mark.parametrize("bias", ["normal", None])
+def test_prefill_equals_sdpa(dtype, causal, window, bias):
+    case = small_prefill(21 + window, dtype=dtype, bias=bias, window=window, causal=causal)
+    np.testing.assert_allclose(run_prefill(case), sdpa_prefill(case), rtol=0, atol=1e-12)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_prefill_partial_queries_equals_sdpa(causal):
+    # fewer queries than keys: they sit at the last n_q positions
+    case = small_prefill(31, bias="normal", window=7, causal=causal, lens=[30, 17, 5],
+                         q_lens=[4, 17, 1])
+    np.testing.assert_allclose(run_prefill(case), sdpa_prefill(case), rtol=0, atol=1e-12)
+
+
+def test_prefill_asymmetric_bias_index():
+    # bias[b,h,i,j] with i = query position, j = key position: transposing it
+    # must change the result (so the SDPA check above really pins the order)
+    case = small_prefill(41, bias="normal", lens=[20, 9, 33])
+    ref = run_prefill(case)
+    tb = case.attn_bias.transpose(2, 3).contiguous()
+    assert np.max(np.abs(run_prefill(case, bias=tb) - ref)) > 1e-3
+
+
+# ----------------------------------------------------------------------------
+# hand-worked closed forms
+# ----------------------------------------------------------------------------
+def hand_case(k_rows, v_rows, q, bias_row, scale, window=-1):
+    """One sequence, one head, D=2, keys scattered over a 4-block pool in the
+    order table = [2, 0, 3] (so logical block 0 is physical block 2)."""
+    L = len(k_rows)
+    table = np.array([[2, 0, 3]], np.int32)
+    k = np.full((4, 1, BS, 2), np.nan, np.float32)
+    v = np.full((4, 1, BS, 2), np.nan, np.float32)
+    for j in range(L):
+        k[table[0, j // BS], 0, j % BS] = k_rows[j]
+        v[table[0, j // BS], 0, j % BS] = v_rows[j]
+    bias = None
+    if bias_row is not None:
+        bias = np.full((1, 1, 48), np.nan, np.float32)
+        bias[0, 0, :L] = bias_row
+    return oracle.decode(np.array([[q]], np.float32), k, v, table,
+                         np.array([L], np.int32), bias, window, scale, 48)[0, 0]
+
+
+def test_hand_bias_added_before_scale():
+    # Two keys with q.k = 0 for both, bias (0, 2), scale 1/2. Adding the bias
+    # before the 1/sqrt(d_k) factor gives scores (0, 1): weights 1 : e.
+    # (Adding it after would give (0, 2): weights 1 : e^2.)
+    v0, v1 = np.array([1.0, -2.0]), np.array([3.0, 5.0])
+    got = hand_case([[0, 1], [0, -1]], [v0, v1], [1, 0], [0.0, 2.0], 0.5)
+    want = (v0 + math.e * v1) / (1 + math.e)
+    np.testing.assert_allclose(got, want, rtol=0, atol=1e-15)
+
+
+def test_hand_dot_product_and_gather():
+    # 20 keys across two physical blocks (2 then 0). q = (1, 2), k_j = (j, -j)
+    # so q.k_j = -j; the bias a_j = j cancels it exactly: all scores equal,
+    # and the output is the plain mean of the values v_j = (j, j^2).
+    L = 20
+    k = [[j, -j] for j in range(L)]
+    v = [[j, j * j] for j in range(L)]
+    got = hand_case(k, v, [1, 2], [float(j) for j in range(L)], 0.7)
+    want = np.array([np.mean(np.arange(L)), np.mean(np.arange(L) ** 2)])
+    np.testing.assert_allclose(got, want, rtol=0, atol=1e-12)
+
+
+def test_hand_window_keeps_last_w():
+    # Same equal-score set-up with window 5: the decode query at position 19
+    # sees keys 15..19 only, so the output is the mean of v_15..v_19.
+    L = 20
+    k = [[j, -j] for j in range(L)]
+    v = [[j, j * j] for j in range(L)]
+    got = hand_case(k, v, [1, 2], [float(j) for j in range(L)], 0.7, window=5)
+    js = np.arange(15, 20)
+    np.testing.assert_allclose(got, [js.mean(), (js ** 2).mean()], rtol=0, atol=1e-12)
+
+
+def test_hand_sign_of_dot_product():
+    # No bias, scale 1, keys k_0 = (0,0), k_1 = (1,0) and q = (ln 3, 0):
+    # scores (0, ln 3): weights 1 : 3, out = (v0 + 3 v1) / 4.
+    v0, v1 = np.array([4.0, 0.0]), np.array([0.0, 8.0])
+    q = [np.float32(math.log(3.0)), 0.0]
+    got = hand_case([[0, 0], [1, 0]], [v0, v1], q, None, 1.0)
+    w1 = math.exp(float(np.float32(math.log(3.0))))
+    np.testing.assert_allclose(got, (v0 + w1 * v1) / (1 + w1), rtol=0, atol=1e-15)
+
+
+# ----------------------------------------------------------------------------
+# special cases
+# ----------------------------------------------------------------------------
+def test_single_token_returns_its_value():
+    case = small_decode(51, lens=[1, 1, 1, 1])
+    out = run_decode(case)
+    for b in range(4):
+        v0 = case.v_cache[case.block_tables[b, 0].long(), :, 0, :].double().numpy()
+        np.testing.assert_array_equal(out[b], v0)
+
+
+def test_window_one_returns_newest_value():
+    case = small_decode(52, window=1, lens=(2, 45))
+    out = run_decode(case)
+    for b in range(4):
+        j = int(case.lens[b]) - 1
+        vj = case.v_cache[case.block_tables[b, j // BS].long(), :, j % BS, :].double().numpy()
+        np.testing.assert_array_equal(out[b], vj)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_prefill_window_one_returns_own_value(causal):
+    case = small_prefill(53, window=1, causal=causal)
+    out = run_prefill(case)
+    for b in range(case.num_seqs):
+        q0 = int(case.query_start_loc[b])
+        for t in range(int(case.lens[b])):
+            vt = case.v_cache[case.block_tables[b, t // BS].long(), :, t % BS, :]
+            np.testing.assert_array_equal(out[q0 + t], vt.double().numpy())
+
+
+def test_window_at_least_length_equals_no_window():
+    case = small_decode(54, lens=(1, 40))
+    ref = run_decode(case, window=-1)
+    for w in (40, 41, 1000):
+        np.testing.assert_array_equal(run_decode(case, window=w), ref)
+    pc = small_prefill(55, lens=(1, 40), causal=False)
+    pref = run_prefill(pc, window=-1)
+    np.testing.assert_array_equal(run_prefill(pc, window=40), pref)
+
+
+def test_null_bias_equals_zero_bias_bit_exact():
+    case = small_decode(56, bias="zero")
+    np.testing.assert_array_equal(run_decode(case, bias=None), run_decode(case))
+    pc = small_prefill(57, bias=None)
+    zero = torch.zeros(pc.num_seqs, pc.num_heads, pc.max_seq_len, pc.max_seq_len)
+    np.testing.assert_array_equal(run_prefill(pc, bias=zero), run_prefill(pc))
+
+
+def test_constant_bias_equals_no_bias():
+    case = small_decode(58, bias=None)
+    c = torch.full((4, 3, 48), 3.75)
+    np.testing.assert_allclose(run_decode(case, bias=c), run_decode(case), rtol=0, atol=1e-12)
+
+
+def test_empty_and_fully_masked_rows_are_zero():
+    case = small_decode(59, lens=[0, 5, 17, 3])
+    bias = torch.zeros(4, 3, 48)
+    bias[2] = float("-inf")         # every score of sequence 2 is -inf
+    out = run_decode(case, bias=bias)
+    assert np.all(out[0] == 0) and np.all(out[2] == 0)
+    assert np.all(np.isfinite(out))
+
+
+def test_block_relabelling_is_bit_exact():
+    case = small_decode(60, lens=(10, 45))
+    ref = run_decode(case)
+    nb = case.num_blocks
+    perm = torch.from_numpy(np.random.default_rng(7).permutation(nb))
+    inv = torch.argsort(perm)
+    # physical block p moves to slot inv[p]
+    k2 = case.k_cache[perm]
+    v2 = case.v_cache[perm]
+    t2 = inv[case.block_tables.long()].int()
+    out = oracle.decode(case.q, k2, v2, t2, case.context_lens, case.attn_bias, -1,
+                        case.scale, case.max_seq_len)
+    np.testing.assert_array_equal(out, ref)
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+def test_bias_probe_isolates_one_key(dtype):
+    # bias -1e4 everywhere except 0 at one key j*: exp of the gap is exactly 0
+    # in float64, so out = v_{j*} exactly.
+    case = small_decode(61, dtype=dtype, bias=None, lens=[37, 37, 37, 37])
+    for js in (0, 15, 16, 31, 36):
+        bias = torch.full((4, 3, 48), -1e4)
+        bias[:, :, js] = 0.0
+        out = run_decode(case, bias=bias)
+        for b in range(4):
+            vj = case.v_cache[case.block_tables[b, js // BS].long(), :, js % BS, :]
+            np.testing.assert_array_equal(out[b], vj.double().numpy())
+
+
+def test_poisoned_slots_are_never_read():
+    for seed in range(3):
+        case = small_decode(70 + seed, lens=(1, 45), window=7)
+        assert torch.isnan(case.k_cache).any()
+        assert np.all(np.isfinite(run_decode(case)))
+        pc = small_prefill(80 + seed, window=5)
+        assert np.all(np.isfinite(run_prefill(pc)))
+
+
+def test_oracle_rejects_bad_scalars():
+    case = small_decode(90)
+    with pytest.raises(ValueError):
+        run_decode(case, window=0)
+    with pytest.raises(ValueError):
+        oracle.decode(case.q, case.k_cache, case.v_cache, case.block_tables,
+                      case.context_lens, None, -1, 1.0, 8)       # L > max_seq_len
