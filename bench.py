@@ -1,0 +1,296 @@
+"""Benchmark of biased paged-attention decode on one MI355X.
+
+Default workload: the large biased decode (256 sequences x 32 heads,
+head_dim 128, bf16 q/K/V, fp32 bias [256,32,4096], L ~ U[1024,4096], random
+block permutation). One step = one paged_attn_decode call = one decode step of
+one attention layer for all 256 sequences; throughput is decode tokens/s
+(sequences served per second) and the achieved HBM bandwidth of the call.
+
+Prints ONE JSON line. Options:
+  --gpus N        only 1 is supported (the path runs on one GPU)
+  --steps K       timed steps (default 20)
+  --warmup W      untimed warm-up steps (default 5)
+  --workload X    large_biased_decode_bf16 (default) | modernbert_prefill_f32 |
+                  copy_probe (a plain device copy of known size, for
+                  calibrating the rocprofv3 byte counters)
+  --no-cpu-baseline   skip the oracle timing
+  --no-variants       skip the window / null-bias / no-bias-build variants
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import sliding_window_mask_amd as pa  # noqa: E402
+import workloads  # noqa: E402
+
+METRIC = "decode tokens/s and achieved HBM GB/s (% of MI355X peak), biased paged attn"
+HBM_PEAK_GBPS = 8000.0
+FP32_MFMA_PEAK_TFLOPS = 157.3
+PROFILES = os.path.join(ROOT, "profiles")
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def source_sha(name):
+    p = os.path.join(ROOT, "sliding_window_mask_amd", "csrc", name)
+    return hashlib.sha256(open(p, "rb").read()).hexdigest()[:16]
+
+
+def read_traffic(workload, kernel_src):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if it
+    was taken on the current kernel source; otherwise None."""
+    path = os.path.join(PROFILES, "%s_traffic.txt" % workload)
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    for ln in open(path):
+        if "=" in ln and not ln.startswith("#"):
+            k, v = ln.split("=", 1)
+            kv[k.strip()] = v.strip()
+    if kv.get("kernel_source_sha") != source_sha(kernel_src):
+        return None
+    try:
+        return float(kv["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def time_steps(fn, steps, warmup):
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    start.record()
+    for _ in range(steps):
+        fn()
+    end.record()
+    torch.cuda.synchronize()
+    return start.elapsed_time(end) / steps          # ms per step
+
+
+# ----------------------------------------------------------------------------
+# decode
+# ----------------------------------------------------------------------------
+def decode_bytes(lens, H, D, esize, window, with_bias):
+    """Algorithmic HBM bytes of one decode call: for every (sequence, head)
+    the visible tokens' K and V rows (2*D*e bytes) and bias entries (4 bytes),
+    plus the q read and out write (2*D*e). Block-table and length reads
+    (< 0.1%) are not counted."""
+    L = lens.astype(np.int64)
+    n_vis = np.minimum(L, window) if window > 0 else L
+    per_tok = 2 * D * esize + (4 if with_bias else 0)
+    return int(H * np.sum(n_vis * per_tok + 2 * D * esize))
+
+
+def compact_sample(case, seqs):
+    """Host copies of the inputs of a subset of sequences, with a compact cache
+    holding only the blocks they reference (for the oracle)."""
+    idx = torch.as_tensor(seqs, dtype=torch.long, device=case.block_tables.device)
+    bt = case.block_tables[idx].cpu()
+    used = torch.unique(bt)
+    remap = torch.full((case.num_blocks,), -1, dtype=torch.int32)
+    remap[used] = torch.arange(used.numel(), dtype=torch.int32)
+    dev_used = used.to(case.k_cache.device)
+    return dict(q=case.q[idx].cpu(), k=case.k_cache[dev_used].cpu(),
+                v=case.v_cache[dev_used].cpu(), bt=remap[bt.long()],
+                cl=case.context_lens[idx].cpu(),
+                bias=None if case.attn_bias is None else case.attn_bias[idx].cpu())
+
+
+def cpu_baseline_decode(case, out_gpu):
+    """Time the float64 oracle (as it stands) on a bounded sample of the same
+    workload; also report the GPU-vs-oracle error on that sample."""
+    import oracle
+    oracle.build(force=False)
+    rng = np.random.default_rng(12345)
+
+    def run(n):
+        seqs = np.sort(rng.choice(case.num_seqs, size=n, replace=False))
+        s = compact_sample(case, seqs)
+        t0 = time.perf_counter()
+        ref = oracle.decode(s["q"], s["k"], s["v"], s["bt"], s["cl"], s["bias"],
+                            case.sliding_window, case.scale, case.max_seq_len)
+        dt = time.perf_counter() - t0
+        g = out_gpu[torch.as_tensor(seqs, device=out_gpu.device)].float().cpu().double().numpy()
+        return n, dt, float(np.max(np.abs(g - ref))), seqs
+
+    n, dt, _, _ = run(4)                                  # rate estimate
+    target_s = 15.0
+    n = int(min(case.num_seqs, max(4, math.floor(target_s / max(dt / n, 1e-6)))))
+    n, dt, err, seqs = run(n)
+    return {"value": n / dt, "unit": "tokens/s", "cores": oracle.num_threads(),
+            "kind": "oracle",
+            "sample": "%d of the %d sequences (all 32 heads, their full contexts), "
+                      "float64 C loop over the block table, %.1f s" % (n, case.num_seqs, dt),
+            "gpu_vs_oracle_max_abs_err_on_sample": err}
+
+
+def bench_decode(args):
+    t0 = time.time()
+    case = workloads.large_biased_decode_bf16(device="cuda")
+    torch.cuda.synchronize()
+    log("inputs ready in %.1f s (%d blocks)" % (time.time() - t0, case.num_blocks))
+    B, H, D = case.q.shape
+    lib = pa.lib()
+    out = torch.empty_like(case.q)
+    P = lib.pa_decode_default_partition(B, H, D, case.max_seq_len, case.sliding_window)
+    ws = lib.workspace_for(case.q, case.max_seq_len, case.sliding_window)
+
+    def step(window=-1, bias="case", which=lib, o=out, w=ws):
+        which.paged_attn_decode(case.q, case.k_cache, case.v_cache, case.block_tables,
+                                case.context_lens, case.attn_bias if bias == "case" else bias,
+                                window, case.scale, max_seq_len=case.max_seq_len, out=o,
+                                workspace=w)
+
+    ms = time_steps(step, args.steps, args.warmup)
+    nbytes = decode_bytes(case.lens, H, D, 2, -1, True)
+    gbps = nbytes / (ms * 1e-3) / 1e9
+    tokens_per_s = B / (ms * 1e-3)
+    log("decode: %.4f ms/step, %.0f tokens/s, %.1f GB/s" % (ms, tokens_per_s, gbps))
+    traffic = read_traffic("decode_large_biased_bf16", "pa_decode.hip")
+    line = {
+        "metric": METRIC, "value": tokens_per_s, "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "large_biased_decode_bf16", "num_seqs": B, "num_heads": H,
+                   "head_dim": D, "block_size": 16, "context_lens": "uniform [1024, 4096]",
+                   "num_blocks": case.num_blocks, "max_seq_len": case.max_seq_len,
+                   "attn_bias": "fp32 [256, 32, 4096] N(0,1)", "sliding_window": -1,
+                   "partition_tokens": P, "parallelism": "single GPU"},
+        "achieved_GBps": gbps,
+        "algorithmic_bytes_per_step": nbytes,
+        "roofline": {"bound": "hbm", "achieved": gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": gbps / HBM_PEAK_GBPS,
+                     "traffic": traffic,
+                     "kernel": "paged_attn_decode call (pa_decode_partition + pa_decode_merge)"},
+    }
+    if not args.no_variants:
+        var = {}
+        msw = time_steps(lambda: step(window=1024), args.steps, args.warmup)
+        bw = decode_bytes(case.lens, H, D, 2, 1024, True)
+        var["window_1024"] = {"ms_per_step": msw, "tokens_per_s": B / (msw * 1e-3),
+                              "GBps": bw / (msw * 1e-3) / 1e9}
+        msn = time_steps(lambda: step(bias=None), args.steps, args.warmup)
+        bn = decode_bytes(case.lens, H, D, 2, -1, False)
+        var["null_bias"] = {"ms_per_step": msn, "tokens_per_s": B / (msn * 1e-3),
+                            "GBps": bn / (msn * 1e-3) / 1e9}
+        if os.path.exists(pa.LIB_NOBIAS_PATH):
+            nob = pa.PagedAttnLib(pa.LIB_NOBIAS_PATH)
+            msb = time_steps(lambda: step(bias=None, which=nob), args.steps, args.warmup)
+            var["null_bias_in_no_bias_build"] = {"ms_per_step": msb,
+                                                 "tokens_per_s": B / (msb * 1e-3),
+                                                 "GBps": bn / (msb * 1e-3) / 1e9}
+            var["null_bias_slowdown_vs_no_bias_build"] = msn / msb - 1.0
+        line["variants"] = var
+        log("variants: %s" % json.dumps(var))
+    if not args.no_cpu_baseline:
+        step()
+        torch.cuda.synchronize()
+        line["cpu_baseline"] = cpu_baseline_decode(case, out)
+    return line
+
+
+# ----------------------------------------------------------------------------
+# prefill (12-layer ModernBERT-shaped encoder)
+# ----------------------------------------------------------------------------
+def prefill_flops(lens, H, D, window):
+    L = lens.astype(np.int64)
+    if window > 0:
+        W = np.minimum(window, L)
+        pairs = L * (2 * W - 1) - W * (W - 1)
+    else:
+        pairs = L * L
+    return int(4 * D * H * np.sum(pairs))
+
+
+def bench_prefill(args):
+    layers = [workloads.modernbert_prefill_f32(l, device="cuda")
+              for l in range(workloads.MODERNBERT_LAYERS)]
+    torch.cuda.synchronize()
+    outs = [torch.empty_like(c.q) for c in layers]
+    lib = pa.lib()
+
+    def step():
+        for c, o in zip(layers, outs):
+            lib.paged_attn_prefill(c.q, c.k_cache, c.v_cache, c.block_tables, c.context_lens,
+                                   c.query_start_loc, None, c.sliding_window, False, c.scale,
+                                   max_seq_len=c.max_seq_len, out=o)
+
+    ms = time_steps(step, args.steps, args.warmup)
+    c0 = layers[0]
+    flops = sum(prefill_flops(c.lens, 12, 64, c.sliding_window) for c in layers)
+    tflops = flops / (ms * 1e-3) / 1e12
+    tokens = int(c0.lens.sum())
+    line = {
+        "metric": "encoder prefill tokens/s (12 layers) and MFMA TFLOP/s", "value":
+        tokens / (ms * 1e-3), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "config": {"workload": "modernbert_prefill_f32", "layers": 12, "num_seqs": 32,
+                   "num_heads": 12, "head_dim": 64, "context_lens": "uniform [64, 1024]",
+                   "windows": [workloads.modernbert_window(l) for l in range(12)]},
+        "roofline": {"bound": "mfma", "achieved": tflops, "peak": FP32_MFMA_PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "frac": tflops / FP32_MFMA_PEAK_TFLOPS,
+                     "traffic": None, "kernel": "pa_prefill_f32 (12 launches per step)"},
+        "algorithmic_flops_per_step": flops,
+    }
+    return line
+
+
+def bench_copy(args):
+    """A plain device-to-device copy of known size (256 MiB read + 256 MiB
+    written per launch), used to calibrate the rocprofv3 byte counters."""
+    n = 256 << 20
+    src = torch.empty(n, dtype=torch.uint8, device="cuda").random_(0, 255)
+    dst = torch.empty_like(src)
+    ms = time_steps(lambda: dst.copy_(src), args.steps, args.warmup)
+    return {"metric": "copy probe GB/s", "value": 2 * n / (ms * 1e-3) / 1e9, "unit": "GB/s",
+            "bytes_read_per_launch": n, "bytes_written_per_launch": n, "ms_per_step": ms,
+            "steps": args.steps, "warmup": args.warmup, "n_gpus": 1}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="large_biased_decode_bf16")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-variants", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py runs on one GPU only: the paged-attention path is measured on a "
+              "single MI355X (--gpus 1).", file=sys.stderr)
+        sys.exit(2)
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    if args.workload == "large_biased_decode_bf16":
+        line = bench_decode(args)
+    elif args.workload == "modernbert_prefill_f32":
+        line = bench_prefill(args)
+    elif args.workload == "copy_probe":
+        line = bench_copy(args)
+    else:
+        raise SystemExit("unknown workload %s" % args.workload)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,176 @@
+/*
+ * paged_attn.h — C ABI of the MI355X (gfx950) biased, windowed paged-attention
+ * library (libpaged_attn.so).
+ *
+ * The library computes, per query row,
+ *     out = softmax((q K^T + A) * scale) V,
+ * the attention-with-additive-bias formula of "[Kernel][Model] PagedAttention:
+ * Support custom attention bias for T5 model (1/2)" (vllm-project/vllm#11334,
+ * PR description), with `scale` standing for 1/sqrt(d_k). A is an optional,
+ * fully materialised fp32 bias padded to max_seq_len (same PR description);
+ * a NULL bias pointer is a no-op (same page, review answer on whether the bias
+ * is materialised when unused). Keys and values are read through a block
+ * table; cross-attention simply passes the encoder's block table ("Add
+ * Encoder-decoder model support and T5 Model support", vllm-project/vllm#3117,
+ * the thread that settles on separate self- and cross-attention block tables).
+ * The optional sliding window follows "[V1] Add sliding window support to Flex
+ * Attention backend" (vllm-project/vllm#24089).
+ *
+ * Scores, masks and positions (readings where the pages are silent):
+ *   s_j = (q . k_j + a_j) * scale          (bias added before the scale)
+ *   a query at logical position p sees key j iff  0 <= j < L  and, when
+ *   sliding_window = W >= 1, |p - j| < W; a causal query also needs j <= p.
+ *   Decode: the query is at p = L - 1. Prefill: the n_q queries of a sequence
+ *   are at p = L - n_q .. L - 1 (n_q = L for an encoder: query t at t).
+ *   A row with L = 0, or whose every score is -inf, outputs 0.
+ *
+ * Layouts (all row-major, all device memory owned by the caller):
+ *   k_cache, v_cache  [num_blocks, num_kv_heads, block_size, head_dim], dtype
+ *   block_tables      int32 [num_seqs, max_blocks_per_seq]; entry n is the
+ *                     physical block of logical tokens 16n .. 16n+15. Entries
+ *                     that back no visible token are never read (table
+ *                     padding, and with a window the blocks wholly before it).
+ *   context_lens      int32 [num_seqs], 0 <= L <= max_seq_len
+ *   attn_bias         fp32, decode [num_seqs, num_heads, max_seq_len],
+ *                     prefill [num_seqs, num_heads, max_seq_len, max_seq_len],
+ *                     indexed by logical positions; entries of keys that are
+ *                     not visible are never read. NULL = no bias.
+ *
+ * Conventions of every entry point:
+ *   - returns a pa_status_t; never aborts or throws; pa_last_error() gives a
+ *     message for the last non-OK status of the calling thread;
+ *   - scalar arguments, pointer nullness and alignment are validated on the
+ *     host BEFORE any HIP call; the contents of device arrays (lengths, table
+ *     entries) are not validated unless the environment variable
+ *     PA_VALIDATE=1 is set, in which case they are copied to the host
+ *     (synchronously) and range-checked first;
+ *   - work is enqueued asynchronously on `stream` (a hipStream_t; NULL = the
+ *     default stream); device faults surface at the caller's next sync;
+ *   - the library allocates nothing and keeps no state between calls; calls
+ *     on different streams with distinct outputs/workspaces may overlap.
+ */
+#ifndef PAGED_ATTN_H
+#define PAGED_ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define PA_ABI_VERSION 1
+
+typedef enum { PA_DTYPE_F32 = 0, PA_DTYPE_BF16 = 1 } pa_dtype_t;
+
+typedef enum {
+  PA_OK = 0,
+  PA_ERR_NULL_POINTER = 1, /* a required pointer is NULL                        */
+  PA_ERR_INVALID_ARG = 2,  /* a scalar is out of range / PA_VALIDATE found bad data */
+  PA_ERR_UNSUPPORTED = 3,  /* valid but not implemented (head_dim, block_size ...) */
+  PA_ERR_MISALIGNED = 4,   /* q/k/v/out not 16-byte aligned, bias not 4-byte     */
+  PA_ERR_WORKSPACE = 5,    /* decode workspace missing or too small              */
+  PA_ERR_HIP = 6           /* a HIP runtime call or kernel launch failed          */
+} pa_status_t;
+
+/* PA_ABI_VERSION of the built library. */
+int pa_abi_version(void);
+
+/* Thread-local message describing the last non-OK status ("" if none). */
+const char* pa_last_error(void);
+
+/* Partition length (tokens, a multiple of 16) the decode path uses when
+ * partition_tokens = 0 is passed, for this problem shape. */
+int32_t pa_decode_default_partition(int32_t num_seqs, int32_t num_heads, int32_t head_dim,
+                                    int32_t max_seq_len, int32_t sliding_window,
+                                    pa_dtype_t dtype);
+
+/* Bytes of device workspace paged_attn_decode needs for this shape and
+ * partition length (0 = the default partition). 0 means no workspace is
+ * needed (every sequence fits one partition). Returns 0 also for invalid
+ * arguments; paged_attn_decode reports those. */
+size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_heads, int32_t head_dim,
+                                 int32_t max_seq_len, int32_t sliding_window,
+                                 int32_t partition_tokens, pa_dtype_t dtype);
+
+/*
+ * Decode attention: one query per (sequence, head), at position L-1, for
+ * decoder self-attention (the sequence's own table) or cross-attention (the
+ * encoder table and encoder lengths, sliding_window = -1). See the header
+ * comment for the formula and visibility rule.
+ *
+ *   out            [num_seqs, num_heads, head_dim], dtype (written)
+ *   q              [num_seqs, num_heads, head_dim], dtype
+ *   k_cache/v_cache, block_tables, context_lens, attn_bias: see above
+ *                  (attn_bias [num_seqs, num_heads, max_seq_len] or NULL)
+ *   sliding_window -1 (off) or >= 1: the W newest tokens stay visible
+ *   scale          finite; normally 1/sqrt(head_dim)
+ *   num_kv_heads   must equal num_heads in this version
+ *   head_dim       64 or 128;  block_size  16
+ *   max_blocks_per_seq * 16 >= max_seq_len
+ *   num_blocks     rows of the caches (used by PA_VALIDATE only)
+ *   dtype          PA_DTYPE_F32 or PA_DTYPE_BF16 for q, caches and out
+ *   partition_tokens  0 = default; else a multiple of 16 in [16, 4096]: the
+ *                  split-K partition length (each partition is one workgroup;
+ *                  a second kernel merges partitions in a fixed order)
+ *   workspace      device memory of >= pa_decode_workspace_bytes(...) bytes,
+ *                  256-byte aligned; may be NULL when that size is 0. Its
+ *                  contents need no initialisation and are scratch.
+ *   stream         hipStream_t or NULL
+ * Errors: NULL_POINTER, INVALID_ARG, UNSUPPORTED, MISALIGNED, WORKSPACE, HIP.
+ * num_seqs == 0 returns PA_OK without launching anything.
+ */
+pa_status_t paged_attn_decode(void* out, const void* q, const void* k_cache,
+                              const void* v_cache, const int32_t* block_tables,
+                              const int32_t* context_lens, const float* attn_bias,
+                              int32_t sliding_window, float scale, int32_t num_seqs,
+                              int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
+                              int32_t block_size, int32_t max_blocks_per_seq,
+                              int32_t max_seq_len, int64_t num_blocks, pa_dtype_t dtype,
+                              int32_t partition_tokens, void* workspace,
+                              size_t workspace_bytes, void* stream);
+
+/*
+ * Prefill attention over packed queries, for bidirectional encoder-only
+ * attention (causal = 0; n_q = L per sequence) or causal decoder prompts
+ * (causal = 1). Uses MFMA for both contractions.
+ *
+ *   out             [total_q, num_heads, head_dim], dtype (written)
+ *   q               [total_q, num_heads, head_dim], dtype
+ *   query_start_loc int32 [num_seqs + 1], non-decreasing, query_start_loc[0]
+ *                   = 0, query_start_loc[num_seqs] = total_q; sequence b owns
+ *                   rows query_start_loc[b] .. query_start_loc[b+1]-1 and
+ *                   0 <= n_q <= L must hold
+ *   attn_bias       [num_seqs, num_heads, max_seq_len, max_seq_len] fp32, or NULL
+ *   causal          0 or 1
+ *   dtype           PA_DTYPE_F32 or PA_DTYPE_BF16
+ *   Other arguments as for paged_attn_decode. No workspace is needed.
+ * Errors: NULL_POINTER, INVALID_ARG, UNSUPPORTED, MISALIGNED, HIP.
+ */
+pa_status_t paged_attn_prefill(void* out, const void* q, const void* k_cache,
+                               const void* v_cache, const int32_t* block_tables,
+                               const int32_t* context_lens, const int32_t* query_start_loc,
+                               const float* attn_bias, int32_t sliding_window, int32_t causal,
+                               float scale, int32_t num_seqs, int32_t num_heads,
+                               int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                               int32_t max_blocks_per_seq, int32_t max_seq_len,
+                               int64_t num_blocks, int64_t total_q, pa_dtype_t dtype,
+                               void* stream);
+
+/*
+ * Host-side range check of decode/prefill metadata held in HOST memory (the
+ * check PA_VALIDATE=1 runs on copies): every L in [0, max_seq_len], every
+ * block-table entry that backs a visible token in [0, num_blocks), and, when
+ * query_start_loc is not NULL, 0 = qsl[0] <= ... <= qsl[num_seqs] = total_q
+ * with 0 <= n_q <= L. Returns PA_OK or PA_ERR_INVALID_ARG (message in
+ * pa_last_error()). Makes no HIP call.
+ */
+pa_status_t pa_check_metadata(const int32_t* block_tables, const int32_t* context_lens,
+                              const int32_t* query_start_loc, int32_t sliding_window,
+                              int32_t causal, int32_t num_seqs, int32_t max_blocks_per_seq,
+                              int32_t max_seq_len, int64_t num_blocks, int64_t total_q);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* PAGED_ATTN_H */

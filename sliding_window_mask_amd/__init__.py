@@ -1,0 +1,209 @@
+"""Python binding of libpaged_attn.so (biased, windowed paged attention on MI355X).
+
+Argument marshalling only: every step of the computation runs in the HIP
+kernels behind the C ABI declared in ``include/paged_attn.h``. PyTorch is used
+for device memory and streams; tensors are passed as raw pointers together
+with the current HIP stream. There is no CPU or PyTorch fallback: if the
+library is not built, or a call fails, an exception is raised.
+
+Functions mirror the C entry points:
+  paged_attn_decode(...)         decoder self-attention / cross-attention decode
+  paged_attn_prefill(...)        encoder-only (bidirectional) or causal prefill
+  pa_decode_workspace_bytes(...)
+  pa_decode_default_partition(...)
+  pa_check_metadata(...)         host-side range check of lengths / tables
+  pa_abi_version()
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libpaged_attn.so")
+LIB_NOBIAS_PATH = os.path.join(_HERE, "libpaged_attn_nobias.so")
+
+PA_DTYPE_F32 = 0
+PA_DTYPE_BF16 = 1
+STATUS = {0: "PA_OK", 1: "PA_ERR_NULL_POINTER", 2: "PA_ERR_INVALID_ARG",
+          3: "PA_ERR_UNSUPPORTED", 4: "PA_ERR_MISALIGNED", 5: "PA_ERR_WORKSPACE",
+          6: "PA_ERR_HIP"}
+
+
+class PagedAttnError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__("%s: %s" % (STATUS.get(status, status), message))
+        self.status = status
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.float32:
+        return PA_DTYPE_F32
+    if t.dtype == torch.bfloat16:
+        return PA_DTYPE_BF16
+    raise TypeError("paged attention supports float32 and bfloat16, got %s" % t.dtype)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    if stream is None:
+        return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    if isinstance(stream, torch.cuda.Stream):
+        return ctypes.c_void_p(stream.cuda_stream)
+    return ctypes.c_void_p(int(stream))
+
+
+class PagedAttnLib:
+    """One loaded copy of the library (the product build or the no-bias build)."""
+
+    def __init__(self, path: str = LIB_PATH):
+        if not os.path.exists(path):
+            raise RuntimeError(
+                "%s is not built; run `python -c 'import __graft_entry__ as g; g.build()'`"
+                % path)
+        self.path = path
+        lib = ctypes.CDLL(path)
+        P, I32, I64, F32, SZ = (ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64,
+                                ctypes.c_float, ctypes.c_size_t)
+        lib.pa_abi_version.restype = ctypes.c_int
+        lib.pa_abi_version.argtypes = []
+        lib.pa_last_error.restype = ctypes.c_char_p
+        lib.pa_last_error.argtypes = []
+        lib.pa_decode_default_partition.restype = I32
+        lib.pa_decode_default_partition.argtypes = [I32, I32, I32, I32, I32, ctypes.c_int]
+        lib.pa_decode_workspace_bytes.restype = SZ
+        lib.pa_decode_workspace_bytes.argtypes = [I32, I32, I32, I32, I32, I32, ctypes.c_int]
+        lib.paged_attn_decode.restype = ctypes.c_int
+        lib.paged_attn_decode.argtypes = [P, P, P, P, P, P, P, I32, F32, I32, I32, I32, I32,
+                                          I32, I32, I32, I64, ctypes.c_int, I32, P, SZ, P]
+        lib.paged_attn_prefill.restype = ctypes.c_int
+        lib.paged_attn_prefill.argtypes = [P, P, P, P, P, P, P, P, I32, I32, F32, I32, I32,
+                                           I32, I32, I32, I32, I32, I64, I64, ctypes.c_int, P]
+        lib.pa_check_metadata.restype = ctypes.c_int
+        lib.pa_check_metadata.argtypes = [P, P, P, I32, I32, I32, I32, I32, I64, I64]
+        self._lib = lib
+
+    # -- small queries ------------------------------------------------------
+    def pa_abi_version(self) -> int:
+        return int(self._lib.pa_abi_version())
+
+    def pa_last_error(self) -> str:
+        return self._lib.pa_last_error().decode()
+
+    def _check(self, st: int) -> None:
+        if st != 0:
+            raise PagedAttnError(st, self.pa_last_error())
+
+    def pa_decode_default_partition(self, num_seqs, num_heads, head_dim, max_seq_len,
+                                    sliding_window, dtype=PA_DTYPE_BF16) -> int:
+        return int(self._lib.pa_decode_default_partition(num_seqs, num_heads, head_dim,
+                                                         max_seq_len, sliding_window, dtype))
+
+    def pa_decode_workspace_bytes(self, num_seqs, num_heads, head_dim, max_seq_len,
+                                  sliding_window, partition_tokens=0,
+                                  dtype=PA_DTYPE_BF16) -> int:
+        return int(self._lib.pa_decode_workspace_bytes(num_seqs, num_heads, head_dim,
+                                                       max_seq_len, sliding_window,
+                                                       partition_tokens, dtype))
+
+    def pa_check_metadata(self, block_tables, context_lens, query_start_loc, sliding_window,
+                          causal, max_seq_len, num_blocks, total_q=0) -> None:
+        """Range-check host (CPU) int32 tensors; raises PagedAttnError."""
+        for t in (block_tables, context_lens, query_start_loc):
+            if t is not None and (t.device.type != "cpu" or t.dtype != torch.int32
+                                  or not t.is_contiguous()):
+                raise TypeError("pa_check_metadata takes contiguous CPU int32 tensors")
+        self._check(self._lib.pa_check_metadata(
+            _ptr(block_tables), _ptr(context_lens), _ptr(query_start_loc),
+            int(sliding_window), int(causal), context_lens.shape[0], block_tables.shape[1],
+            int(max_seq_len), int(num_blocks), int(total_q)))
+
+    # -- entry points -------------------------------------------------------
+    def workspace_for(self, q, max_seq_len, sliding_window, partition_tokens=0):
+        """Allocate (torch) the decode workspace a call with these shapes needs."""
+        B, H, D = q.shape
+        n = self.pa_decode_workspace_bytes(B, H, D, max_seq_len, sliding_window,
+                                           partition_tokens, _dtype_code(q))
+        if n == 0:
+            return None
+        return torch.empty(n, dtype=torch.uint8, device=q.device)
+
+    def paged_attn_decode(self, q, k_cache, v_cache, block_tables, context_lens, attn_bias,
+                          sliding_window, scale, *, max_seq_len, out=None, workspace=None,
+                          partition_tokens=0, stream=None):
+        """Decode attention for q [B,H,D]; returns out [B,H,D] (q's dtype).
+
+        k_cache, v_cache [num_blocks,H,16,D]; block_tables int32 [B,max_blocks];
+        context_lens int32 [B]; attn_bias fp32 [B,H,max_seq_len] or None.
+        Cross-attention: pass the encoder table and lengths, sliding_window -1."""
+        B, H, D = q.shape
+        if out is None:
+            out = torch.empty_like(q)
+        if workspace is None:
+            workspace = self.workspace_for(q, max_seq_len, sliding_window, partition_tokens)
+        ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+        self._check(self._lib.paged_attn_decode(
+            _ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables),
+            _ptr(context_lens), _ptr(attn_bias), int(sliding_window), float(scale), B, H,
+            k_cache.shape[1], D, k_cache.shape[2], block_tables.shape[1], int(max_seq_len),
+            k_cache.shape[0], _dtype_code(q), int(partition_tokens), _ptr(workspace), ws_bytes,
+            _stream(stream)))
+        return out
+
+    def paged_attn_prefill(self, q, k_cache, v_cache, block_tables, context_lens,
+                           query_start_loc, attn_bias, sliding_window, causal, scale, *,
+                           max_seq_len, out=None, stream=None):
+        """Prefill attention for packed q [total_q,H,D]; returns out like q.
+
+        query_start_loc int32 [B+1]; attn_bias fp32 [B,H,max_seq_len,max_seq_len]
+        or None; causal False for encoder-only bidirectional attention."""
+        TQ, H, D = q.shape
+        if out is None:
+            out = torch.empty_like(q)
+        self._check(self._lib.paged_attn_prefill(
+            _ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables),
+            _ptr(context_lens), _ptr(query_start_loc), _ptr(attn_bias), int(sliding_window),
+            int(bool(causal)), float(scale), context_lens.shape[0], H, k_cache.shape[1], D,
+            k_cache.shape[2], block_tables.shape[1], int(max_seq_len), k_cache.shape[0], TQ,
+            _dtype_code(q), _stream(stream)))
+        return out
+
+
+_default = None
+
+
+def lib() -> PagedAttnLib:
+    """The product library (loaded once)."""
+    global _default
+    if _default is None:
+        _default = PagedAttnLib(LIB_PATH)
+    return _default
+
+
+def paged_attn_decode(*args, **kwargs):
+    return lib().paged_attn_decode(*args, **kwargs)
+
+
+def paged_attn_prefill(*args, **kwargs):
+    return lib().paged_attn_prefill(*args, **kwargs)
+
+
+def pa_decode_workspace_bytes(*args, **kwargs):
+    return lib().pa_decode_workspace_bytes(*args, **kwargs)
+
+
+def pa_decode_default_partition(*args, **kwargs):
+    return lib().pa_decode_default_partition(*args, **kwargs)
+
+
+def pa_check_metadata(*args, **kwargs):
+    return lib().pa_check_metadata(*args, **kwargs)
+
+
+def pa_abi_version():
+    return lib().pa_abi_version()

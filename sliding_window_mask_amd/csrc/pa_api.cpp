@@ -1,0 +1,338 @@
+// Host side of the C ABI declared in include/paged_attn.h: argument
+// validation (before any HIP call), partition sizing, workspace carving,
+// optional range checks of device metadata, and kernel dispatch.
+#include "paged_attn.h"
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <vector>
+
+#include "pa_internal.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+pa_status_t fail(pa_status_t st, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof g_err, fmt, ap);
+  va_end(ap);
+  return st;
+}
+
+pa_status_t ok() {
+  g_err[0] = '\0';
+  return PA_OK;
+}
+
+bool aligned(const void* p, size_t n) { return (reinterpret_cast<uintptr_t>(p) % n) == 0; }
+
+// Tokens a decode partition grid must cover per sequence: every visible token
+// plus the part of the first block before the window.
+int32_t decode_span(int32_t max_seq_len, int32_t window) {
+  if (window > 0 && (int64_t)window + pa::kBlockSize - 1 < max_seq_len)
+    return window + pa::kBlockSize - 1;
+  return max_seq_len;
+}
+
+int32_t round_up16(int32_t x) { return (x + pa::kBlockSize - 1) / pa::kBlockSize * pa::kBlockSize; }
+
+int32_t default_partition(int32_t num_seqs, int32_t num_heads, int32_t max_seq_len,
+                          int32_t window) {
+  const int32_t span = decode_span(max_seq_len, window);
+  const int64_t pairs = (int64_t)num_seqs * num_heads;
+  // Aim for >= 2048 workgroups (8 per CU); never shorter than 128 tokens.
+  int32_t P = 512;
+  while (P > 128 && pairs * ((span + P - 1) / P) < 2048) P /= 2;
+  if (span <= P) P = span > 0 ? round_up16(span) : pa::kBlockSize;  // one partition
+  return P;
+}
+
+struct DecodePlan {
+  int32_t partition;
+  int32_t num_partitions;
+  size_t ws_bytes;
+  size_t off_m, off_l;   // byte offsets of the m and l arrays (o starts at 0)
+};
+
+DecodePlan plan_decode(int32_t num_seqs, int32_t num_heads, int32_t head_dim,
+                       int32_t max_seq_len, int32_t window, int32_t partition) {
+  DecodePlan p{};
+  p.partition = partition > 0 ? partition : default_partition(num_seqs, num_heads, max_seq_len,
+                                                               window);
+  const int32_t span = decode_span(max_seq_len, window);
+  p.num_partitions = span > 0 ? (span + p.partition - 1) / p.partition : 1;
+  if (p.num_partitions <= 1) {
+    p.num_partitions = 1;
+    p.ws_bytes = 0;
+    return p;
+  }
+  const size_t rows = (size_t)num_seqs * num_heads * p.num_partitions;
+  auto up256 = [](size_t x) { return (x + 255) / 256 * 256; };
+  p.off_m = up256(rows * head_dim * sizeof(float));
+  p.off_l = p.off_m + up256(rows * sizeof(float));
+  p.ws_bytes = p.off_l + up256(rows * sizeof(float));
+  return p;
+}
+
+pa_status_t check_common(const void* out, const void* q, const void* k, const void* v,
+                         const int32_t* bt, const int32_t* cl, const float* bias,
+                         int32_t window, float scale, int32_t num_seqs, int32_t num_heads,
+                         int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                         int32_t max_blocks, int32_t max_seq_len, int64_t num_blocks,
+                         pa_dtype_t dtype) {
+  if (dtype != PA_DTYPE_F32 && dtype != PA_DTYPE_BF16)
+    return fail(PA_ERR_UNSUPPORTED, "dtype %d is not supported (0 = fp32, 1 = bf16)", (int)dtype);
+  if (head_dim != 64 && head_dim != 128)
+    return fail(PA_ERR_UNSUPPORTED, "head_dim %d is not supported (64 or 128)", head_dim);
+  if (block_size != pa::kBlockSize)
+    return fail(PA_ERR_UNSUPPORTED, "block_size %d is not supported (16)", block_size);
+  if (num_heads < 1 || num_heads > 65535)
+    return fail(PA_ERR_INVALID_ARG, "num_heads %d out of range [1, 65535]", num_heads);
+  if (num_kv_heads != num_heads)
+    return fail(PA_ERR_UNSUPPORTED, "num_kv_heads (%d) must equal num_heads (%d)", num_kv_heads,
+                num_heads);
+  if (num_seqs < 0 || num_seqs > 65535)
+    return fail(PA_ERR_INVALID_ARG, "num_seqs %d out of range [0, 65535]", num_seqs);
+  if (max_seq_len < 0 || max_blocks < 0 || num_blocks < 0)
+    return fail(PA_ERR_INVALID_ARG, "negative size (max_seq_len %d, max_blocks_per_seq %d, "
+                "num_blocks %lld)", max_seq_len, max_blocks, (long long)num_blocks);
+  if ((int64_t)max_blocks * pa::kBlockSize < max_seq_len)
+    return fail(PA_ERR_INVALID_ARG, "max_blocks_per_seq * 16 (%lld) < max_seq_len (%d)",
+                (long long)max_blocks * pa::kBlockSize, max_seq_len);
+  if (window == 0 || window < -1)
+    return fail(PA_ERR_INVALID_ARG, "sliding_window %d: use -1 (off) or >= 1", window);
+  if (!std::isfinite(scale)) return fail(PA_ERR_INVALID_ARG, "scale is not finite");
+  if (num_seqs == 0) return PA_OK;
+  if (!out || !q || !k || !v || !bt || !cl)
+    return fail(PA_ERR_NULL_POINTER, "a required pointer is NULL (out %p q %p k %p v %p "
+                "block_tables %p context_lens %p)", out, q, k, v, (const void*)bt,
+                (const void*)cl);
+  if (!aligned(out, 16) || !aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16))
+    return fail(PA_ERR_MISALIGNED, "out, q, k_cache and v_cache must be 16-byte aligned");
+  if (!aligned(bt, 4) || !aligned(cl, 4) || (bias && !aligned(bias, 4)))
+    return fail(PA_ERR_MISALIGNED, "block_tables, context_lens and attn_bias must be 4-byte "
+                "aligned");
+  return PA_OK;
+}
+
+bool validate_env() {
+  const char* e = std::getenv("PA_VALIDATE");
+  return e && e[0] && std::strcmp(e, "0") != 0;
+}
+
+pa_status_t validate_device(const int32_t* bt, const int32_t* cl, const int32_t* qsl,
+                            int32_t window, int32_t causal, int32_t num_seqs, int32_t max_blocks,
+                            int32_t max_seq_len, int64_t num_blocks, int64_t total_q,
+                            hipStream_t stream) {
+  std::vector<int32_t> hbt((size_t)num_seqs * max_blocks), hcl(num_seqs), hqsl;
+  hipError_t e = hipMemcpyAsync(hcl.data(), cl, sizeof(int32_t) * num_seqs,
+                                hipMemcpyDeviceToHost, stream);
+  if (e == hipSuccess && !hbt.empty())
+    e = hipMemcpyAsync(hbt.data(), bt, sizeof(int32_t) * hbt.size(), hipMemcpyDeviceToHost,
+                       stream);
+  if (e == hipSuccess && qsl) {
+    hqsl.resize(num_seqs + 1);
+    e = hipMemcpyAsync(hqsl.data(), qsl, sizeof(int32_t) * hqsl.size(), hipMemcpyDeviceToHost,
+                       stream);
+  }
+  if (e == hipSuccess) e = hipStreamSynchronize(stream);
+  if (e != hipSuccess)
+    return fail(PA_ERR_HIP, "PA_VALIDATE copy failed: %s", hipGetErrorString(e));
+  return pa_check_metadata(hbt.data(), hcl.data(), qsl ? hqsl.data() : nullptr, window, causal,
+                           num_seqs, max_blocks, max_seq_len, num_blocks, total_q);
+}
+
+}  // namespace
+
+extern "C" {
+
+int pa_abi_version(void) { return PA_ABI_VERSION; }
+
+const char* pa_last_error(void) { return g_err; }
+
+int32_t pa_decode_default_partition(int32_t num_seqs, int32_t num_heads, int32_t head_dim,
+                                    int32_t max_seq_len, int32_t sliding_window,
+                                    pa_dtype_t dtype) {
+  (void)head_dim;
+  (void)dtype;
+  if (num_seqs < 0 || num_heads < 1 || max_seq_len < 0) return 0;
+  return default_partition(num_seqs, num_heads, max_seq_len, sliding_window);
+}
+
+size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_heads, int32_t head_dim,
+                                 int32_t max_seq_len, int32_t sliding_window,
+                                 int32_t partition_tokens, pa_dtype_t dtype) {
+  (void)dtype;
+  if (num_seqs < 0 || num_heads < 1 || head_dim < 1 || max_seq_len < 0) return 0;
+  if (partition_tokens < 0 || partition_tokens % pa::kBlockSize != 0 ||
+      partition_tokens > pa::kMaxPartition)
+    return 0;
+  return plan_decode(num_seqs, num_heads, head_dim, max_seq_len, sliding_window,
+                     partition_tokens).ws_bytes;
+}
+
+pa_status_t pa_check_metadata(const int32_t* block_tables, const int32_t* context_lens,
+                              const int32_t* query_start_loc, int32_t sliding_window,
+                              int32_t causal, int32_t num_seqs, int32_t max_blocks_per_seq,
+                              int32_t max_seq_len, int64_t num_blocks, int64_t total_q) {
+  (void)causal;
+  if (num_seqs < 0) return fail(PA_ERR_INVALID_ARG, "num_seqs < 0");
+  if (num_seqs > 0 && (!context_lens || (max_blocks_per_seq > 0 && !block_tables)))
+    return fail(PA_ERR_NULL_POINTER, "metadata pointer is NULL");
+  if (query_start_loc) {
+    if (query_start_loc[0] != 0)
+      return fail(PA_ERR_INVALID_ARG, "query_start_loc[0] = %d, expected 0", query_start_loc[0]);
+    if (query_start_loc[num_seqs] != total_q)
+      return fail(PA_ERR_INVALID_ARG, "query_start_loc[%d] = %d, expected total_q = %lld",
+                  num_seqs, query_start_loc[num_seqs], (long long)total_q);
+  }
+  for (int32_t b = 0; b < num_seqs; ++b) {
+    const int32_t L = context_lens[b];
+    if (L < 0 || L > max_seq_len)
+      return fail(PA_ERR_INVALID_ARG, "context_lens[%d] = %d outside [0, %d]", b, L, max_seq_len);
+    int32_t first_pos = L - 1;   // decode: the one query
+    if (query_start_loc) {
+      const int32_t nq = query_start_loc[b + 1] - query_start_loc[b];
+      if (nq < 0 || nq > L)
+        return fail(PA_ERR_INVALID_ARG, "sequence %d has %d queries for %d keys", b, nq, L);
+      if (nq == 0) continue;
+      first_pos = L - nq;
+    }
+    if (L == 0) continue;
+    int32_t lo = 0;
+    if (sliding_window > 0 && first_pos - sliding_window + 1 > 0)
+      lo = first_pos - sliding_window + 1;
+    for (int32_t n = lo / pa::kBlockSize; n < (L + pa::kBlockSize - 1) / pa::kBlockSize; ++n) {
+      const int32_t id = block_tables[(int64_t)b * max_blocks_per_seq + n];
+      if (id < 0 || id >= num_blocks)
+        return fail(PA_ERR_INVALID_ARG, "block_tables[%d][%d] = %d outside [0, %lld)", b, n, id,
+                    (long long)num_blocks);
+    }
+  }
+  return ok();
+}
+
+pa_status_t paged_attn_decode(void* out, const void* q, const void* k_cache,
+                              const void* v_cache, const int32_t* block_tables,
+                              const int32_t* context_lens, const float* attn_bias,
+                              int32_t sliding_window, float scale, int32_t num_seqs,
+                              int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
+                              int32_t block_size, int32_t max_blocks_per_seq,
+                              int32_t max_seq_len, int64_t num_blocks, pa_dtype_t dtype,
+                              int32_t partition_tokens, void* workspace,
+                              size_t workspace_bytes, void* stream) {
+  pa_status_t st = check_common(out, q, k_cache, v_cache, block_tables, context_lens, attn_bias,
+                                sliding_window, scale, num_seqs, num_heads, num_kv_heads,
+                                head_dim, block_size, max_blocks_per_seq, max_seq_len,
+                                num_blocks, dtype);
+  if (st != PA_OK) return st;
+  if (partition_tokens < 0 || partition_tokens % pa::kBlockSize != 0 ||
+      partition_tokens > pa::kMaxPartition)
+    return fail(PA_ERR_INVALID_ARG, "partition_tokens %d: use 0 or a multiple of 16 in "
+                "[16, %d]", partition_tokens, pa::kMaxPartition);
+  if (num_seqs == 0) return ok();
+  const DecodePlan plan = plan_decode(num_seqs, num_heads, head_dim, max_seq_len,
+                                      sliding_window, partition_tokens);
+  if (plan.num_partitions > 65535)
+    return fail(PA_ERR_INVALID_ARG, "too many partitions (%d)", plan.num_partitions);
+  if (plan.ws_bytes > 0) {
+    if (!workspace || workspace_bytes < plan.ws_bytes)
+      return fail(PA_ERR_WORKSPACE, "decode workspace of %zu bytes needed, %zu given (%p)",
+                  plan.ws_bytes, workspace_bytes, workspace);
+    if (!aligned(workspace, 256))
+      return fail(PA_ERR_MISALIGNED, "workspace must be 256-byte aligned");
+  }
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (validate_env()) {
+    st = validate_device(block_tables, context_lens, nullptr, sliding_window, 0, num_seqs,
+                         max_blocks_per_seq, max_seq_len, num_blocks, 0, s);
+    if (st != PA_OK) return st;
+  }
+  pa::DecodeArgs a{};
+  a.out = out;
+  a.q = q;
+  a.k_cache = k_cache;
+  a.v_cache = v_cache;
+  a.block_tables = block_tables;
+  a.context_lens = context_lens;
+  a.attn_bias = attn_bias;
+  a.window = sliding_window;
+  a.scale_log2 = (float)((double)scale * 1.4426950408889634074);
+  a.num_seqs = num_seqs;
+  a.num_heads = num_heads;
+  a.head_dim = head_dim;
+  a.max_blocks = max_blocks_per_seq;
+  a.max_seq_len = max_seq_len;
+  a.dtype = (int32_t)dtype;
+  a.partition = plan.partition;
+  a.num_partitions = plan.num_partitions;
+  if (plan.ws_bytes > 0) {
+    char* ws = static_cast<char*>(workspace);
+    a.ws_o = reinterpret_cast<float*>(ws);
+    a.ws_m = reinterpret_cast<float*>(ws + plan.off_m);
+    a.ws_l = reinterpret_cast<float*>(ws + plan.off_l);
+  }
+  hipError_t e = pa::launch_decode(a, s);
+  if (e != hipSuccess) return fail(PA_ERR_HIP, "decode launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
+pa_status_t paged_attn_prefill(void* out, const void* q, const void* k_cache,
+                               const void* v_cache, const int32_t* block_tables,
+                               const int32_t* context_lens, const int32_t* query_start_loc,
+                               const float* attn_bias, int32_t sliding_window, int32_t causal,
+                               float scale, int32_t num_seqs, int32_t num_heads,
+                               int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                               int32_t max_blocks_per_seq, int32_t max_seq_len,
+                               int64_t num_blocks, int64_t total_q, pa_dtype_t dtype,
+                               void* stream) {
+  pa_status_t st = check_common(out, q, k_cache, v_cache, block_tables, context_lens, attn_bias,
+                                sliding_window, scale, num_seqs, num_heads, num_kv_heads,
+                                head_dim, block_size, max_blocks_per_seq, max_seq_len,
+                                num_blocks, dtype);
+  if (st != PA_OK) return st;
+  if (causal != 0 && causal != 1) return fail(PA_ERR_INVALID_ARG, "causal must be 0 or 1");
+  if (total_q < 0 || total_q > INT32_MAX)
+    return fail(PA_ERR_INVALID_ARG, "total_q %lld out of range", (long long)total_q);
+  if (num_seqs == 0) return ok();
+  if (!query_start_loc) return fail(PA_ERR_NULL_POINTER, "query_start_loc is NULL");
+  if (!aligned(query_start_loc, 4))
+    return fail(PA_ERR_MISALIGNED, "query_start_loc must be 4-byte aligned");
+  if (dtype != PA_DTYPE_F32)
+    return fail(PA_ERR_UNSUPPORTED, "prefill supports fp32 only in this version");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (validate_env()) {
+    st = validate_device(block_tables, context_lens, query_start_loc, sliding_window, causal,
+                         num_seqs, max_blocks_per_seq, max_seq_len, num_blocks, total_q, s);
+    if (st != PA_OK) return st;
+  }
+  if (total_q == 0 || max_seq_len == 0) return ok();
+  pa::PrefillArgs a{};
+  a.out = out;
+  a.q = q;
+  a.k_cache = k_cache;
+  a.v_cache = v_cache;
+  a.block_tables = block_tables;
+  a.context_lens = context_lens;
+  a.query_start_loc = query_start_loc;
+  a.attn_bias = attn_bias;
+  a.window = sliding_window;
+  a.causal = causal;
+  a.scale_log2 = (float)((double)scale * 1.4426950408889634074);
+  a.num_seqs = num_seqs;
+  a.num_heads = num_heads;
+  a.head_dim = head_dim;
+  a.max_blocks = max_blocks_per_seq;
+  a.max_seq_len = max_seq_len;
+  a.dtype = (int32_t)dtype;
+  hipError_t e = pa::launch_prefill(a, s);
+  if (e != hipSuccess) return fail(PA_ERR_HIP, "prefill launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
+}  // extern "C"

@@ -1,0 +1,92 @@
+"""GPU parity of paged_attn_prefill (MFMA path, through the C ABI) against the
+float64 oracle: the 12-layer ModernBERT-shaped encoder workload (sampled),
+and small cases over lengths, windows, bias, causal masks and partial query
+sets."""
+import numpy as np
+import pytest
+import torch
+
+import workloads
+from gpu_helpers import (BS, assert_close, gpu_prefill, log, oracle_prefill, sample_prefill,
+                         to_device)
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda"
+
+
+def small(seed, lens, D=64, H=3, window=-1, causal=False, bias=None, q_lens=None, msl=None):
+    msl = msl or max(16, -(-max(lens) // 16) * 16)
+    return workloads.prefill_case(seed, num_seqs=len(lens), num_heads=H, head_dim=D, lens=lens,
+                                  max_seq_len=msl, dtype=torch.float32, bias=bias,
+                                  sliding_window=window, causal=causal, q_lens=q_lens)
+
+
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("window", [-1, 1, 3, 16, 64])
+@pytest.mark.parametrize("causal", [False, True])
+def test_small_prefill(D, window, causal):
+    lens = [1, 15, 16, 17, 63, 64, 65, 130]
+    case = to_device(small(500 + D + window, lens, D=D, window=window, causal=causal))
+    assert_close(gpu_prefill(case), oracle_prefill(case), torch.float32,
+                 "D=%d W=%d causal=%s" % (D, window, causal))
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("window", [-1, 9])
+def test_prefill_with_bias(causal, window):
+    case = to_device(small(600, [5, 33, 70, 129], window=window, causal=causal, bias="normal",
+                           msl=144))
+    assert_close(gpu_prefill(case), oracle_prefill(case), torch.float32,
+                 "bias W=%d causal=%s" % (window, causal))
+
+
+def test_prefill_null_bias_equals_zero_bias():
+    case = to_device(small(610, [5, 33, 70], msl=80))
+    zero = torch.zeros(3, 3, 80, 80, device=DEV)
+    a = gpu_prefill(case, bias=zero)
+    b = gpu_prefill(case, bias=None)
+    assert torch.equal(a, b)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_prefill_partial_queries(causal):
+    case = to_device(small(620, [40, 17, 100, 130], q_lens=[4, 17, 1, 70], window=21,
+                           causal=causal, msl=144))
+    assert_close(gpu_prefill(case), oracle_prefill(case), torch.float32, "partial q")
+
+
+def test_prefill_window_one_returns_own_value():
+    case = to_device(small(630, [1, 20, 77], window=1))
+    out = gpu_prefill(case).cpu()
+    qsl = case.query_start_loc.cpu()
+    for b in range(3):
+        for t in range(int(case.lens[b])):
+            v = case.v_cache[case.block_tables[b, t // BS].long(), :, t % BS, :].cpu()
+            assert torch.equal(out[int(qsl[b]) + t], v)
+
+
+def test_prefill_empty_sequences():
+    case = to_device(small(640, [0, 5, 0, 20], msl=32))
+    assert_close(gpu_prefill(case), oracle_prefill(case), torch.float32, "empty")
+
+
+def test_prefill_deterministic():
+    case = to_device(small(650, [300, 511, 64], window=64, msl=512))
+    a = gpu_prefill(case)
+    assert torch.equal(gpu_prefill(case), a)
+
+
+@pytest.mark.parametrize("layer", list(range(workloads.MODERNBERT_LAYERS)))
+def test_modernbert_prefill_layer_sampled(layer):
+    """Full-size layer (32 sequences, L up to 1024, 12 heads) in the launch
+    configuration the benchmark times; the oracle checks a sample of whole
+    sequences (the longest, the shortest and two more)."""
+    log("modernbert layer %d window %d" % (layer, workloads.modernbert_window(layer)))
+    case = workloads.modernbert_prefill_f32(layer, device=DEV)
+    out = gpu_prefill(case)
+    L = case.lens
+    seqs = sorted(set([int(np.argmax(L)), int(np.argmin(L)), layer % 32, (7 * layer + 3) % 32]))
+    sub = sample_prefill(case, seqs)
+    ref = oracle_prefill(sub)
+    assert_close(out[sub.rows.to(DEV)], ref, torch.float32, "layer %d sample" % layer)
