@@ -29,6 +29,9 @@ FLAGS = [
     "-ffp-contract=off",
     # no packed fp32 instructions
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # keep MFMA accumulators in VGPRs (no AGPR round trips for the softmax
+    # rescale of the prefill accumulators)
+    "-mllvm", "--amdgpu-mfma-vgpr-form",
     "-Wall", "-Wno-unused-result",
 ]
 

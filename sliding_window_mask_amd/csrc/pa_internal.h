@@ -46,6 +46,7 @@ struct PrefillArgs {
   float scale_log2;
   int32_t num_seqs, num_heads, head_dim, max_blocks, max_seq_len;
   int32_t dtype;
+  int32_t num_qtiles;         // query tiles per sequence in the grid (set by the launcher)
 };
 
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);

@@ -10,13 +10,23 @@
 // (v_mfma_f32_16x16x4_f32, fp32 products and accumulation).
 //
 // Work decomposition: one workgroup of 4 wave64s per (64-query tile, head,
-// sequence); wave w owns 16 query rows. The workgroup walks the keys its rows
-// can see in tiles of 64 keys (32 at D = 128), gathering each block through the
-// block table into LDS (K and V, rows padded by 4 floats against bank
-// conflicts) while the previous tile is being multiplied: the next tile's
-// global loads are issued into registers before the current tile's MFMAs.
-// Key tiles, and 16-key chunks within them, that no row of a wave can see are
-// skipped, so a window of 64 costs about the band, not the full square.
+// sequence); wave w owns 16 query rows. Workgroups are numbered so that every
+// query tile of one (sequence, head) lands on the same XCD (the hardware
+// deals consecutive workgroup ids round-robin over the 8 XCDs): the K/V of a
+// sequence is then pulled into one XCD's L2 and re-read from there by all of
+// its query tiles.
+//
+// The workgroup walks the keys its rows can see in tiles of 32 keys (16 at
+// D = 128). Tiles are gathered through the block table into a double-buffered
+// LDS ring (rows padded by 4 floats against bank conflicts) with one barrier
+// per tile: while tile k is multiplied, tile k+1 sits in the other LDS buffer
+// and tile k+2 is in flight from memory into registers; the block-table
+// entries are read one more tile ahead, so no key load waits on a table load.
+// Tiles that no row of a wave can see are skipped by that wave, so a window
+// of 64 costs about the band, not the full square; 16-key chunks that every
+// row of the wave sees whole skip the per-element mask. Causal and windowed
+// masks are compile-time variants, so the full-attention kernel carries no
+// mask arithmetic at all except at the sequence end.
 //
 // MFMA operand layout (16x16x4, lane l, g = l / 16, c = l % 16):
 //   A[i][k] from lane (i + 16 k), B[k][j] from lane (j + 16 k),
@@ -40,12 +50,19 @@ typedef float float4_t __attribute__((ext_vector_type(4)));
 
 constexpr int kThreads = 256;
 constexpr int kQTile = 64;      // queries per workgroup (16 per wave)
-constexpr int kPad = 4;         // floats of padding per LDS row
+#ifndef PA_PREFILL_PAD
+#define PA_PREFILL_PAD 4
+#endif
+constexpr int kPad = PA_PREFILL_PAD;   // floats of padding per LDS row
+constexpr int kXcds = 8;        // XCDs of an MI355X
 
-// Keys per LDS tile: 4 blocks at D = 64, 2 at D = 128 (K + V tiles stay
-// under 64 KiB of LDS either way).
+// Keys per LDS tile: 32 at D = 64, 16 at D = 128 (two K + V buffers take
+// 34 KiB of LDS, so LDS does not cap occupancy below the register limit).
+#ifndef PA_PREFILL_KTILE64
+#define PA_PREFILL_KTILE64 32
+#endif
 template <int D>
-constexpr int key_tile() { return D == 64 ? 64 : 32; }
+constexpr int key_tile() { return D == 64 ? PA_PREFILL_KTILE64 : 16; }
 
 __device__ __forceinline__ float4_t mfma16x16x4(float a, float b, float4_t c) {
   return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
@@ -63,25 +80,33 @@ __device__ __forceinline__ void key_range(int p0, int p1, int L, int window, int
   }
 }
 
-template <int D, bool HAS_BIAS>
+template <int D, bool HAS_BIAS, bool CAUSAL, bool WINDOW>
 __global__ void __launch_bounds__(kThreads)
 pa_prefill_f32(PrefillArgs a) {
   constexpr int kKTile = key_tile<D>();
-  constexpr int kChunks = kKTile / 16;    // 16-key chunks per tile
-  constexpr int kRow = D + kPad;          // LDS row stride (floats)
-  constexpr int kDQ = D / 4;              // dims per lane group in the S^T step
-  constexpr int kNDT = D / 16;            // output slices of 16 dims
+  constexpr int kChunks = kKTile / 16;               // 16-key chunks per tile
+  constexpr int kRow = D + kPad;                     // LDS row stride (floats)
+  constexpr int kDQ = D / 4;                         // dims per lane group (S^T step)
+  constexpr int kNDT = D / 16;                       // output slices of 16 dims
   constexpr int kLoads = kKTile * D / 4 / kThreads;  // 16-byte loads per thread per tile
+  constexpr int kRowsPerLoad = kThreads * 4 / D;     // tile rows one load instruction covers
+  static_assert(kLoads >= 1 && kRowsPerLoad <= 16 && 16 % kRowsPerLoad == 0, "tile shape");
 
-  const int tile = blockIdx.x;
-  const int h = blockIdx.y;
-  const int b = blockIdx.z;
+  // ---- XCD-aware workgroup numbering ----
+  const int H = a.num_heads;
+  const int n = blockIdx.x;
+  const int slot = n / kXcds;
+  const int pair = (slot / a.num_qtiles) * kXcds + n % kXcds;
+  const int tile = slot % a.num_qtiles;
+  if (pair >= a.num_seqs * H) return;
+  const int b = pair / H;
+  const int h = pair % H;
+
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
   const int c = lane & 15;
   const int g = lane >> 4;
-  const int H = a.num_heads;
 
   const int L = a.context_lens[b];
   const int q0 = a.query_start_loc[b];
@@ -97,48 +122,64 @@ pa_prefill_f32(PrefillArgs a) {
   const int w_first = t_first + wave * 16;
   const bool wave_active = w_first < nq;
   const int w_last = min(w_first + 16, nq) - 1;
+  const bool wave_full = w_last == w_first + 15;
   int wv_lo = 0, wv_hi = 0;
   if (wave_active) key_range(pos0 + w_first, pos0 + w_last, L, a.window, a.causal, wv_lo, wv_hi);
+  const int wp0 = pos0 + w_first, wp1 = pos0 + w_last;   // wave's first/last position
 
   // this lane's query row
   const int t = w_first + c;
   const bool row_ok = t < nq;
   const int p = pos0 + t;
 
-  // Q operand: D/4 contiguous floats per lane
+  // Q operand: D/4 contiguous floats per lane, pre-multiplied by
+  // scale * log2(e) so that S^T comes out of the matrix cores already in the
+  // base-2 score domain (rows past n_q are zero)
+  const float cs = a.scale_log2;
   float qreg[kDQ];
   {
-    // rows past n_q read the tile's first (valid) row and are zeroed
     const int tq = row_ok ? t : t_first;
-    const float* qrow = static_cast<const float*>(a.q) + ((int64_t)(q0 + tq) * H + h) * D + kDQ * g;
+    const float* qrow =
+        static_cast<const float*>(a.q) + ((int64_t)(q0 + tq) * H + h) * D + kDQ * g;
 #pragma unroll
     for (int i = 0; i < kDQ; i += 4) {
       float4_t v = *reinterpret_cast<const float4_t*>(qrow + i);
       if (!row_ok) v = float4_t{0, 0, 0, 0};
-      qreg[i] = v[0]; qreg[i + 1] = v[1]; qreg[i + 2] = v[2]; qreg[i + 3] = v[3];
+      qreg[i] = v[0] * cs; qreg[i + 1] = v[1] * cs; qreg[i + 2] = v[2] * cs;
+      qreg[i + 3] = v[3] * cs;
     }
   }
 
-  __shared__ float k_lds[kKTile * kRow];
-  __shared__ float v_lds[kKTile * kRow];
+  __shared__ float kv_lds[2][2][kKTile * kRow];      // [buffer][K, V][row * kRow + col]
 
   const float* kc = static_cast<const float*>(a.k_cache);
   const float* vc = static_cast<const float*>(a.v_cache);
   const int32_t* table = a.block_tables + (int64_t)b * a.max_blocks;
   const int kstart = wg_lo & ~(kBlockSize - 1);
   const int ntiles = wg_hi > kstart ? (wg_hi - kstart + kKTile - 1) / kKTile : 0;
+  const int nblk_seq = (L + kBlockSize - 1) / kBlockSize;
 
-  // global -> register staging of one key tile (zeros for keys >= L)
+  // block-table entries of one tile (uniform across the workgroup)
+  constexpr int kTB = (kKTile + kBlockSize - 1) / kBlockSize;
+  int tb[kTB];
+  auto load_table = [&](int tk) {
+#pragma unroll
+    for (int i = 0; i < kTB; ++i) {
+      const int blk = (kstart + tk * kKTile) / kBlockSize + i;
+      tb[i] = blk < nblk_seq ? table[blk] : 0;
+    }
+  };
+  // global -> registers: one tile of K and V (zeros for keys >= L)
   float4_t kst[kLoads], vst[kLoads];
   auto fetch = [&](int tk) {
     const int base = kstart + tk * kKTile;
 #pragma unroll
     for (int i = 0; i < kLoads; ++i) {
-      const int e = (i * kThreads + tid) * 4;      // float index within the tile
-      const int r = e / D, col = e % D;
+      const int r = i * kRowsPerLoad + tid / (D / 4);
+      const int col = (tid % (D / 4)) * 4;
       const int j = base + r;
       if (j < L) {
-        const int64_t phys = table[j / kBlockSize];
+        const int64_t phys = tb[(i * kRowsPerLoad) / kBlockSize];
         const int64_t off = ((phys * H + h) * kBlockSize + (j % kBlockSize)) * D + col;
         kst[i] = *reinterpret_cast<const float4_t*>(kc + off);
         vst[i] = *reinterpret_cast<const float4_t*>(vc + off);
@@ -148,114 +189,151 @@ pa_prefill_f32(PrefillArgs a) {
       }
     }
   };
-  auto stash = [&]() {
+  auto stash = [&](int buf) {
 #pragma unroll
     for (int i = 0; i < kLoads; ++i) {
-      const int e = (i * kThreads + tid) * 4;
-      const int r = e / D, col = e % D;
-      *reinterpret_cast<float4_t*>(&k_lds[r * kRow + col]) = kst[i];
-      *reinterpret_cast<float4_t*>(&v_lds[r * kRow + col]) = vst[i];
+      const int r = i * kRowsPerLoad + tid / (D / 4);
+      const int col = (tid % (D / 4)) * 4;
+      *reinterpret_cast<float4_t*>(&kv_lds[buf][0][r * kRow + col]) = kst[i];
+      *reinterpret_cast<float4_t*>(&kv_lds[buf][1][r * kRow + col]) = vst[i];
     }
   };
 
   float4_t acc[kNDT];
 #pragma unroll
   for (int dt = 0; dt < kNDT; ++dt) acc[dt] = float4_t{0, 0, 0, 0};
-  float m_run = -INFINITY, l_run = 0.0f;
+  // Online softmax with a lazily moved reference: weights are 2^(s - m_ref);
+  // m_ref only moves (rescaling acc and l) when a row's max exceeds it by
+  // more than 2^8, so weights stay <= 256 and the rescale is rare.
+  float m_ref = -INFINITY, l_run = 0.0f;
+  // bias row of this query (rows past n_q point at the tile's first row and
+  // are masked; every bias read is in bounds)
   const float* bias_row =
-      (HAS_BIAS && row_ok)
-          ? a.attn_bias + (((int64_t)b * H + h) * a.max_seq_len + p) * a.max_seq_len
-          : nullptr;
+      HAS_BIAS ? a.attn_bias + (((int64_t)b * H + h) * a.max_seq_len + (row_ok ? p : pos0 + t_first)) *
+                                   a.max_seq_len
+               : nullptr;
 
-  if (ntiles > 0) fetch(0);
-  for (int tk = 0; tk < ntiles; ++tk) {
-    __syncthreads();                     // everyone is done reading the old tile
-    stash();
-    __syncthreads();
-    if (tk + 1 < ntiles) fetch(tk + 1);  // in flight during this tile's math
-    const int base = kstart + tk * kKTile;
-    if (!wave_active || base >= wv_hi || base + kKTile <= wv_lo) continue;
-
-    // ---- S^T = K Q^T for the chunks of 16 keys ----
-    float4_t s[kChunks];
-    bool live[kChunks];
-#pragma unroll
-    for (int ch = 0; ch < kChunks; ++ch) {
-      const int c0 = base + ch * 16;
-      live[ch] = c0 < wv_hi && c0 + 16 > wv_lo;
-      s[ch] = float4_t{0, 0, 0, 0};
+  // ---- prologue: tile 0 into LDS buffer 0, tile 1 in flight, table of tile 2 ----
+  if (ntiles > 0) {
+    load_table(0);
+    fetch(0);
+    stash(0);
+    if (ntiles > 1) {
+      load_table(1);
+      fetch(1);
+      if (ntiles > 2) load_table(2);
     }
+  }
+  __syncthreads();
+
+  for (int tk = 0; tk < ntiles; ++tk) {
+    const int buf = tk & 1;
+    const int base = kstart + tk * kKTile;
+    if (wave_active && base < wv_hi && base + kKTile > wv_lo) {
+      const float* k_lds = kv_lds[buf][0];
+      const float* v_lds = kv_lds[buf][1];
+
+      // ---- S^T = K Q^T (base-2 scores): the chunks' MFMA chains interleaved ----
+      float4_t s[kChunks];
 #pragma unroll
-    for (int ch = 0; ch < kChunks; ++ch) {
-      if (!live[ch]) continue;
-      const float* krow = &k_lds[(ch * 16 + c) * kRow + kDQ * g];
+      for (int ch = 0; ch < kChunks; ++ch) s[ch] = float4_t{0, 0, 0, 0};
 #pragma unroll
       for (int i = 0; i < kDQ; i += 4) {
-        const float4_t kv = *reinterpret_cast<const float4_t*>(krow + i);
-        s[ch] = mfma16x16x4(kv[0], qreg[i], s[ch]);
-        s[ch] = mfma16x16x4(kv[1], qreg[i + 1], s[ch]);
-        s[ch] = mfma16x16x4(kv[2], qreg[i + 2], s[ch]);
-        s[ch] = mfma16x16x4(kv[3], qreg[i + 3], s[ch]);
-      }
-    }
-
-    // ---- scores, mask, online softmax (query c, keys 4g + r of each chunk) ----
-    float mt = -INFINITY;
 #pragma unroll
-    for (int ch = 0; ch < kChunks; ++ch) {
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int j = base + ch * 16 + 4 * g + r;
-        bool vis = live[ch] && row_ok && j < L;
-        if (a.causal) vis = vis && j <= p;
-        if (a.window > 0) vis = vis && abs(p - j) < a.window;
-        float x = -INFINITY;
-        if (vis) {
-          float tsum = s[ch][r];
-          if constexpr (HAS_BIAS) tsum = tsum + bias_row[j];
-          x = tsum * a.scale_log2;
+        for (int ch = 0; ch < kChunks; ++ch) {
+          const float4_t kv =
+              *reinterpret_cast<const float4_t*>(&k_lds[(ch * 16 + c) * kRow + kDQ * g + i]);
+          s[ch] = mfma16x16x4(kv[0], qreg[i], s[ch]);
+          s[ch] = mfma16x16x4(kv[1], qreg[i + 1], s[ch]);
+          s[ch] = mfma16x16x4(kv[2], qreg[i + 2], s[ch]);
+          s[ch] = mfma16x16x4(kv[3], qreg[i + 3], s[ch]);
         }
-        s[ch][r] = x;
-        mt = fmaxf(mt, x);
       }
-    }
-    mt = fmaxf(mt, __shfl_xor(mt, 16));
-    mt = fmaxf(mt, __shfl_xor(mt, 32));
-    const float m_new = fmaxf(m_run, mt);
-    const float m_use = (m_new == -INFINITY) ? 0.0f : m_new;
-    const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
-    m_run = m_new;
-    float lsum = 0.0f;
 #pragma unroll
-    for (int ch = 0; ch < kChunks; ++ch) {
+      for (int ch = 0; ch < kChunks; ++ch) {
+        const int c0 = base + ch * 16;
+        const int j0 = c0 + 4 * g;
+        // bias (added as a * scale * log2(e): the same sum as (q.k + a) * scale)
+        if constexpr (HAS_BIAS) {
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const float pr = __builtin_amdgcn_exp2f(s[ch][r] - m_use);
-        s[ch][r] = pr;
-        lsum += pr;
-      }
-    }
-    l_run = fmaf(l_run, alpha, lsum);
-#pragma unroll
-    for (int dt = 0; dt < kNDT; ++dt) acc[dt] *= alpha;
-
-    // ---- O^T += V^T P^T ----
-#pragma unroll
-    for (int ch = 0; ch < kChunks; ++ch) {
-      if (!live[ch]) continue;
-#pragma unroll
-      for (int kk = 0; kk < 4; ++kk) {
-        const float* vrow = &v_lds[(ch * 16 + 4 * g + kk) * kRow + kNDT * c];
-        float vv[kNDT];
-#pragma unroll
-        for (int i = 0; i < kNDT; i += 4) {
-          const float4_t x = *reinterpret_cast<const float4_t*>(vrow + i);
-          vv[i] = x[0]; vv[i + 1] = x[1]; vv[i + 2] = x[2]; vv[i + 3] = x[3];
+          for (int r = 0; r < 4; ++r) s[ch][r] = s[ch][r] + bias_row[min(j0 + r, L - 1)] * cs;
         }
+        // per-element mask only where some row of the wave does not see the
+        // whole chunk (chunk edges of the sequence, the window or the diagonal)
+        bool whole = wave_full && c0 + 16 <= L;
+        if constexpr (CAUSAL) whole = whole && c0 + 15 <= wp0;
+        if constexpr (WINDOW) whole = whole && wp1 - c0 < a.window && c0 + 15 - wp0 < a.window;
+        if (!whole) {
 #pragma unroll
-        for (int dt = 0; dt < kNDT; ++dt) acc[dt] = mfma16x16x4(vv[dt], s[ch][kk], acc[dt]);
+          for (int r = 0; r < 4; ++r) {
+            const int j = j0 + r;
+            bool vis = row_ok && j < L;
+            if constexpr (CAUSAL) vis = vis && j <= p;
+            if constexpr (WINDOW) vis = vis && abs(p - j) < a.window;
+            s[ch][r] = vis ? s[ch][r] : -INFINITY;
+          }
+        }
+      }
+
+      // ---- row max over the tile: 4 values per chunk, then lanes c + 16 g ----
+      float mt = -INFINITY;
+#pragma unroll
+      for (int ch = 0; ch < kChunks; ++ch)
+        mt = fmaxf(fmaxf(mt, fmaxf(s[ch][0], s[ch][1])), fmaxf(s[ch][2], s[ch][3]));
+      {
+        const auto x16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(mt),
+                                                          __float_as_uint(mt), false, false);
+        mt = fmaxf(__uint_as_float(x16[0]), __uint_as_float(x16[1]));
+        const auto x32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(mt),
+                                                          __float_as_uint(mt), false, false);
+        mt = fmaxf(__uint_as_float(x32[0]), __uint_as_float(x32[1]));
+      }
+      const bool move = mt > m_ref + 8.0f;        // false while mt = -inf
+      if (__builtin_amdgcn_ballot_w64(move) != 0) {
+        // rows that do not move keep alpha = 1 (their m_ref may still be
+        // -inf: exp2(-inf - -inf) would be NaN); a first move from -inf
+        // gives alpha = 0 on an empty accumulator
+        const float alpha = move ? __builtin_amdgcn_exp2f(m_ref - mt) : 1.0f;
+        m_ref = move ? mt : m_ref;
+        l_run *= alpha;
+#pragma unroll
+        for (int dt = 0; dt < kNDT; ++dt) acc[dt] *= alpha;
+      }
+      const float m_use = (m_ref == -INFINITY) ? 0.0f : m_ref;
+#pragma unroll
+      for (int ch = 0; ch < kChunks; ++ch) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const float pr = __builtin_amdgcn_exp2f(s[ch][r] - m_use);
+          s[ch][r] = pr;
+          l_run += pr;
+        }
+      }
+
+      // ---- O^T += V^T P^T ----
+#pragma unroll
+      for (int ch = 0; ch < kChunks; ++ch) {
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) {
+          const float* vrow = &v_lds[(ch * 16 + 4 * g + kk) * kRow + kNDT * c];
+          float vv[kNDT];
+#pragma unroll
+          for (int i = 0; i < kNDT; i += 4) {
+            const float4_t x = *reinterpret_cast<const float4_t*>(vrow + i);
+            vv[i] = x[0]; vv[i + 1] = x[1]; vv[i + 2] = x[2]; vv[i + 3] = x[3];
+          }
+#pragma unroll
+          for (int dt = 0; dt < kNDT; ++dt) acc[dt] = mfma16x16x4(vv[dt], s[ch][kk], acc[dt]);
+        }
       }
     }
+    // refill: tile tk+1 (in registers) -> the other buffer, tile tk+2 -> registers
+    if (tk + 1 < ntiles) stash(buf ^ 1);
+    if (tk + 2 < ntiles) {
+      fetch(tk + 2);
+      if (tk + 3 < ntiles) load_table(tk + 3);
+    }
+    __syncthreads();
   }
 
   // ---- epilogue: out = O / l ----
@@ -276,13 +354,37 @@ pa_prefill_f32(PrefillArgs a) {
   }
 }
 
+template <int D, bool HAS_BIAS>
+void launch_mask(const PrefillArgs& a, dim3 grid, hipStream_t stream) {
+  if (a.causal) {
+    if (a.window > 0)
+      hipLaunchKernelGGL((pa_prefill_f32<D, HAS_BIAS, true, true>), grid, dim3(kThreads), 0,
+                         stream, a);
+    else
+      hipLaunchKernelGGL((pa_prefill_f32<D, HAS_BIAS, true, false>), grid, dim3(kThreads), 0,
+                         stream, a);
+  } else {
+    if (a.window > 0)
+      hipLaunchKernelGGL((pa_prefill_f32<D, HAS_BIAS, false, true>), grid, dim3(kThreads), 0,
+                         stream, a);
+    else
+      hipLaunchKernelGGL((pa_prefill_f32<D, HAS_BIAS, false, false>), grid, dim3(kThreads), 0,
+                         stream, a);
+  }
+}
+
 template <int D>
-hipError_t launch_d(const PrefillArgs& a, hipStream_t stream) {
-  dim3 grid((a.max_seq_len + kQTile - 1) / kQTile, a.num_heads, a.num_seqs);
+hipError_t launch_d(PrefillArgs a, hipStream_t stream) {
+  a.num_qtiles = (a.max_seq_len + kQTile - 1) / kQTile;
+  const int64_t pairs = (int64_t)a.num_seqs * a.num_heads;
+  const int64_t groups = (pairs + kXcds - 1) / kXcds;
+  const int64_t nwg = groups * kXcds * a.num_qtiles;
+  if (nwg > 0x7fffffff) return hipErrorInvalidValue;
+  dim3 grid((unsigned)nwg);
   if (a.attn_bias)
-    hipLaunchKernelGGL((pa_prefill_f32<D, true>), grid, dim3(kThreads), 0, stream, a);
+    launch_mask<D, true>(a, grid, stream);
   else
-    hipLaunchKernelGGL((pa_prefill_f32<D, false>), grid, dim3(kThreads), 0, stream, a);
+    launch_mask<D, false>(a, grid, stream);
   return hipGetLastError();
 }
 
