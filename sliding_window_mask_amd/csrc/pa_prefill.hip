@@ -49,7 +49,11 @@ namespace {
 typedef float float4_t __attribute__((ext_vector_type(4)));
 
 constexpr int kThreads = 256;
-constexpr int kQTile = 64;      // queries per workgroup (16 per wave)
+constexpr int kWaves = kThreads / 64;
+// 16-query groups per wave at D = 64 (the workgroup covers 64 * groups queries)
+#ifndef PA_PREFILL_GROUPS
+#define PA_PREFILL_GROUPS 1
+#endif
 #ifndef PA_PREFILL_PAD
 #define PA_PREFILL_PAD 4
 #endif
@@ -80,7 +84,7 @@ __device__ __forceinline__ void key_range(int p0, int p1, int L, int window, int
   }
 }
 
-template <int D, bool HAS_BIAS, bool CAUSAL, bool WINDOW>
+template <int D, int NG, bool HAS_BIAS, bool CAUSAL, bool WINDOW>
 __global__ void __launch_bounds__(kThreads)
 pa_prefill_f32(PrefillArgs a) {
   constexpr int kKTile = key_tile<D>();
@@ -90,6 +94,8 @@ pa_prefill_f32(PrefillArgs a) {
   constexpr int kNDT = D / 16;                       // output slices of 16 dims
   constexpr int kLoads = kKTile * D / 4 / kThreads;  // 16-byte loads per thread per tile
   constexpr int kRowsPerLoad = kThreads * 4 / D;     // tile rows one load instruction covers
+  constexpr int kWaveRows = 16 * NG;                 // query rows per wave
+  constexpr int kQT = kWaves * kWaveRows;            // query rows per workgroup
   static_assert(kLoads >= 1 && kRowsPerLoad <= 16 && 16 % kRowsPerLoad == 0, "tile shape");
 
   // ---- XCD-aware workgroup numbering ----
@@ -111,42 +117,53 @@ pa_prefill_f32(PrefillArgs a) {
   const int L = a.context_lens[b];
   const int q0 = a.query_start_loc[b];
   const int nq = a.query_start_loc[b + 1] - q0;
-  const int t_first = tile * kQTile;
+  const int t_first = tile * kQT;
   if (t_first >= nq) return;
   const int pos0 = L - nq;                 // position of query 0
 
   // workgroup and wave query ranges (positions), clamped to valid rows
-  const int wg_last = min(t_first + kQTile, nq) - 1;
+  const int wg_last = min(t_first + kQT, nq) - 1;
   int wg_lo, wg_hi;
-  key_range(pos0 + t_first, pos0 + wg_last, L, a.window, a.causal, wg_lo, wg_hi);
-  const int w_first = t_first + wave * 16;
+  key_range(pos0 + t_first, pos0 + wg_last, L, a.window, CAUSAL, wg_lo, wg_hi);
+  const int w_first = t_first + wave * kWaveRows;
   const bool wave_active = w_first < nq;
-  const int w_last = min(w_first + 16, nq) - 1;
-  const bool wave_full = w_last == w_first + 15;
   int wv_lo = 0, wv_hi = 0;
-  if (wave_active) key_range(pos0 + w_first, pos0 + w_last, L, a.window, a.causal, wv_lo, wv_hi);
-  const int wp0 = pos0 + w_first, wp1 = pos0 + w_last;   // wave's first/last position
+  if (wave_active)
+    key_range(pos0 + w_first, pos0 + min(w_first + kWaveRows, nq) - 1, L, a.window, CAUSAL,
+              wv_lo, wv_hi);
 
-  // this lane's query row
-  const int t = w_first + c;
-  const bool row_ok = t < nq;
-  const int p = pos0 + t;
+  // per query group: first/last position, whether all 16 rows are valid,
+  // this lane's row
+  int gp0[NG], gp1[NG], t[NG], p[NG];
+  bool gfull[NG], row_ok[NG];
+#pragma unroll
+  for (int q = 0; q < NG; ++q) {
+    const int first = w_first + 16 * q;
+    const int last = min(first + 16, nq) - 1;
+    gp0[q] = pos0 + first;
+    gp1[q] = pos0 + last;
+    gfull[q] = last == first + 15;
+    t[q] = first + c;
+    row_ok[q] = t[q] < nq;
+    p[q] = pos0 + t[q];
+  }
 
-  // Q operand: D/4 contiguous floats per lane, pre-multiplied by
+  // Q operands: D/4 contiguous floats per lane, pre-multiplied by
   // scale * log2(e) so that S^T comes out of the matrix cores already in the
   // base-2 score domain (rows past n_q are zero)
   const float cs = a.scale_log2;
-  float qreg[kDQ];
-  {
-    const int tq = row_ok ? t : t_first;
+  float qreg[NG][kDQ];
+#pragma unroll
+  for (int q = 0; q < NG; ++q) {
+    const int tq = row_ok[q] ? t[q] : t_first;
     const float* qrow =
         static_cast<const float*>(a.q) + ((int64_t)(q0 + tq) * H + h) * D + kDQ * g;
 #pragma unroll
     for (int i = 0; i < kDQ; i += 4) {
       float4_t v = *reinterpret_cast<const float4_t*>(qrow + i);
-      if (!row_ok) v = float4_t{0, 0, 0, 0};
-      qreg[i] = v[0] * cs; qreg[i + 1] = v[1] * cs; qreg[i + 2] = v[2] * cs;
-      qreg[i + 3] = v[3] * cs;
+      if (!row_ok[q]) v = float4_t{0, 0, 0, 0};
+      qreg[q][i] = v[0] * cs; qreg[q][i + 1] = v[1] * cs; qreg[q][i + 2] = v[2] * cs;
+      qreg[q][i + 3] = v[3] * cs;
     }
   }
 
@@ -169,20 +186,22 @@ pa_prefill_f32(PrefillArgs a) {
       tb[i] = blk < nblk_seq ? table[blk] : 0;
     }
   };
-  // global -> registers: one tile of K and V (zeros for keys >= L)
+  // global -> registers: one tile of K and V (zeros for keys >= L). The
+  // block base is uniform; only the sequence's last tile needs the key check.
   float4_t kst[kLoads], vst[kLoads];
   auto fetch = [&](int tk) {
     const int base = kstart + tk * kKTile;
+    const bool tail = base + kKTile > L;
 #pragma unroll
     for (int i = 0; i < kLoads; ++i) {
       const int r = i * kRowsPerLoad + tid / (D / 4);
       const int col = (tid % (D / 4)) * 4;
-      const int j = base + r;
-      if (j < L) {
-        const int64_t phys = tb[(i * kRowsPerLoad) / kBlockSize];
-        const int64_t off = ((phys * H + h) * kBlockSize + (j % kBlockSize)) * D + col;
-        kst[i] = *reinterpret_cast<const float4_t*>(kc + off);
-        vst[i] = *reinterpret_cast<const float4_t*>(vc + off);
+      const int64_t blk_off = ((int64_t)tb[(i * kRowsPerLoad) / kBlockSize] * H + h) *
+                              (kBlockSize * D);
+      const int in_blk = ((base + r) % kBlockSize) * D + col;
+      if (!tail || base + r < L) {
+        kst[i] = *reinterpret_cast<const float4_t*>(kc + blk_off + in_blk);
+        vst[i] = *reinterpret_cast<const float4_t*>(vc + blk_off + in_blk);
       } else {
         kst[i] = float4_t{0, 0, 0, 0};
         vst[i] = float4_t{0, 0, 0, 0};
@@ -199,19 +218,27 @@ pa_prefill_f32(PrefillArgs a) {
     }
   };
 
-  float4_t acc[kNDT];
+  float4_t acc[NG][kNDT];
 #pragma unroll
-  for (int dt = 0; dt < kNDT; ++dt) acc[dt] = float4_t{0, 0, 0, 0};
+  for (int q = 0; q < NG; ++q)
+#pragma unroll
+    for (int dt = 0; dt < kNDT; ++dt) acc[q][dt] = float4_t{0, 0, 0, 0};
   // Online softmax with a lazily moved reference: weights are 2^(s - m_ref);
   // m_ref only moves (rescaling acc and l) when a row's max exceeds it by
   // more than 2^8, so weights stay <= 256 and the rescale is rare.
-  float m_ref = -INFINITY, l_run = 0.0f;
-  // bias row of this query (rows past n_q point at the tile's first row and
-  // are masked; every bias read is in bounds)
-  const float* bias_row =
-      HAS_BIAS ? a.attn_bias + (((int64_t)b * H + h) * a.max_seq_len + (row_ok ? p : pos0 + t_first)) *
-                                   a.max_seq_len
-               : nullptr;
+  float m_ref[NG], l_run[NG];
+  const float* bias_row[NG];
+#pragma unroll
+  for (int q = 0; q < NG; ++q) {
+    m_ref[q] = -INFINITY;
+    l_run[q] = 0.0f;
+    // rows past n_q point at the tile's first row and are masked, so every
+    // bias read is in bounds
+    bias_row[q] = HAS_BIAS ? a.attn_bias + (((int64_t)b * H + h) * a.max_seq_len +
+                                            (row_ok[q] ? p[q] : pos0 + t_first)) *
+                                               a.max_seq_len
+                           : nullptr;
+  }
 
   // ---- prologue: tile 0 into LDS buffer 0, tile 1 in flight, table of tile 2 ----
   if (ntiles > 0) {
@@ -233,84 +260,92 @@ pa_prefill_f32(PrefillArgs a) {
       const float* k_lds = kv_lds[buf][0];
       const float* v_lds = kv_lds[buf][1];
 
-      // ---- S^T = K Q^T (base-2 scores): the chunks' MFMA chains interleaved ----
-      float4_t s[kChunks];
+      // ---- S^T = K Q^T (base-2 scores); each K operand feeds every group ----
+      float4_t s[NG][kChunks];
 #pragma unroll
-      for (int ch = 0; ch < kChunks; ++ch) s[ch] = float4_t{0, 0, 0, 0};
+      for (int q = 0; q < NG; ++q)
+#pragma unroll
+        for (int ch = 0; ch < kChunks; ++ch) s[q][ch] = float4_t{0, 0, 0, 0};
 #pragma unroll
       for (int i = 0; i < kDQ; i += 4) {
 #pragma unroll
         for (int ch = 0; ch < kChunks; ++ch) {
           const float4_t kv =
               *reinterpret_cast<const float4_t*>(&k_lds[(ch * 16 + c) * kRow + kDQ * g + i]);
-          s[ch] = mfma16x16x4(kv[0], qreg[i], s[ch]);
-          s[ch] = mfma16x16x4(kv[1], qreg[i + 1], s[ch]);
-          s[ch] = mfma16x16x4(kv[2], qreg[i + 2], s[ch]);
-          s[ch] = mfma16x16x4(kv[3], qreg[i + 3], s[ch]);
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+#pragma unroll
+            for (int q = 0; q < NG; ++q) s[q][ch] = mfma16x16x4(kv[e], qreg[q][i + e], s[q][ch]);
         }
       }
+
 #pragma unroll
-      for (int ch = 0; ch < kChunks; ++ch) {
-        const int c0 = base + ch * 16;
-        const int j0 = c0 + 4 * g;
-        // bias (added as a * scale * log2(e): the same sum as (q.k + a) * scale)
-        if constexpr (HAS_BIAS) {
+      for (int q = 0; q < NG; ++q) {
 #pragma unroll
-          for (int r = 0; r < 4; ++r) s[ch][r] = s[ch][r] + bias_row[min(j0 + r, L - 1)] * cs;
+        for (int ch = 0; ch < kChunks; ++ch) {
+          const int c0 = base + ch * 16;
+          const int j0 = c0 + 4 * g;
+          // bias (added as a * scale * log2(e): the same sum as (q.k + a) * scale)
+          if constexpr (HAS_BIAS) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+              s[q][ch][r] = s[q][ch][r] + bias_row[q][min(j0 + r, L - 1)] * cs;
+          }
+          // per-element mask only where some row of the group does not see
+          // the whole chunk (sequence end, window edges, diagonal)
+          bool whole = gfull[q] && c0 + 16 <= L;
+          if constexpr (CAUSAL) whole = whole && c0 + 15 <= gp0[q];
+          if constexpr (WINDOW)
+            whole = whole && gp1[q] - c0 < a.window && c0 + 15 - gp0[q] < a.window;
+          if (!whole) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+              const int j = j0 + r;
+              bool vis = row_ok[q] && j < L;
+              if constexpr (CAUSAL) vis = vis && j <= p[q];
+              if constexpr (WINDOW) vis = vis && abs(p[q] - j) < a.window;
+              s[q][ch][r] = vis ? s[q][ch][r] : -INFINITY;
+            }
+          }
         }
-        // per-element mask only where some row of the wave does not see the
-        // whole chunk (chunk edges of the sequence, the window or the diagonal)
-        bool whole = wave_full && c0 + 16 <= L;
-        if constexpr (CAUSAL) whole = whole && c0 + 15 <= wp0;
-        if constexpr (WINDOW) whole = whole && wp1 - c0 < a.window && c0 + 15 - wp0 < a.window;
-        if (!whole) {
+
+        // ---- row max over the tile: 4 values per chunk, then lanes c + 16 g ----
+        float mt = -INFINITY;
+#pragma unroll
+        for (int ch = 0; ch < kChunks; ++ch)
+          mt = fmaxf(fmaxf(mt, fmaxf(s[q][ch][0], s[q][ch][1])), fmaxf(s[q][ch][2], s[q][ch][3]));
+        {
+          const auto x16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(mt),
+                                                            __float_as_uint(mt), false, false);
+          mt = fmaxf(__uint_as_float(x16[0]), __uint_as_float(x16[1]));
+          const auto x32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(mt),
+                                                            __float_as_uint(mt), false, false);
+          mt = fmaxf(__uint_as_float(x32[0]), __uint_as_float(x32[1]));
+        }
+        const bool move = mt > m_ref[q] + 8.0f;        // false while mt = -inf
+        if (__builtin_amdgcn_ballot_w64(move) != 0) {
+          // rows that do not move keep alpha = 1 (their m_ref may still be
+          // -inf: exp2(-inf - -inf) would be NaN); a first move from -inf
+          // gives alpha = 0 on an empty accumulator
+          const float alpha = move ? __builtin_amdgcn_exp2f(m_ref[q] - mt) : 1.0f;
+          m_ref[q] = move ? mt : m_ref[q];
+          l_run[q] *= alpha;
+#pragma unroll
+          for (int dt = 0; dt < kNDT; ++dt) acc[q][dt] *= alpha;
+        }
+        const float m_use = (m_ref[q] == -INFINITY) ? 0.0f : m_ref[q];
+#pragma unroll
+        for (int ch = 0; ch < kChunks; ++ch) {
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
-            const int j = j0 + r;
-            bool vis = row_ok && j < L;
-            if constexpr (CAUSAL) vis = vis && j <= p;
-            if constexpr (WINDOW) vis = vis && abs(p - j) < a.window;
-            s[ch][r] = vis ? s[ch][r] : -INFINITY;
+            const float pr = __builtin_amdgcn_exp2f(s[q][ch][r] - m_use);
+            s[q][ch][r] = pr;
+            l_run[q] += pr;
           }
         }
       }
 
-      // ---- row max over the tile: 4 values per chunk, then lanes c + 16 g ----
-      float mt = -INFINITY;
-#pragma unroll
-      for (int ch = 0; ch < kChunks; ++ch)
-        mt = fmaxf(fmaxf(mt, fmaxf(s[ch][0], s[ch][1])), fmaxf(s[ch][2], s[ch][3]));
-      {
-        const auto x16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(mt),
-                                                          __float_as_uint(mt), false, false);
-        mt = fmaxf(__uint_as_float(x16[0]), __uint_as_float(x16[1]));
-        const auto x32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(mt),
-                                                          __float_as_uint(mt), false, false);
-        mt = fmaxf(__uint_as_float(x32[0]), __uint_as_float(x32[1]));
-      }
-      const bool move = mt > m_ref + 8.0f;        // false while mt = -inf
-      if (__builtin_amdgcn_ballot_w64(move) != 0) {
-        // rows that do not move keep alpha = 1 (their m_ref may still be
-        // -inf: exp2(-inf - -inf) would be NaN); a first move from -inf
-        // gives alpha = 0 on an empty accumulator
-        const float alpha = move ? __builtin_amdgcn_exp2f(m_ref - mt) : 1.0f;
-        m_ref = move ? mt : m_ref;
-        l_run *= alpha;
-#pragma unroll
-        for (int dt = 0; dt < kNDT; ++dt) acc[dt] *= alpha;
-      }
-      const float m_use = (m_ref == -INFINITY) ? 0.0f : m_ref;
-#pragma unroll
-      for (int ch = 0; ch < kChunks; ++ch) {
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const float pr = __builtin_amdgcn_exp2f(s[ch][r] - m_use);
-          s[ch][r] = pr;
-          l_run += pr;
-        }
-      }
-
-      // ---- O^T += V^T P^T ----
+      // ---- O^T += V^T P^T; each V operand feeds every group ----
 #pragma unroll
       for (int ch = 0; ch < kChunks; ++ch) {
 #pragma unroll
@@ -323,7 +358,10 @@ pa_prefill_f32(PrefillArgs a) {
             vv[i] = x[0]; vv[i + 1] = x[1]; vv[i + 2] = x[2]; vv[i + 3] = x[3];
           }
 #pragma unroll
-          for (int dt = 0; dt < kNDT; ++dt) acc[dt] = mfma16x16x4(vv[dt], s[ch][kk], acc[dt]);
+          for (int dt = 0; dt < kNDT; ++dt)
+#pragma unroll
+            for (int q = 0; q < NG; ++q)
+              acc[q][dt] = mfma16x16x4(vv[dt], s[q][ch][kk], acc[q][dt]);
         }
       }
     }
@@ -337,54 +375,58 @@ pa_prefill_f32(PrefillArgs a) {
   }
 
   // ---- epilogue: out = O / l ----
-  float l_tot = l_run;
-  l_tot += __shfl_xor(l_tot, 16);
-  l_tot += __shfl_xor(l_tot, 32);
-  if (!row_ok) return;
-  const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
-  float* orow = static_cast<float*>(a.out) + ((int64_t)(q0 + t) * H + h) * D + kDQ * g;
 #pragma unroll
-  for (int r = 0; r < 4; ++r) {
+  for (int q = 0; q < NG; ++q) {
+    float l_tot = l_run[q];
+    l_tot += __shfl_xor(l_tot, 16);
+    l_tot += __shfl_xor(l_tot, 32);
+    if (!row_ok[q]) continue;
+    const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
+    float* orow = static_cast<float*>(a.out) + ((int64_t)(q0 + t[q]) * H + h) * D + kDQ * g;
 #pragma unroll
-    for (int dt = 0; dt < kNDT; dt += 4) {
-      float4_t o = {acc[dt][r] * inv, acc[dt + 1][r] * inv, acc[dt + 2][r] * inv,
-                    acc[dt + 3][r] * inv};
-      *reinterpret_cast<float4_t*>(orow + kNDT * r + dt) = o;
+    for (int r = 0; r < 4; ++r) {
+#pragma unroll
+      for (int dt = 0; dt < kNDT; dt += 4) {
+        float4_t o = {acc[q][dt][r] * inv, acc[q][dt + 1][r] * inv, acc[q][dt + 2][r] * inv,
+                      acc[q][dt + 3][r] * inv};
+        *reinterpret_cast<float4_t*>(orow + kNDT * r + dt) = o;
+      }
     }
   }
 }
 
-template <int D, bool HAS_BIAS>
+template <int D, int NG, bool HAS_BIAS>
 void launch_mask(const PrefillArgs& a, dim3 grid, hipStream_t stream) {
   if (a.causal) {
     if (a.window > 0)
-      hipLaunchKernelGGL((pa_prefill_f32<D, HAS_BIAS, true, true>), grid, dim3(kThreads), 0,
+      hipLaunchKernelGGL((pa_prefill_f32<D, NG, HAS_BIAS, true, true>), grid, dim3(kThreads), 0,
                          stream, a);
     else
-      hipLaunchKernelGGL((pa_prefill_f32<D, HAS_BIAS, true, false>), grid, dim3(kThreads), 0,
-                         stream, a);
+      hipLaunchKernelGGL((pa_prefill_f32<D, NG, HAS_BIAS, true, false>), grid, dim3(kThreads),
+                         0, stream, a);
   } else {
     if (a.window > 0)
-      hipLaunchKernelGGL((pa_prefill_f32<D, HAS_BIAS, false, true>), grid, dim3(kThreads), 0,
-                         stream, a);
+      hipLaunchKernelGGL((pa_prefill_f32<D, NG, HAS_BIAS, false, true>), grid, dim3(kThreads),
+                         0, stream, a);
     else
-      hipLaunchKernelGGL((pa_prefill_f32<D, HAS_BIAS, false, false>), grid, dim3(kThreads), 0,
-                         stream, a);
+      hipLaunchKernelGGL((pa_prefill_f32<D, NG, HAS_BIAS, false, false>), grid, dim3(kThreads),
+                         0, stream, a);
   }
 }
 
-template <int D>
+template <int D, int NG>
 hipError_t launch_d(PrefillArgs a, hipStream_t stream) {
-  a.num_qtiles = (a.max_seq_len + kQTile - 1) / kQTile;
+  constexpr int kQT = kWaves * 16 * NG;
+  a.num_qtiles = (a.max_seq_len + kQT - 1) / kQT;
   const int64_t pairs = (int64_t)a.num_seqs * a.num_heads;
   const int64_t groups = (pairs + kXcds - 1) / kXcds;
   const int64_t nwg = groups * kXcds * a.num_qtiles;
   if (nwg > 0x7fffffff) return hipErrorInvalidValue;
   dim3 grid((unsigned)nwg);
   if (a.attn_bias)
-    launch_mask<D, true>(a, grid, stream);
+    launch_mask<D, NG, true>(a, grid, stream);
   else
-    launch_mask<D, false>(a, grid, stream);
+    launch_mask<D, NG, false>(a, grid, stream);
   return hipGetLastError();
 }
 
@@ -392,7 +434,8 @@ hipError_t launch_d(PrefillArgs a, hipStream_t stream) {
 
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream) {
   if (a.dtype != 0) return hipErrorInvalidValue;   // host API rejects bf16 first
-  return a.head_dim == 64 ? launch_d<64>(a, stream) : launch_d<128>(a, stream);
+  return a.head_dim == 64 ? launch_d<64, PA_PREFILL_GROUPS>(a, stream)
+                          : launch_d<128, 1>(a, stream);
 }
 
 }  // namespace pa
