@@ -178,7 +178,8 @@ def bench_decode(args):
         "roofline": {"bound": "hbm", "achieved": gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": gbps / HBM_PEAK_GBPS,
                      "traffic": traffic,
-                     "kernel": "paged_attn_decode call (pa_decode_partition + pa_decode_merge)"},
+                     "kernel": "paged_attn_decode call: pa_decode_partition" +
+                               ("" if ws is None else " + pa_decode_merge")},
     }
     if not args.no_variants:
         var = {}

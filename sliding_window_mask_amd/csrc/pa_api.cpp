@@ -45,9 +45,10 @@ int32_t default_partition(int32_t num_seqs, int32_t num_heads, int32_t max_seq_l
                           int32_t window) {
   const int32_t span = decode_span(max_seq_len, window);
   const int64_t pairs = (int64_t)num_seqs * num_heads;
-  // Aim for >= 2048 workgroups (8 per CU); never shorter than 128 tokens.
-  int32_t P = 512;
-  while (P > 128 && pairs * ((span + P - 1) / P) < 2048) P /= 2;
+  // Long partitions stream best (fewer partial blocks, no merge pass); split
+  // only until there are >= 4096 workgroups (16 per CU), never below 128.
+  int32_t P = pa::kMaxPartition;
+  while (P > 128 && pairs * ((span + P - 1) / P) < 4096) P /= 2;
   if (span <= P) P = span > 0 ? round_up16(span) : pa::kBlockSize;  // one partition
   return P;
 }
