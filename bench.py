@@ -11,8 +11,9 @@ Prints ONE JSON line. Options:
   --steps K       timed steps (default 20)
   --warmup W      untimed warm-up steps (default 5)
   --workload X    large_biased_decode_bf16 (default) | modernbert_prefill_f32 |
-                  copy_probe (a plain device copy of known size, for
-                  calibrating the rocprofv3 byte counters)
+                  t5_small_self_decode_bf16 | t5_large_cross_decode_bf16 (cold-cache
+                  median of single calls) | copy_probe (a plain device copy of
+                  known size, for calibrating the rocprofv3 byte counters)
   --no-cpu-baseline   skip the oracle timing
   --no-variants       skip the window / null-bias / no-bias-build variants
 """
@@ -266,6 +267,53 @@ def bench_copy(args):
             "steps": args.steps, "warmup": args.warmup, "n_gpus": 1}
 
 
+def bench_small_decode(args, name):
+    """T5-shaped decode workloads (small working sets: an L2 + Infinity Cache
+    flush precedes every timed call, and each call is timed on its own)."""
+    if name == "t5_small_self_decode_bf16":
+        case = workloads.t5_small_self_decode_bf16(device="cuda")
+    else:
+        case = workloads.t5_large_cross_decode_bf16(device="cuda", bias=None)
+    B, H, D = case.q.shape
+    lib = pa.lib()
+    out = torch.empty_like(case.q)
+    ws = lib.workspace_for(case.q, case.max_seq_len, case.sliding_window)
+    flush = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+
+    def call():
+        lib.paged_attn_decode(case.q, case.k_cache, case.v_cache, case.block_tables,
+                              case.context_lens, case.attn_bias, case.sliding_window,
+                              case.scale, max_seq_len=case.max_seq_len, out=out, workspace=ws)
+
+    for _ in range(args.warmup):
+        call()
+    times = []
+    for _ in range(args.steps):
+        flush.zero_()
+        s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        s.record()
+        call()
+        e.record()
+        torch.cuda.synchronize()
+        times.append(s.elapsed_time(e))
+    ms = float(np.median(times))
+    nbytes = decode_bytes(case.lens, H, D, 2, -1, case.attn_bias is not None)
+    gbps = nbytes / (ms * 1e-3) / 1e9
+    return {"metric": "decode tokens/s and achieved HBM GB/s (cold caches, median call)",
+            "value": B / (ms * 1e-3), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+            "warmup": args.warmup, "ms_per_step": ms, "p10_ms": float(np.percentile(times, 10)),
+            "p90_ms": float(np.percentile(times, 90)), "higher_is_better": True,
+            "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+            "config": {"workload": name, "num_seqs": B, "num_heads": H, "head_dim": D,
+                       "partition_tokens": lib.pa_decode_default_partition(
+                           B, H, D, case.max_seq_len, -1),
+                       "attn_bias": None if case.attn_bias is None else "fp32 (T5 buckets)"},
+            "roofline": {"bound": "hbm", "achieved": gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                         "frac": gbps / HBM_PEAK_GBPS, "traffic": None,
+                         "kernel": "paged_attn_decode call"},
+            "algorithmic_bytes_per_step": nbytes}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -286,6 +334,8 @@ def main():
         line = bench_decode(args)
     elif args.workload == "modernbert_prefill_f32":
         line = bench_prefill(args)
+    elif args.workload in ("t5_small_self_decode_bf16", "t5_large_cross_decode_bf16"):
+        line = bench_small_decode(args, args.workload)
     elif args.workload == "copy_probe":
         line = bench_copy(args)
     else:

@@ -55,6 +55,14 @@ def _load():
         lib.oracle_prefill_f64.restype = ctypes.c_int
         lib.oracle_prefill_f64.argtypes = [P, P, P, P, P, P, P, P, I32, I32, F64,
                                            I32, I32, I32, I32, I32, I32, I32]
+        lib.oracle_t5_bucket_array.restype = None
+        lib.oracle_t5_bucket_array.argtypes = [P, ctypes.c_int64, I32, I32, I32, P]
+        lib.oracle_decode_relpos_f64.restype = ctypes.c_int
+        lib.oracle_decode_relpos_f64.argtypes = [P, P, P, P, P, P, P, I32, I32, I32, I32, F64,
+                                                 I32, I32, I32, I32, I32, I32, I32]
+        lib.oracle_prefill_relpos_f64.restype = ctypes.c_int
+        lib.oracle_prefill_relpos_f64.argtypes = [P, P, P, P, P, P, P, P, I32, I32, I32, I32,
+                                                  I32, F64, I32, I32, I32, I32, I32, I32, I32]
         lib.oracle_num_threads.restype = ctypes.c_int
         _lib = lib
     return _lib
@@ -151,4 +159,54 @@ def prefill(q, k_cache, v_cache, block_tables, context_lens, query_start_loc, at
         bt.shape[1] if bt.ndim == 2 else 0, int(max_seq_len), dt)
     if rc != 0:
         raise ValueError("oracle_prefill_f64 rejected its arguments")
+    return out
+
+
+def t5_bucket(relative_position, bidirectional, num_buckets, max_distance):
+    """T5 relative-position buckets (float64 evaluation) of key - query positions."""
+    rp = np.ascontiguousarray(np.asarray(relative_position, dtype=np.int64))
+    out = np.empty(rp.shape, dtype=np.int32)
+    _load().oracle_t5_bucket_array(_ptr(rp), int(rp.size), int(bidirectional),
+                                   int(num_buckets), int(max_distance), _ptr(out))
+    return out
+
+
+def decode_relpos(q, k_cache, v_cache, block_tables, context_lens, rel_table, num_buckets,
+                  max_distance, bidirectional, sliding_window, scale, max_seq_len):
+    """Float64 decode with the bias a_j = rel_table[h][bucket(j - (L-1))]."""
+    dt = _kv_dtype(q)
+    qh, kh, vh = _host(q), _host(k_cache), _host(v_cache)
+    bt = _host(block_tables, np.int32)
+    cl = _host(context_lens, np.int32)
+    tab = _host(rel_table, np.float32)
+    B, H, D = qh.shape
+    out = np.zeros((B, H, D), dtype=np.float64)
+    rc = _load().oracle_decode_relpos_f64(
+        _ptr(out), _ptr(qh), _ptr(kh), _ptr(vh), _ptr(bt), _ptr(cl), _ptr(tab),
+        int(num_buckets), int(max_distance), int(bidirectional), int(sliding_window),
+        float(scale), B, H, D, kh.shape[2], bt.shape[1], int(max_seq_len), dt)
+    if rc != 0:
+        raise ValueError("oracle_decode_relpos_f64 rejected its arguments")
+    return out
+
+
+def prefill_relpos(q, k_cache, v_cache, block_tables, context_lens, query_start_loc, rel_table,
+                   num_buckets, max_distance, bidirectional, sliding_window, causal, scale,
+                   max_seq_len):
+    """Float64 prefill with the bias a(p, j) = rel_table[h][bucket(j - p)]."""
+    dt = _kv_dtype(q)
+    qh, kh, vh = _host(q), _host(k_cache), _host(v_cache)
+    bt = _host(block_tables, np.int32)
+    cl = _host(context_lens, np.int32)
+    qsl = _host(query_start_loc, np.int32)
+    tab = _host(rel_table, np.float32)
+    TQ, H, D = qh.shape
+    B = cl.shape[0]
+    out = np.zeros((TQ, H, D), dtype=np.float64)
+    rc = _load().oracle_prefill_relpos_f64(
+        _ptr(out), _ptr(qh), _ptr(kh), _ptr(vh), _ptr(bt), _ptr(cl), _ptr(qsl), _ptr(tab),
+        int(num_buckets), int(max_distance), int(bidirectional), int(sliding_window),
+        int(causal), float(scale), B, H, D, kh.shape[2], bt.shape[1], int(max_seq_len), dt)
+    if rc != 0:
+        raise ValueError("oracle_prefill_relpos_f64 rejected its arguments")
     return out

@@ -172,6 +172,143 @@ int oracle_prefill_f64(double* out, const void* q, const void* k_cache, const vo
   return 0;
 }
 
+/* ------------------------------------------------------------------------
+ * T5 relative-position bias
+ *
+ * "[Kernel][Model] PagedAttention: Support custom attention bias for T5
+ * model (1/2)" names an in-kernel computation of T5's relative-position bias
+ * as the model-specific alternative to a materialised bias, and its T5
+ * max-distance remark states that beyond the maximum distance (128 for T5)
+ * the last bias value is reused. The bucketing is T5's published one:
+ * relative position r = key position - query position; a bidirectional
+ * (encoder) bias gives keys after the query (r > 0) the upper half of the
+ * buckets and uses |r|, a unidirectional (decoder) bias uses max(-r, 0).
+ * With nb buckets in the half in use, distances below nb/2 get their own
+ * bucket; larger ones are spaced logarithmically up to max_distance, and
+ * every distance beyond lands in the last bucket. Evaluated in float64.
+ * ---------------------------------------------------------------------- */
+int oracle_t5_bucket(int64_t relative_position, int32_t bidirectional, int32_t num_buckets,
+                     int32_t max_distance) {
+  int32_t ret = 0, nb = num_buckets;
+  int64_t n;
+  if (bidirectional) {
+    nb = num_buckets / 2;
+    if (relative_position > 0) ret = nb;
+    n = relative_position < 0 ? -relative_position : relative_position;
+  } else {
+    n = relative_position < 0 ? -relative_position : 0;
+  }
+  int32_t max_exact = nb / 2;
+  if (n < max_exact) return ret + (int32_t)n;
+  double v = (double)max_exact + floor(log((double)n / (double)max_exact) /
+                                       log((double)max_distance / (double)max_exact) *
+                                       (double)(nb - max_exact));
+  int32_t b = v > (double)(nb - 1) ? nb - 1 : (int32_t)v;
+  return ret + b;
+}
+
+void oracle_t5_bucket_array(const int64_t* relative_position, int64_t n, int32_t bidirectional,
+                            int32_t num_buckets, int32_t max_distance, int32_t* out) {
+  for (int64_t i = 0; i < n; ++i)
+    out[i] = oracle_t5_bucket(relative_position[i], bidirectional, num_buckets, max_distance);
+}
+
+static int bad_relpos(int32_t num_buckets, int32_t max_distance, int32_t bidirectional) {
+  int32_t nb = bidirectional ? num_buckets / 2 : num_buckets;
+  if (bidirectional != 0 && bidirectional != 1) return 1;
+  if (num_buckets < 2 || (bidirectional && num_buckets % 2)) return 1;
+  if (nb / 2 < 1 || max_distance <= nb / 2) return 1;
+  return 0;
+}
+
+/* Decode with the bias taken from a T5 bucket table rel_table [H, num_buckets]:
+ * a_j = rel_table[h][bucket(j - (L-1))]; otherwise exactly oracle_decode_f64. */
+int oracle_decode_relpos_f64(double* out, const void* q, const void* k_cache, const void* v_cache,
+                             const int32_t* block_tables, const int32_t* context_lens,
+                             const float* rel_table, int32_t num_buckets, int32_t max_distance,
+                             int32_t bidirectional, int32_t sliding_window, double scale,
+                             int32_t num_seqs, int32_t num_heads, int32_t head_dim,
+                             int32_t block_size, int32_t max_blocks_per_seq, int32_t max_seq_len,
+                             int32_t dtype) {
+  if (bad_scalars(num_seqs, num_heads, head_dim, block_size, max_blocks_per_seq, max_seq_len,
+                  sliding_window, dtype) ||
+      bad_relpos(num_buckets, max_distance, bidirectional))
+    return -1;
+  for (int32_t b = 0; b < num_seqs; ++b)
+    if (context_lens[b] < 0 || context_lens[b] > max_seq_len) return -1;
+  int64_t pairs = (int64_t)num_seqs * num_heads;
+#pragma omp parallel
+  {
+    size_t n = (size_t)(max_seq_len > 0 ? max_seq_len : 1);
+    double* s = (double*)malloc(sizeof(double) * n);
+    float* a = (float*)malloc(sizeof(float) * n);
+#pragma omp for schedule(dynamic, 1)
+    for (int64_t bh = 0; bh < pairs; ++bh) {
+      int32_t b = (int32_t)(bh / num_heads), h = (int32_t)(bh % num_heads);
+      int32_t L = context_lens[b];
+      for (int32_t j = 0; j < L; ++j)
+        a[j] = rel_table[(int64_t)h * num_buckets +
+                         oracle_t5_bucket((int64_t)j - (L - 1), bidirectional, num_buckets,
+                                          max_distance)];
+      attend_row(out + bh * head_dim, q, bh * head_dim, k_cache, v_cache,
+                 block_tables + (int64_t)b * max_blocks_per_seq, a, L - 1, L, sliding_window, 0,
+                 scale, h, num_heads, head_dim, block_size, dtype, s);
+    }
+    free(s);
+    free(a);
+  }
+  return 0;
+}
+
+/* Prefill with the T5 bias: a(p, j) = rel_table[h][bucket(j - p)]. */
+int oracle_prefill_relpos_f64(double* out, const void* q, const void* k_cache,
+                              const void* v_cache, const int32_t* block_tables,
+                              const int32_t* context_lens, const int32_t* query_start_loc,
+                              const float* rel_table, int32_t num_buckets, int32_t max_distance,
+                              int32_t bidirectional, int32_t sliding_window, int32_t causal,
+                              double scale, int32_t num_seqs, int32_t num_heads,
+                              int32_t head_dim, int32_t block_size, int32_t max_blocks_per_seq,
+                              int32_t max_seq_len, int32_t dtype) {
+  if (bad_scalars(num_seqs, num_heads, head_dim, block_size, max_blocks_per_seq, max_seq_len,
+                  sliding_window, dtype) ||
+      bad_relpos(num_buckets, max_distance, bidirectional))
+    return -1;
+  if (causal != 0 && causal != 1) return -1;
+  for (int32_t b = 0; b < num_seqs; ++b) {
+    int32_t nq = query_start_loc[b + 1] - query_start_loc[b];
+    if (context_lens[b] < 0 || context_lens[b] > max_seq_len || nq < 0 || nq > context_lens[b])
+      return -1;
+  }
+  int64_t pairs = (int64_t)num_seqs * num_heads;
+#pragma omp parallel
+  {
+    size_t n = (size_t)(max_seq_len > 0 ? max_seq_len : 1);
+    double* s = (double*)malloc(sizeof(double) * n);
+    float* a = (float*)malloc(sizeof(float) * n);
+#pragma omp for schedule(dynamic, 1)
+    for (int64_t bh = 0; bh < pairs; ++bh) {
+      int32_t b = (int32_t)(bh / num_heads), h = (int32_t)(bh % num_heads);
+      int32_t L = context_lens[b];
+      int32_t q0 = query_start_loc[b];
+      int32_t nq = query_start_loc[b + 1] - q0;
+      for (int32_t t = 0; t < nq; ++t) {
+        int32_t p = L - nq + t;
+        for (int32_t j = 0; j < L; ++j)
+          a[j] = rel_table[(int64_t)h * num_buckets +
+                           oracle_t5_bucket((int64_t)j - p, bidirectional, num_buckets,
+                                            max_distance)];
+        int64_t row = ((int64_t)(q0 + t) * num_heads + h) * head_dim;
+        attend_row(out + row, q, row, k_cache, v_cache,
+                   block_tables + (int64_t)b * max_blocks_per_seq, a, p, L, sliding_window,
+                   causal, scale, h, num_heads, head_dim, block_size, dtype, s);
+      }
+    }
+    free(s);
+    free(a);
+  }
+  return 0;
+}
+
 int oracle_num_threads(void) {
 #ifdef _OPENMP
   return omp_get_max_threads();

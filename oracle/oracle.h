@@ -66,6 +66,32 @@ int oracle_prefill_f64(double* out, const void* q, const void* k_cache, const vo
                        int32_t block_size, int32_t max_blocks_per_seq, int32_t max_seq_len,
                        int32_t dtype);
 
+/* T5 relative-position bucket of relative_position = key - query position
+ * (see oracle.c for the definition); bidirectional 0 (decoder) or 1
+ * (encoder). The array form fills out[i] for relative_position[i]. */
+int oracle_t5_bucket(int64_t relative_position, int32_t bidirectional, int32_t num_buckets,
+                     int32_t max_distance);
+void oracle_t5_bucket_array(const int64_t* relative_position, int64_t n, int32_t bidirectional,
+                            int32_t num_buckets, int32_t max_distance, int32_t* out);
+
+/* Decode / prefill with the bias computed from a T5 bucket table
+ * rel_table [num_heads, num_buckets] (fp32): a(p, j) = rel_table[h][bucket(j - p)]. */
+int oracle_decode_relpos_f64(double* out, const void* q, const void* k_cache, const void* v_cache,
+                             const int32_t* block_tables, const int32_t* context_lens,
+                             const float* rel_table, int32_t num_buckets, int32_t max_distance,
+                             int32_t bidirectional, int32_t sliding_window, double scale,
+                             int32_t num_seqs, int32_t num_heads, int32_t head_dim,
+                             int32_t block_size, int32_t max_blocks_per_seq, int32_t max_seq_len,
+                             int32_t dtype);
+int oracle_prefill_relpos_f64(double* out, const void* q, const void* k_cache,
+                              const void* v_cache, const int32_t* block_tables,
+                              const int32_t* context_lens, const int32_t* query_start_loc,
+                              const float* rel_table, int32_t num_buckets, int32_t max_distance,
+                              int32_t bidirectional, int32_t sliding_window, int32_t causal,
+                              double scale, int32_t num_seqs, int32_t num_heads,
+                              int32_t head_dim, int32_t block_size, int32_t max_blocks_per_seq,
+                              int32_t max_seq_len, int32_t dtype);
+
 /* Number of OpenMP threads the oracle uses (for reporting). */
 int oracle_num_threads(void);
 

@@ -345,3 +345,72 @@ def test_oracle_rejects_bad_scalars():
     with pytest.raises(ValueError):
         oracle.decode(case.q, case.k_cache, case.v_cache, case.block_tables,
                       case.context_lens, None, -1, 1.0, 8)       # L > max_seq_len
+
+
+# ----------------------------------------------------------------------------
+# T5 relative-position bias (in-oracle bucketing)
+# ----------------------------------------------------------------------------
+def test_t5_bucket_closed_forms_unidirectional():
+    # 32 buckets, max distance 128, decoder: exact below 16; beyond, bucket
+    # 16 + floor(16 * log(n/16) / log(8)). log(2)/log(8) = 1/3 and
+    # log(4)/log(8) = 2/3 exactly, so n = 32 -> 16 + 5 and n = 64 -> 16 + 10.
+    rp = -np.array([0, 1, 15, 16, 32, 64, 112, 113, 128, 1000])       # keys before the query
+    want = [0, 1, 15, 16, 21, 26, 30, 31, 31, 31]
+    assert oracle.t5_bucket(rp, 0, 32, 128).tolist() == want
+    # keys after the query (never visible to a causal decoder) share bucket 0
+    assert oracle.t5_bucket([1, 5, 500], 0, 32, 128).tolist() == [0, 0, 0]
+
+
+def test_t5_bucket_closed_forms_bidirectional():
+    # 16 buckets per side, exact below 8; log(n/8)/log(16) is 1/4, 1/2, 3/4, 1
+    # for n = 16, 32, 64, 128: buckets 8 + 2, 8 + 4, 8 + 6, then the clamp 15.
+    n = np.array([0, 7, 8, 16, 32, 64, 128, 5000])
+    assert oracle.t5_bucket(-n, 1, 32, 128).tolist() == [0, 7, 8, 10, 12, 14, 15, 15]
+    # keys after the query use the upper half, with the same spacing
+    pos = n[n > 0]
+    assert (oracle.t5_bucket(pos, 1, 32, 128) - oracle.t5_bucket(-pos, 1, 32, 128)
+            == 16).all()
+
+
+def test_t5_bucket_monotone_and_last_value_beyond_max_distance():
+    d = np.arange(0, 3000)
+    for bidir in (0, 1):
+        b = oracle.t5_bucket(-d, bidir, 32, 128)
+        assert np.all(np.diff(b) >= 0)
+        assert np.all(b[128:] == b[128])
+        assert b[128] == (15 if bidir else 31)
+
+
+def test_t5_bucket_matches_input_generator():
+    # the generator's numpy bucketing (used to materialise T5 biases) and the
+    # oracle's C bucketing are written independently; they must agree
+    d = np.arange(0, 5000)
+    assert np.array_equal(oracle.t5_bucket(-d, 0, 32, 128), workloads.t5_bucket(d))
+
+
+def test_decode_relpos_equals_materialised_bias_bit_exact():
+    case = workloads.decode_case(91, num_seqs=5, num_heads=3, head_dim=16, lens=(1, 200),
+                                 max_seq_len=208, dtype=torch.bfloat16, bias="t5")
+    dense = run_decode(case)
+    inline = oracle.decode_relpos(case.q, case.k_cache, case.v_cache, case.block_tables,
+                                  case.context_lens, case.t5_table, 32, 128, 0, -1,
+                                  case.scale, case.max_seq_len)
+    np.testing.assert_array_equal(inline, dense)
+
+
+@pytest.mark.parametrize("bidir", [0, 1])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("window", [-1, 9])
+def test_prefill_relpos_equals_sdpa(bidir, causal, window):
+    case = small_prefill(92 + bidir, bias=None, window=window, causal=causal,
+                         lens=[40, 150, 7], max_seq_len=160)
+    tab = torch.randn(case.num_heads, 32, generator=torch.Generator().manual_seed(5)) * 0.5
+    got = oracle.prefill_relpos(case.q, case.k_cache, case.v_cache, case.block_tables,
+                                case.context_lens, case.query_start_loc, tab, 32, 128, bidir,
+                                window, int(causal), case.scale, case.max_seq_len)
+    # dense bias built from the bucket map, checked through SDPA
+    pos = np.arange(case.max_seq_len)
+    buckets = oracle.t5_bucket(pos[None, :] - pos[:, None], bidir, 32, 128)   # [p, j]
+    dense = tab[:, torch.from_numpy(buckets.astype(np.int64))]                 # [H, MS, MS]
+    case.attn_bias = dense[None].expand(case.num_seqs, -1, -1, -1).contiguous()
+    np.testing.assert_allclose(got, sdpa_prefill(case), rtol=0, atol=1e-12)
