@@ -192,6 +192,15 @@ def bench_decode(args):
         bn = decode_bytes(case.lens, H, D, 2, -1, False)
         var["null_bias"] = {"ms_per_step": msn, "tokens_per_s": B / (msn * 1e-3),
                             "GBps": bn / (msn * 1e-3) / 1e9}
+        # the same shape with a T5 bias computed in the kernel (32 buckets,
+        # max distance 128) instead of the materialised [256, 32, 4096] stream
+        t5_tab = torch.randn(H, 32, device="cuda") * 0.5
+        msr = time_steps(lambda: lib.paged_attn_decode_relpos(
+            case.q, case.k_cache, case.v_cache, case.block_tables, case.context_lens, t5_tab,
+            32, 128, 0, -1, case.scale, max_seq_len=case.max_seq_len, out=out, workspace=ws),
+            args.steps, args.warmup)
+        var["t5_bias_in_kernel"] = {"ms_per_step": msr, "tokens_per_s": B / (msr * 1e-3),
+                                    "GBps": bn / (msr * 1e-3) / 1e9}
         if os.path.exists(pa.LIB_NOBIAS_PATH):
             nob = pa.PagedAttnLib(pa.LIB_NOBIAS_PATH)
             msb = time_steps(lambda: step(bias=None, which=nob), args.steps, args.warmup)
@@ -298,6 +307,25 @@ def bench_small_decode(args, name):
         times.append(s.elapsed_time(e))
     ms = float(np.median(times))
     nbytes = decode_bytes(case.lens, H, D, 2, -1, case.attn_bias is not None)
+    extra = {}
+    if case.t5_table is not None:
+        # the same T5 bias computed in the kernel from the [8, 32] bucket table
+        rt = []
+        for _ in range(args.steps):
+            flush.zero_()
+            s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            s.record()
+            lib.paged_attn_decode_relpos(case.q, case.k_cache, case.v_cache, case.block_tables,
+                                         case.context_lens, case.t5_table, 32, 128, 0, -1,
+                                         case.scale, max_seq_len=case.max_seq_len, out=out,
+                                         workspace=ws)
+            e.record()
+            torch.cuda.synchronize()
+            rt.append(s.elapsed_time(e))
+        mr = float(np.median(rt))
+        extra["t5_bias_in_kernel"] = {"ms_per_step": mr, "tokens_per_s": B / (mr * 1e-3),
+                                      "GBps": decode_bytes(case.lens, H, D, 2, -1, False) /
+                                      (mr * 1e-3) / 1e9}
     gbps = nbytes / (ms * 1e-3) / 1e9
     return {"metric": "decode tokens/s and achieved HBM GB/s (cold caches, median call)",
             "value": B / (ms * 1e-3), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
@@ -311,7 +339,7 @@ def bench_small_decode(args, name):
             "roofline": {"bound": "hbm", "achieved": gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                          "frac": gbps / HBM_PEAK_GBPS, "traffic": None,
                          "kernel": "paged_attn_decode call"},
-            "algorithmic_bytes_per_step": nbytes}
+            "algorithmic_bytes_per_step": nbytes, "variants": extra}
 
 
 def main():

@@ -46,8 +46,10 @@
  *     (synchronously) and range-checked first;
  *   - work is enqueued asynchronously on `stream` (a hipStream_t; NULL = the
  *     default stream); device faults surface at the caller's next sync;
- *   - the library allocates nothing and keeps no state between calls; calls
- *     on different streams with distinct outputs/workspaces may overlap.
+ *   - the library allocates nothing and keeps no state between calls that
+ *     could change a result (only a per-thread memo of the T5 bucket
+ *     thresholds, a pure function of the bucket shape); calls on different
+ *     streams with distinct outputs/workspaces may overlap.
  */
 #ifndef PAGED_ATTN_H
 #define PAGED_ATTN_H
@@ -156,6 +158,57 @@ pa_status_t paged_attn_prefill(void* out, const void* q, const void* k_cache,
                                int32_t max_blocks_per_seq, int32_t max_seq_len,
                                int64_t num_blocks, int64_t total_q, pa_dtype_t dtype,
                                void* stream);
+
+/*
+ * In-kernel T5 relative-position bias: the same decode / prefill, with the
+ * bias of key j for a query at position p computed from a bucket table
+ * instead of read from a materialised matrix — the model-specific
+ * alternative named in "[Kernel][Model] PagedAttention: Support custom
+ * attention bias for T5 model (1/2)" (PR description, and its T5
+ * max-distance remark: beyond the maximum distance the last value is reused).
+ *
+ *   a(p, j) = rel_table[h * num_buckets + bucket(j - p)]
+ *
+ * T5 bucketing of r = j - p: a unidirectional (decoder) table uses
+ * n = max(-r, 0) over all num_buckets buckets; a bidirectional (encoder)
+ * table gives r > 0 the upper half (offset num_buckets/2) and uses n = |r|.
+ * Within a direction of `half` buckets, n < half/2 is its own bucket; larger
+ * n get half/2 + floor(log(n / (half/2)) / log(max_distance / (half/2)) *
+ * (half - half/2)), capped at half - 1, evaluated in float64 on the host.
+ * Scores are (q.k + a) * scale as with a materialised bias, so a table whose
+ * buckets reproduce a materialised bias gives the identical result.
+ *
+ *   rel_table      fp32 [num_heads, num_buckets], device memory, not NULL
+ *   num_buckets    2..64 (even when bidirectional); T5 uses 32
+ *   max_distance   (half/2, 1024]; T5 uses 128
+ *   bidirectional  0 (decoder self-attention) or 1 (encoder)
+ * Everything else as for paged_attn_decode / paged_attn_prefill (there is no
+ * attn_bias argument). Errors as there, plus INVALID_ARG / NULL_POINTER /
+ * MISALIGNED for the table arguments.
+ */
+pa_status_t paged_attn_decode_relpos(void* out, const void* q, const void* k_cache,
+                                     const void* v_cache, const int32_t* block_tables,
+                                     const int32_t* context_lens, const float* rel_table,
+                                     int32_t num_buckets, int32_t max_distance,
+                                     int32_t bidirectional, int32_t sliding_window, float scale,
+                                     int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
+                                     int32_t head_dim, int32_t block_size,
+                                     int32_t max_blocks_per_seq, int32_t max_seq_len,
+                                     int64_t num_blocks, pa_dtype_t dtype,
+                                     int32_t partition_tokens, void* workspace,
+                                     size_t workspace_bytes, void* stream);
+
+pa_status_t paged_attn_prefill_relpos(void* out, const void* q, const void* k_cache,
+                                      const void* v_cache, const int32_t* block_tables,
+                                      const int32_t* context_lens,
+                                      const int32_t* query_start_loc, const float* rel_table,
+                                      int32_t num_buckets, int32_t max_distance,
+                                      int32_t bidirectional, int32_t sliding_window,
+                                      int32_t causal, float scale, int32_t num_seqs,
+                                      int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
+                                      int32_t block_size, int32_t max_blocks_per_seq,
+                                      int32_t max_seq_len, int64_t num_blocks, int64_t total_q,
+                                      pa_dtype_t dtype, void* stream);
 
 /*
  * Host-side range check of decode/prefill metadata held in HOST memory (the

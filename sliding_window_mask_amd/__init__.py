@@ -9,6 +9,8 @@ library is not built, or a call fails, an exception is raised.
 Functions mirror the C entry points:
   paged_attn_decode(...)         decoder self-attention / cross-attention decode
   paged_attn_prefill(...)        encoder-only (bidirectional) or causal prefill
+  paged_attn_decode_relpos(...)  decode with the T5 relative-position bias in-kernel
+  paged_attn_prefill_relpos(...) prefill with the T5 relative-position bias in-kernel
   pa_decode_workspace_bytes(...)
   pa_decode_default_partition(...)
   pa_check_metadata(...)         host-side range check of lengths / tables
@@ -84,6 +86,14 @@ class PagedAttnLib:
         lib.paged_attn_prefill.restype = ctypes.c_int
         lib.paged_attn_prefill.argtypes = [P, P, P, P, P, P, P, P, I32, I32, F32, I32, I32,
                                            I32, I32, I32, I32, I32, I64, I64, ctypes.c_int, P]
+        lib.paged_attn_decode_relpos.restype = ctypes.c_int
+        lib.paged_attn_decode_relpos.argtypes = [P, P, P, P, P, P, P, I32, I32, I32, I32, F32,
+                                                 I32, I32, I32, I32, I32, I32, I32, I64,
+                                                 ctypes.c_int, I32, P, SZ, P]
+        lib.paged_attn_prefill_relpos.restype = ctypes.c_int
+        lib.paged_attn_prefill_relpos.argtypes = [P, P, P, P, P, P, P, P, I32, I32, I32, I32,
+                                                  I32, F32, I32, I32, I32, I32, I32, I32, I32,
+                                                  I64, I64, ctypes.c_int, P]
         lib.pa_check_metadata.restype = ctypes.c_int
         lib.pa_check_metadata.argtypes = [P, P, P, I32, I32, I32, I32, I32, I64, I64]
         self._lib = lib
@@ -173,6 +183,43 @@ class PagedAttnLib:
             _dtype_code(q), _stream(stream)))
         return out
 
+    def paged_attn_decode_relpos(self, q, k_cache, v_cache, block_tables, context_lens,
+                                 rel_table, num_buckets, max_distance, bidirectional,
+                                 sliding_window, scale, *, max_seq_len, out=None,
+                                 workspace=None, partition_tokens=0, stream=None):
+        """Decode with the T5 relative-position bias computed in the kernel from
+        rel_table [H, num_buckets] (fp32); see include/paged_attn.h."""
+        B, H, D = q.shape
+        if out is None:
+            out = torch.empty_like(q)
+        if workspace is None:
+            workspace = self.workspace_for(q, max_seq_len, sliding_window, partition_tokens)
+        ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+        self._check(self._lib.paged_attn_decode_relpos(
+            _ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables),
+            _ptr(context_lens), _ptr(rel_table), int(num_buckets), int(max_distance),
+            int(bidirectional), int(sliding_window), float(scale), B, H, k_cache.shape[1], D,
+            k_cache.shape[2], block_tables.shape[1], int(max_seq_len), k_cache.shape[0],
+            _dtype_code(q), int(partition_tokens), _ptr(workspace), ws_bytes, _stream(stream)))
+        return out
+
+    def paged_attn_prefill_relpos(self, q, k_cache, v_cache, block_tables, context_lens,
+                                  query_start_loc, rel_table, num_buckets, max_distance,
+                                  bidirectional, sliding_window, causal, scale, *, max_seq_len,
+                                  out=None, stream=None):
+        """Prefill with the T5 relative-position bias computed in the kernel."""
+        TQ, H, D = q.shape
+        if out is None:
+            out = torch.empty_like(q)
+        self._check(self._lib.paged_attn_prefill_relpos(
+            _ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables),
+            _ptr(context_lens), _ptr(query_start_loc), _ptr(rel_table), int(num_buckets),
+            int(max_distance), int(bidirectional), int(sliding_window), int(bool(causal)),
+            float(scale), context_lens.shape[0], H, k_cache.shape[1], D, k_cache.shape[2],
+            block_tables.shape[1], int(max_seq_len), k_cache.shape[0], TQ, _dtype_code(q),
+            _stream(stream)))
+        return out
+
 
 _default = None
 
@@ -191,6 +238,14 @@ def paged_attn_decode(*args, **kwargs):
 
 def paged_attn_prefill(*args, **kwargs):
     return lib().paged_attn_prefill(*args, **kwargs)
+
+
+def paged_attn_decode_relpos(*args, **kwargs):
+    return lib().paged_attn_decode_relpos(*args, **kwargs)
+
+
+def paged_attn_prefill_relpos(*args, **kwargs):
+    return lib().paged_attn_prefill_relpos(*args, **kwargs)
 
 
 def pa_decode_workspace_bytes(*args, **kwargs):

@@ -121,6 +121,68 @@ pa_status_t check_common(const void* out, const void* q, const void* k, const vo
   return PA_OK;
 }
 
+// T5 bucket of a non-negative distance within one direction, in float64 (the
+// precision the bucket decision is taken in): exact below max_exact, then
+// max_exact + floor(log(n / max_exact) / log(max_distance / max_exact) *
+// (half - max_exact)), capped at half - 1.
+int32_t rel_half_bucket_f64(int64_t n, int32_t half, int32_t max_exact, int32_t max_distance) {
+  if (n < max_exact) return (int32_t)n;
+  const double v = (double)max_exact +
+                   std::floor(std::log((double)n / (double)max_exact) /
+                              std::log((double)max_distance / (double)max_exact) *
+                              (double)(half - max_exact));
+  return v > (double)(half - 1) ? half - 1 : (int32_t)v;
+}
+
+// Fill the kernel-side description of a T5 bias: thresholds thr[k] = the
+// smallest distance whose bucket is >= max_exact + 1 + k. Memoised per
+// thread on (half, max_distance): a pure function of the bucket shape.
+pa_status_t make_relpos(const float* table, int32_t num_buckets, int32_t max_distance,
+                        int32_t bidirectional, pa::RelPos* r) {
+  if (!table) return fail(PA_ERR_NULL_POINTER, "rel_table is NULL");
+  if (!aligned(table, 4)) return fail(PA_ERR_MISALIGNED, "rel_table must be 4-byte aligned");
+  if (bidirectional != 0 && bidirectional != 1)
+    return fail(PA_ERR_INVALID_ARG, "bidirectional must be 0 or 1");
+  if (num_buckets < 2 || num_buckets > 2 * pa::kMaxRelThresholds ||
+      (bidirectional && num_buckets % 2 != 0))
+    return fail(PA_ERR_INVALID_ARG, "num_buckets %d: use 2..%d (even when bidirectional)",
+                num_buckets, 2 * pa::kMaxRelThresholds);
+  const int32_t half = bidirectional ? num_buckets / 2 : num_buckets;
+  const int32_t max_exact = half / 2;
+  if (max_exact < 1)
+    return fail(PA_ERR_INVALID_ARG, "num_buckets %d leaves no exact bucket", num_buckets);
+  if (max_distance <= max_exact || max_distance > pa::kMaxRelDistance)
+    return fail(PA_ERR_INVALID_ARG, "max_distance %d: use (%d, %d]", max_distance, max_exact,
+                pa::kMaxRelDistance);
+  struct Memo {
+    int32_t half = -1, max_distance = -1, nthr = 0;
+    int32_t thr[pa::kMaxRelThresholds];
+  };
+  static thread_local Memo memo;
+  if (memo.half != half || memo.max_distance != max_distance) {
+    int32_t nthr = 0, cur = max_exact;
+    for (int64_t n = max_exact; n <= max_distance && cur < half - 1; ++n) {
+      const int32_t bk = rel_half_bucket_f64(n, half, max_exact, max_distance);
+      while (cur < bk && cur < half - 1) {   // buckets cur+1 .. bk start at n
+        memo.thr[nthr++] = (int32_t)n;
+        ++cur;
+      }
+    }
+    memo.half = half;
+    memo.max_distance = max_distance;
+    memo.nthr = nthr;
+  }
+  r->table = table;
+  r->num_buckets = num_buckets;
+  r->half = half;
+  r->max_exact = max_exact;
+  r->max_distance = max_distance;
+  r->bidirectional = bidirectional;
+  r->nthr = memo.nthr;
+  for (int32_t k = 0; k < memo.nthr; ++k) r->thr[k] = memo.thr[k];
+  return PA_OK;
+}
+
 bool validate_env() {
   const char* e = std::getenv("PA_VALIDATE");
   return e && e[0] && std::strcmp(e, "0") != 0;
@@ -218,15 +280,18 @@ pa_status_t pa_check_metadata(const int32_t* block_tables, const int32_t* contex
   return ok();
 }
 
-pa_status_t paged_attn_decode(void* out, const void* q, const void* k_cache,
-                              const void* v_cache, const int32_t* block_tables,
-                              const int32_t* context_lens, const float* attn_bias,
-                              int32_t sliding_window, float scale, int32_t num_seqs,
-                              int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
-                              int32_t block_size, int32_t max_blocks_per_seq,
-                              int32_t max_seq_len, int64_t num_blocks, pa_dtype_t dtype,
-                              int32_t partition_tokens, void* workspace,
-                              size_t workspace_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+pa_status_t decode_impl(void* out, const void* q, const void* k_cache, const void* v_cache,
+                        const int32_t* block_tables, const int32_t* context_lens,
+                        const float* attn_bias, const pa::RelPos* rel, int32_t sliding_window,
+                        float scale, int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
+                        int32_t head_dim, int32_t block_size, int32_t max_blocks_per_seq,
+                        int32_t max_seq_len, int64_t num_blocks, pa_dtype_t dtype,
+                        int32_t partition_tokens, void* workspace, size_t workspace_bytes,
+                        void* stream) {
   pa_status_t st = check_common(out, q, k_cache, v_cache, block_tables, context_lens, attn_bias,
                                 sliding_window, scale, num_seqs, num_heads, num_kv_heads,
                                 head_dim, block_size, max_blocks_per_seq, max_seq_len,
@@ -272,6 +337,7 @@ pa_status_t paged_attn_decode(void* out, const void* q, const void* k_cache,
   a.dtype = (int32_t)dtype;
   a.partition = plan.partition;
   a.num_partitions = plan.num_partitions;
+  if (rel) a.rel = *rel;
   if (plan.ws_bytes > 0) {
     char* ws = static_cast<char*>(workspace);
     a.ws_o = reinterpret_cast<float*>(ws);
@@ -283,15 +349,14 @@ pa_status_t paged_attn_decode(void* out, const void* q, const void* k_cache,
   return ok();
 }
 
-pa_status_t paged_attn_prefill(void* out, const void* q, const void* k_cache,
-                               const void* v_cache, const int32_t* block_tables,
-                               const int32_t* context_lens, const int32_t* query_start_loc,
-                               const float* attn_bias, int32_t sliding_window, int32_t causal,
-                               float scale, int32_t num_seqs, int32_t num_heads,
-                               int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
-                               int32_t max_blocks_per_seq, int32_t max_seq_len,
-                               int64_t num_blocks, int64_t total_q, pa_dtype_t dtype,
-                               void* stream) {
+pa_status_t prefill_impl(void* out, const void* q, const void* k_cache, const void* v_cache,
+                         const int32_t* block_tables, const int32_t* context_lens,
+                         const int32_t* query_start_loc, const float* attn_bias,
+                         const pa::RelPos* rel, int32_t sliding_window, int32_t causal,
+                         float scale, int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
+                         int32_t head_dim, int32_t block_size, int32_t max_blocks_per_seq,
+                         int32_t max_seq_len, int64_t num_blocks, int64_t total_q,
+                         pa_dtype_t dtype, void* stream) {
   pa_status_t st = check_common(out, q, k_cache, v_cache, block_tables, context_lens, attn_bias,
                                 sliding_window, scale, num_seqs, num_heads, num_kv_heads,
                                 head_dim, block_size, max_blocks_per_seq, max_seq_len,
@@ -331,9 +396,84 @@ pa_status_t paged_attn_prefill(void* out, const void* q, const void* k_cache,
   a.max_blocks = max_blocks_per_seq;
   a.max_seq_len = max_seq_len;
   a.dtype = (int32_t)dtype;
+  if (rel) a.rel = *rel;
   hipError_t e = pa::launch_prefill(a, s);
   if (e != hipSuccess) return fail(PA_ERR_HIP, "prefill launch failed: %s", hipGetErrorString(e));
   return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+pa_status_t paged_attn_decode(void* out, const void* q, const void* k_cache,
+                              const void* v_cache, const int32_t* block_tables,
+                              const int32_t* context_lens, const float* attn_bias,
+                              int32_t sliding_window, float scale, int32_t num_seqs,
+                              int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
+                              int32_t block_size, int32_t max_blocks_per_seq,
+                              int32_t max_seq_len, int64_t num_blocks, pa_dtype_t dtype,
+                              int32_t partition_tokens, void* workspace,
+                              size_t workspace_bytes, void* stream) {
+  return decode_impl(out, q, k_cache, v_cache, block_tables, context_lens, attn_bias, nullptr,
+                     sliding_window, scale, num_seqs, num_heads, num_kv_heads, head_dim,
+                     block_size, max_blocks_per_seq, max_seq_len, num_blocks, dtype,
+                     partition_tokens, workspace, workspace_bytes, stream);
+}
+
+pa_status_t paged_attn_decode_relpos(void* out, const void* q, const void* k_cache,
+                                     const void* v_cache, const int32_t* block_tables,
+                                     const int32_t* context_lens, const float* rel_table,
+                                     int32_t num_buckets, int32_t max_distance,
+                                     int32_t bidirectional, int32_t sliding_window, float scale,
+                                     int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
+                                     int32_t head_dim, int32_t block_size,
+                                     int32_t max_blocks_per_seq, int32_t max_seq_len,
+                                     int64_t num_blocks, pa_dtype_t dtype,
+                                     int32_t partition_tokens, void* workspace,
+                                     size_t workspace_bytes, void* stream) {
+  pa::RelPos rel{};
+  pa_status_t st = make_relpos(rel_table, num_buckets, max_distance, bidirectional, &rel);
+  if (st != PA_OK) return st;
+  return decode_impl(out, q, k_cache, v_cache, block_tables, context_lens, nullptr, &rel,
+                     sliding_window, scale, num_seqs, num_heads, num_kv_heads, head_dim,
+                     block_size, max_blocks_per_seq, max_seq_len, num_blocks, dtype,
+                     partition_tokens, workspace, workspace_bytes, stream);
+}
+
+pa_status_t paged_attn_prefill(void* out, const void* q, const void* k_cache,
+                               const void* v_cache, const int32_t* block_tables,
+                               const int32_t* context_lens, const int32_t* query_start_loc,
+                               const float* attn_bias, int32_t sliding_window, int32_t causal,
+                               float scale, int32_t num_seqs, int32_t num_heads,
+                               int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                               int32_t max_blocks_per_seq, int32_t max_seq_len,
+                               int64_t num_blocks, int64_t total_q, pa_dtype_t dtype,
+                               void* stream) {
+  return prefill_impl(out, q, k_cache, v_cache, block_tables, context_lens, query_start_loc,
+                      attn_bias, nullptr, sliding_window, causal, scale, num_seqs, num_heads,
+                      num_kv_heads, head_dim, block_size, max_blocks_per_seq, max_seq_len,
+                      num_blocks, total_q, dtype, stream);
+}
+
+pa_status_t paged_attn_prefill_relpos(void* out, const void* q, const void* k_cache,
+                                      const void* v_cache, const int32_t* block_tables,
+                                      const int32_t* context_lens,
+                                      const int32_t* query_start_loc, const float* rel_table,
+                                      int32_t num_buckets, int32_t max_distance,
+                                      int32_t bidirectional, int32_t sliding_window,
+                                      int32_t causal, float scale, int32_t num_seqs,
+                                      int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
+                                      int32_t block_size, int32_t max_blocks_per_seq,
+                                      int32_t max_seq_len, int64_t num_blocks, int64_t total_q,
+                                      pa_dtype_t dtype, void* stream) {
+  pa::RelPos rel{};
+  pa_status_t st = make_relpos(rel_table, num_buckets, max_distance, bidirectional, &rel);
+  if (st != PA_OK) return st;
+  return prefill_impl(out, q, k_cache, v_cache, block_tables, context_lens, query_start_loc,
+                      nullptr, &rel, sliding_window, causal, scale, num_seqs, num_heads,
+                      num_kv_heads, head_dim, block_size, max_blocks_per_seq, max_seq_len,
+                      num_blocks, total_q, dtype, stream);
 }
 
 }  // extern "C"

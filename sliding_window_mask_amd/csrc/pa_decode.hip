@@ -176,7 +176,9 @@ __device__ __forceinline__ void store_out(void* out, int64_t idx, float v) {
 // ---------------------------------------------------------------------------
 // kernel 1: one partition of one (sequence, head)
 // ---------------------------------------------------------------------------
-template <int DT, int D, bool HAS_BIAS, bool SINGLE>
+// BIAS: 0 none, 1 materialised row attn_bias[b, h, :], 2 T5 relative-position
+// bias from a bucket table (a.rel).
+template <int DT, int D, int BIAS, bool SINGLE>
 __global__ void __launch_bounds__(kDecodeThreads)
 pa_decode_partition(DecodeArgs a) {
   using G = Geo<DT, D>;
@@ -202,13 +204,15 @@ pa_decode_partition(DecodeArgs a) {
   const int nblk = (t1 - t0 + kBlockSize - 1) / kBlockSize;
   const int nb0 = t0 / kBlockSize;                     // first logical block
 
-  // LDS: q slices | reductions | per-wave outputs | scores | block ids
+  // LDS: q slices | reductions | per-wave outputs | scores | block ids |
+  //      relative-position bias by distance (BIAS == 2)
   extern __shared__ uint4 smem_u4[];
   uint4* q_lds = smem_u4;                              // [LPT] 16-byte slices
   float* red_lds = reinterpret_cast<float*>(q_lds + G::kLPT);   // [8]
   float* o_lds = red_lds + 8;                          // [4][D]
   float* s_lds = o_lds + kDecodeWaves * D;             // [P] scores, then weights
   int* tbl_lds = reinterpret_cast<int*>(s_lds + P);    // [P/16] physical ids
+  float* rel_lds = reinterpret_cast<float*>(tbl_lds + P / kBlockSize);  // [max_distance + 1]
 
   // stage q and the block-table slice
   const int64_t row = (int64_t)b * H + h;
@@ -217,6 +221,13 @@ pa_decode_partition(DecodeArgs a) {
         static_cast<const char*>(a.q) + row * G::kRowBytes)[tid];
   const int32_t* table = a.block_tables + (int64_t)b * a.max_blocks + nb0;
   for (int i = tid; i < nblk; i += kDecodeThreads) tbl_lds[i] = table[i];
+  if constexpr (BIAS == 2) {
+    // bias of a key at distance d = (L-1) - j before the query, d <= max_distance
+    // (every longer distance shares the last bucket)
+    const float* head_row = a.rel.table + (int64_t)h * a.rel.num_buckets;
+    for (int d = tid; d <= a.rel.max_distance; d += kDecodeThreads)
+      rel_lds[d] = rel_bias(-d, a.rel, head_row);
+  }
   __syncthreads();
 
   const int seg = lane % G::kLPT;
@@ -229,14 +240,14 @@ pa_decode_partition(DecodeArgs a) {
   // ---- K pass: raw dot products into s_lds ----
   // (bias entries of this thread's first tokens are requested first, so they
   // arrive while the keys stream in)
-  const float* bias_row = HAS_BIAS ? a.attn_bias + row * a.max_seq_len : nullptr;
+  const float* bias_row = BIAS == 1 ? a.attn_bias + row * a.max_seq_len : nullptr;
   const int ntok = nblk * kBlockSize;
   float bpre[kBiasPre];
 #pragma unroll
   for (int k = 0; k < kBiasPre; ++k) {
     const int j = t0 + tid + k * kDecodeThreads;
     bpre[k] = 0.0f;
-    if (HAS_BIAS && tid + k * kDecodeThreads < ntok && j >= lo && j < L) bpre[k] = bias_row[j];
+    if (BIAS == 1 && tid + k * kDecodeThreads < ntok && j >= lo && j < L) bpre[k] = bias_row[j];
   }
   for (int n0 = wave; n0 < nblk; n0 += kUnroll * kDecodeWaves) {
     int64_t ph[kUnroll];
@@ -278,7 +289,8 @@ pa_decode_partition(DecodeArgs a) {
       float s = -INFINITY;
       if (j >= lo && j < L) {
         float t = s_lds[i];
-        if constexpr (HAS_BIAS) t = t + bpre[k];
+        if constexpr (BIAS == 1) t = t + bpre[k];
+        if constexpr (BIAS == 2) t = t + rel_lds[min(L - 1 - j, a.rel.max_distance)];
         s = t * a.scale_log2;
       }
       s_lds[i] = s;
@@ -290,7 +302,8 @@ pa_decode_partition(DecodeArgs a) {
     float s = -INFINITY;
     if (j >= lo && j < L) {
       float t = s_lds[i];
-      if constexpr (HAS_BIAS) t = t + bias_row[j];
+      if constexpr (BIAS == 1) t = t + bias_row[j];
+      if constexpr (BIAS == 2) t = t + rel_lds[min(L - 1 - j, a.rel.max_distance)];
       s = t * a.scale_log2;
     }
     s_lds[i] = s;
@@ -411,19 +424,20 @@ __global__ void __launch_bounds__(D) pa_decode_merge(DecodeArgs a) {
   store_out<DT>(a.out, row * D + tid, den > 0.0f ? num / den : 0.0f);
 }
 
-template <int DT, int D, bool HAS_BIAS>
+template <int DT, int D, int BIAS>
 hipError_t launch_typed(const DecodeArgs& a, hipStream_t stream) {
   using G = Geo<DT, D>;
-  const size_t lds = sizeof(float) * a.partition + sizeof(int) * (a.partition / kBlockSize) +
-                     sizeof(float) * (kDecodeWaves * D + 8) + 16 * G::kLPT;
+  size_t lds = sizeof(float) * a.partition + sizeof(int) * (a.partition / kBlockSize) +
+               sizeof(float) * (kDecodeWaves * D + 8) + 16 * G::kLPT;
+  if (BIAS == 2) lds += sizeof(float) * (a.rel.max_distance + 1);
   dim3 grid(a.num_heads, a.num_partitions, a.num_seqs);
   if (a.num_partitions == 1) {
-    hipLaunchKernelGGL((pa_decode_partition<DT, D, HAS_BIAS, true>), grid,
-                       dim3(kDecodeThreads), lds, stream, a);
+    hipLaunchKernelGGL((pa_decode_partition<DT, D, BIAS, true>), grid, dim3(kDecodeThreads),
+                       lds, stream, a);
     return hipGetLastError();
   }
-  hipLaunchKernelGGL((pa_decode_partition<DT, D, HAS_BIAS, false>), grid,
-                     dim3(kDecodeThreads), lds, stream, a);
+  hipLaunchKernelGGL((pa_decode_partition<DT, D, BIAS, false>), grid, dim3(kDecodeThreads), lds,
+                     stream, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL((pa_decode_merge<DT, D>), dim3((unsigned)a.num_seqs * a.num_heads),
@@ -433,11 +447,11 @@ hipError_t launch_typed(const DecodeArgs& a, hipStream_t stream) {
 
 template <int DT, int D>
 hipError_t launch_bias(const DecodeArgs& a, hipStream_t stream) {
+  if (a.rel.table) return launch_typed<DT, D, 2>(a, stream);
 #ifdef PA_NO_BIAS
-  return launch_typed<DT, D, false>(a, stream);
+  return launch_typed<DT, D, 0>(a, stream);
 #else
-  return a.attn_bias ? launch_typed<DT, D, true>(a, stream)
-                     : launch_typed<DT, D, false>(a, stream);
+  return a.attn_bias ? launch_typed<DT, D, 1>(a, stream) : launch_typed<DT, D, 0>(a, stream);
 #endif
 }
 

@@ -12,6 +12,26 @@ constexpr int kDecodeThreads = 256;   // 4 wave64s per decode workgroup
 constexpr int kDecodeWaves = kDecodeThreads / 64;
 constexpr int kMaxPartition = 4096;   // tokens per split-K partition, upper bound
 
+constexpr int kMaxRelThresholds = 32; // relative-position bucket thresholds
+constexpr int kMaxRelDistance = 1024;  // largest supported max_distance
+
+// T5 relative-position bias, in the form the kernels use: the bias of key j
+// for a query at position p is table[h * num_buckets + bucket(j - p)], where
+// for r = j - p <= 0 the bucket is half_bucket(-r), and for r > 0 it is
+// half + half_bucket(r) (bidirectional) or 0 (unidirectional).
+// half_bucket(n) = n for n < max_exact, else max_exact + #{k : n >= thr[k]}.
+// The host derives thr from the float64 bucket formula.
+struct RelPos {
+  const float* table;          // [num_heads, num_buckets] fp32, or null
+  int32_t num_buckets;         // buckets per head (both directions)
+  int32_t half;                // buckets per direction
+  int32_t max_exact;           // distances with a bucket of their own
+  int32_t max_distance;        // every distance >= this shares the last bucket
+  int32_t bidirectional;
+  int32_t nthr;
+  int32_t thr[kMaxRelThresholds];
+};
+
 // Arguments of one decode call, as validated by the host API.
 struct DecodeArgs {
   void* out;
@@ -30,6 +50,7 @@ struct DecodeArgs {
   float* ws_m;                // [B*H*NP] running max (base 2), or null
   float* ws_l;                // [B*H*NP] running sum
   float* ws_o;                // [B*H*NP*D] unnormalised outputs
+  RelPos rel;                 // used when rel.table is set (attn_bias is then null)
 };
 
 struct PrefillArgs {
@@ -47,7 +68,26 @@ struct PrefillArgs {
   int32_t num_seqs, num_heads, head_dim, max_blocks, max_seq_len;
   int32_t dtype;
   int32_t num_qtiles;         // query tiles per sequence in the grid (set by the launcher)
+  RelPos rel;                 // used when rel.table is set (attn_bias is then null)
 };
+
+// Bucket of a non-negative distance within one direction (see RelPos).
+__device__ __forceinline__ int rel_half_bucket(int n, const RelPos& r) {
+  if (n < r.max_exact) return n;
+  int b = r.max_exact;
+  for (int k = 0; k < r.nthr; ++k) b += n >= r.thr[k] ? 1 : 0;
+  return b;
+}
+
+// Bias value of relative position rel = key - query position for one head.
+__device__ __forceinline__ float rel_bias(int rel, const RelPos& r, const float* head_row) {
+  int bucket;
+  if (rel > 0)
+    bucket = r.bidirectional ? r.half + rel_half_bucket(rel, r) : 0;
+  else
+    bucket = rel_half_bucket(-rel, r);
+  return head_row[bucket];
+}
 
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream);

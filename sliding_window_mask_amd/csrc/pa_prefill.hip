@@ -84,7 +84,9 @@ __device__ __forceinline__ void key_range(int p0, int p1, int L, int window, int
   }
 }
 
-template <int D, int NG, bool HAS_BIAS, bool CAUSAL, bool WINDOW>
+// BIAS: 0 none, 1 materialised attn_bias[b, h, p, j], 2 T5 relative-position
+// bias from a bucket table (a.rel).
+template <int D, int NG, int BIAS, bool CAUSAL, bool WINDOW>
 __global__ void __launch_bounds__(kThreads)
 pa_prefill_f32(PrefillArgs a) {
   constexpr int kKTile = key_tile<D>();
@@ -168,6 +170,15 @@ pa_prefill_f32(PrefillArgs a) {
   }
 
   __shared__ float kv_lds[2][2][kKTile * kRow];      // [buffer][K, V][row * kRow + col]
+  // T5 bias of relative position r = j - p, for r in [-max_distance, max_distance]
+  // (longer distances share the end buckets), pre-multiplied by scale * log2(e)
+  __shared__ float rel_lds[BIAS == 2 ? 2 * kMaxRelDistance + 1 : 1];
+  const int rel_md = BIAS == 2 ? a.rel.max_distance : 0;
+  if constexpr (BIAS == 2) {
+    const float* head_row = a.rel.table + (int64_t)h * a.rel.num_buckets;
+    for (int i = tid; i <= 2 * rel_md; i += kThreads)
+      rel_lds[i] = rel_bias(i - rel_md, a.rel, head_row) * a.scale_log2;
+  }
 
   const float* kc = static_cast<const float*>(a.k_cache);
   const float* vc = static_cast<const float*>(a.v_cache);
@@ -234,7 +245,7 @@ pa_prefill_f32(PrefillArgs a) {
     l_run[q] = 0.0f;
     // rows past n_q point at the tile's first row and are masked, so every
     // bias read is in bounds
-    bias_row[q] = HAS_BIAS ? a.attn_bias + (((int64_t)b * H + h) * a.max_seq_len +
+    bias_row[q] = BIAS == 1 ? a.attn_bias + (((int64_t)b * H + h) * a.max_seq_len +
                                             (row_ok[q] ? p[q] : pos0 + t_first)) *
                                                a.max_seq_len
                            : nullptr;
@@ -286,10 +297,15 @@ pa_prefill_f32(PrefillArgs a) {
           const int c0 = base + ch * 16;
           const int j0 = c0 + 4 * g;
           // bias (added as a * scale * log2(e): the same sum as (q.k + a) * scale)
-          if constexpr (HAS_BIAS) {
+          if constexpr (BIAS == 1) {
 #pragma unroll
             for (int r = 0; r < 4; ++r)
               s[q][ch][r] = s[q][ch][r] + bias_row[q][min(j0 + r, L - 1)] * cs;
+          }
+          if constexpr (BIAS == 2) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+              s[q][ch][r] = s[q][ch][r] + rel_lds[min(max(j0 + r - p[q], -rel_md), rel_md) + rel_md];
           }
           // per-element mask only where some row of the group does not see
           // the whole chunk (sequence end, window edges, diagonal)
@@ -395,21 +411,21 @@ pa_prefill_f32(PrefillArgs a) {
   }
 }
 
-template <int D, int NG, bool HAS_BIAS>
+template <int D, int NG, int BIAS>
 void launch_mask(const PrefillArgs& a, dim3 grid, hipStream_t stream) {
   if (a.causal) {
     if (a.window > 0)
-      hipLaunchKernelGGL((pa_prefill_f32<D, NG, HAS_BIAS, true, true>), grid, dim3(kThreads), 0,
+      hipLaunchKernelGGL((pa_prefill_f32<D, NG, BIAS, true, true>), grid, dim3(kThreads), 0,
                          stream, a);
     else
-      hipLaunchKernelGGL((pa_prefill_f32<D, NG, HAS_BIAS, true, false>), grid, dim3(kThreads),
+      hipLaunchKernelGGL((pa_prefill_f32<D, NG, BIAS, true, false>), grid, dim3(kThreads),
                          0, stream, a);
   } else {
     if (a.window > 0)
-      hipLaunchKernelGGL((pa_prefill_f32<D, NG, HAS_BIAS, false, true>), grid, dim3(kThreads),
+      hipLaunchKernelGGL((pa_prefill_f32<D, NG, BIAS, false, true>), grid, dim3(kThreads),
                          0, stream, a);
     else
-      hipLaunchKernelGGL((pa_prefill_f32<D, NG, HAS_BIAS, false, false>), grid, dim3(kThreads),
+      hipLaunchKernelGGL((pa_prefill_f32<D, NG, BIAS, false, false>), grid, dim3(kThreads),
                          0, stream, a);
   }
 }
@@ -423,10 +439,12 @@ hipError_t launch_d(PrefillArgs a, hipStream_t stream) {
   const int64_t nwg = groups * kXcds * a.num_qtiles;
   if (nwg > 0x7fffffff) return hipErrorInvalidValue;
   dim3 grid((unsigned)nwg);
-  if (a.attn_bias)
-    launch_mask<D, NG, true>(a, grid, stream);
+  if (a.rel.table)
+    launch_mask<D, NG, 2>(a, grid, stream);
+  else if (a.attn_bias)
+    launch_mask<D, NG, 1>(a, grid, stream);
   else
-    launch_mask<D, NG, false>(a, grid, stream);
+    launch_mask<D, NG, 0>(a, grid, stream);
   return hipGetLastError();
 }
 

@@ -166,3 +166,37 @@ def test_check_metadata_host():
 def test_binding_fails_loudly_without_library(tmp_path):
     with pytest.raises(RuntimeError):
         pa.PagedAttnLib(str(tmp_path / "missing.so"))
+
+
+def relpos_decode_call(lib, **kw):
+    a = dict(out=FAKE, q=FAKE, k=FAKE, v=FAKE, bt=FAKE, cl=FAKE, tab=FAKE, nb=32, md=128,
+             bidir=0, window=-1, scale=0.125, B=4, H=4, Hkv=4, D=64, bs=16, maxb=8, msl=128,
+             nblk=64, dtype=0, part=0, ws=None, wsb=0, stream=None)
+    a.update(kw)
+    return lib._lib.paged_attn_decode_relpos(
+        a["out"], a["q"], a["k"], a["v"], a["bt"], a["cl"], a["tab"], a["nb"], a["md"],
+        a["bidir"], a["window"], a["scale"], a["B"], a["H"], a["Hkv"], a["D"], a["bs"],
+        a["maxb"], a["msl"], a["nblk"], a["dtype"], a["part"], a["ws"], a["wsb"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(tab=None), 1), (dict(tab=FAKE + 2), 4), (dict(bidir=2), 2), (dict(nb=1), 2),
+    (dict(nb=31, bidir=1), 2), (dict(nb=66), 2), (dict(md=16), 2), (dict(md=1025), 2),
+    (dict(nb=2, bidir=1), 2), (dict(D=96), 3), (dict(window=0), 2),
+])
+def test_decode_relpos_rejects_on_host(kw, status):
+    lib = pa.lib()
+    st = relpos_decode_call(lib, **kw)
+    assert st == status, (st, lib.pa_last_error())
+
+
+def test_prefill_relpos_rejects_on_host():
+    lib = pa.lib()
+    st = lib._lib.paged_attn_prefill_relpos(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, 32,
+                                            128, 1, -1, 0, 0.125, 2, 4, 4, 64, 16, 8, 128, 64,
+                                            10, 0, None)
+    assert st == 1
+    st = lib._lib.paged_attn_prefill_relpos(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 32,
+                                            4, 1, -1, 0, 0.125, 2, 4, 4, 64, 16, 8, 128, 64, 10,
+                                            0, None)
+    assert st == 2     # max_distance must exceed the exact range (8 for 16 buckets a side)
