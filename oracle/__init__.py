@@ -63,6 +63,9 @@ def _load():
         lib.oracle_prefill_relpos_f64.restype = ctypes.c_int
         lib.oracle_prefill_relpos_f64.argtypes = [P, P, P, P, P, P, P, P, I32, I32, I32, I32,
                                                   I32, F64, I32, I32, I32, I32, I32, I32, I32]
+        lib.oracle_kv_write.restype = ctypes.c_int
+        lib.oracle_kv_write.argtypes = [P, P, P, P, P, ctypes.c_int64, I32, I32, I32,
+                                        ctypes.c_int64, I32]
         lib.oracle_num_threads.restype = ctypes.c_int
         _lib = lib
     return _lib
@@ -210,3 +213,20 @@ def prefill_relpos(q, k_cache, v_cache, block_tables, context_lens, query_start_
     if rc != 0:
         raise ValueError("oracle_prefill_relpos_f64 rejected its arguments")
     return out
+
+
+def kv_write(k_cache, v_cache, k_new, v_new, slot_mapping):
+    """Return copies of the host caches with the new rows scattered in.
+
+    k_cache, v_cache [num_blocks, H, block_size, D]; k_new, v_new [T, H, D];
+    slot_mapping int64 [T] (block * block_size + offset, negative = skip)."""
+    dt = _kv_dtype(k_cache)
+    kc, vc = _host(k_cache).copy(), _host(v_cache).copy()
+    kn, vn = _host(k_new), _host(v_new)
+    sm = _host(slot_mapping, np.int64)
+    nb, H, bs, D = kc.shape
+    rc = _load().oracle_kv_write(_ptr(kc), _ptr(vc), _ptr(kn), _ptr(vn), _ptr(sm),
+                                 int(sm.shape[0]), H, D, bs, nb, dt)
+    if rc != 0:
+        raise ValueError("oracle_kv_write rejected its arguments")
+    return kc, vc

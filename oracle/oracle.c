@@ -309,6 +309,37 @@ int oracle_prefill_relpos_f64(double* out, const void* q, const void* k_cache,
   return 0;
 }
 
+/* ------------------------------------------------------------------------
+ * KV-cache write: the step before decode. Token t's keys and values (all
+ * heads) go to physical slot slot_mapping[t] = block * block_size + offset
+ * of the paged caches (the block-table layout of "Add Encoder-decoder model
+ * support and T5 Model support"); a negative slot means "skip this token".
+ * Element-by-element copy; slots must be distinct.
+ * ---------------------------------------------------------------------- */
+int oracle_kv_write(void* k_cache, void* v_cache, const void* k_new, const void* v_new,
+                    const int64_t* slot_mapping, int64_t num_tokens, int32_t num_heads,
+                    int32_t head_dim, int32_t block_size, int64_t num_blocks, int32_t dtype) {
+  if (num_tokens < 0 || num_heads < 1 || head_dim < 1 || block_size < 1 || num_blocks < 0 ||
+      (dtype != 0 && dtype != 1))
+    return -1;
+  const size_t es = dtype == 0 ? 4 : 2;
+  for (int64_t t = 0; t < num_tokens; ++t) {
+    int64_t slot = slot_mapping[t];
+    if (slot < 0) continue;
+    if (slot >= num_blocks * block_size) return -1;
+    int64_t blk = slot / block_size, off = slot % block_size;
+    for (int32_t h = 0; h < num_heads; ++h) {
+      int64_t src = ((int64_t)t * num_heads + h) * head_dim;
+      int64_t dst = ((blk * num_heads + h) * block_size + off) * head_dim;
+      for (int32_t d = 0; d < head_dim; ++d) {
+        memcpy((char*)k_cache + (dst + d) * es, (const char*)k_new + (src + d) * es, es);
+        memcpy((char*)v_cache + (dst + d) * es, (const char*)v_new + (src + d) * es, es);
+      }
+    }
+  }
+  return 0;
+}
+
 int oracle_num_threads(void) {
 #ifdef _OPENMP
   return omp_get_max_threads();

@@ -92,6 +92,13 @@ int oracle_prefill_relpos_f64(double* out, const void* q, const void* k_cache,
                               int32_t head_dim, int32_t block_size, int32_t max_blocks_per_seq,
                               int32_t max_seq_len, int32_t dtype);
 
+/* Scatter num_tokens new key/value rows [num_tokens, num_heads, head_dim]
+ * into the paged caches at physical slots slot_mapping[t] (block * block_size
+ * + offset; negative = skip). Returns -1 on a slot outside the pool. */
+int oracle_kv_write(void* k_cache, void* v_cache, const void* k_new, const void* v_new,
+                    const int64_t* slot_mapping, int64_t num_tokens, int32_t num_heads,
+                    int32_t head_dim, int32_t block_size, int64_t num_blocks, int32_t dtype);
+
 /* Number of OpenMP threads the oracle uses (for reporting). */
 int oracle_num_threads(void);
 

@@ -414,3 +414,40 @@ def test_prefill_relpos_equals_sdpa(bidir, causal, window):
     dense = tab[:, torch.from_numpy(buckets.astype(np.int64))]                 # [H, MS, MS]
     case.attn_bias = dense[None].expand(case.num_seqs, -1, -1, -1).contiguous()
     np.testing.assert_allclose(got, sdpa_prefill(case), rtol=0, atol=1e-12)
+
+
+# ----------------------------------------------------------------------------
+# KV-cache write (scatter through the slot mapping)
+# ----------------------------------------------------------------------------
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+def test_kv_write_reads_back_through_the_table(dtype):
+    g = torch.Generator().manual_seed(3)
+    nb, H, D, T = 9, 3, 8, 40
+    k = torch.randn(nb, H, BS, D, generator=g).to(dtype)
+    v = torch.randn(nb, H, BS, D, generator=g).to(dtype)
+    kn = torch.randn(T, H, D, generator=g).to(dtype)
+    vn = torch.randn(T, H, D, generator=g).to(dtype)
+    table = torch.tensor([6, 2, 8], dtype=torch.int32)          # logical blocks of one sequence
+    slots = (table[torch.arange(T) // BS].long() * BS + torch.arange(T) % BS)
+    slots[[3, 17]] = -1                                         # skipped tokens
+    kc, vc = oracle.kv_write(k, v, kn, vn, slots)
+    kc, vc = torch.from_numpy(kc), torch.from_numpy(vc)
+    if dtype == torch.bfloat16:
+        kc, vc = kc.view(torch.bfloat16), vc.view(torch.bfloat16)
+    got_k = unpage(kc, table, T).permute(1, 0, 2)              # [T, H, D]
+    got_v = unpage(vc, table, T).permute(1, 0, 2)
+    keep = slots >= 0
+    assert torch.equal(got_k[keep], kn[keep].double())
+    assert torch.equal(got_v[keep], vn[keep].double())
+    # skipped tokens and untouched blocks keep their old contents
+    old_k = unpage(k, table, T).permute(1, 0, 2)
+    assert torch.equal(got_k[~keep], old_k[~keep])
+    for blk in set(range(nb)) - {6, 2, 8}:
+        assert torch.equal(kc[blk], k[blk]) and torch.equal(vc[blk], v[blk])
+
+
+def test_kv_write_rejects_slots_outside_the_pool():
+    k = torch.zeros(2, 1, BS, 4)
+    with pytest.raises(ValueError):
+        oracle.kv_write(k, k, torch.zeros(1, 1, 4), torch.zeros(1, 1, 4),
+                        torch.tensor([2 * BS], dtype=torch.int64))
