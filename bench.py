@@ -12,7 +12,7 @@ Prints ONE JSON line. Options:
   --warmup W      untimed warm-up steps (default 5)
   --workload X    large_biased_decode_bf16 (default) | modernbert_prefill_f32 |
                   t5_small_self_decode_bf16 | t5_large_cross_decode_bf16 (cold-cache
-                  median of single calls) | copy_probe (a plain device copy of
+                  median of single calls) | kv_write_modernbert_f32 | copy_probe (a plain device copy of
                   known size, for calibrating the rocprofv3 byte counters)
   --no-cpu-baseline   skip the oracle timing
   --no-variants       skip the window / null-bias / no-bias-build variants
@@ -342,6 +342,35 @@ def bench_small_decode(args, name):
             "algorithmic_bytes_per_step": nbytes, "variants": extra}
 
 
+def bench_kv_write(args):
+    """KV-cache write of a whole ModernBERT-shaped prompt batch (32 sequences,
+    L ~ U[64,1024], 12 heads, D = 64, fp32) into a randomly permuted block
+    pool: algorithmic bytes = k_new + v_new read + the same written."""
+    case = workloads.modernbert_prefill_f32(0, device="cuda")
+    T, H, D = case.q.shape
+    L = case.lens
+    bt = case.block_tables.cpu()
+    slots = torch.cat([bt[b, torch.arange(int(L[b])) // 16].long() * 16 +
+                       torch.arange(int(L[b])) % 16 for b in range(case.num_seqs)]).to("cuda")
+    kn = torch.randn(T, H, D, device="cuda")
+    vn = torch.randn(T, H, D, device="cuda")
+    lib = pa.lib()
+    ms = time_steps(lambda: lib.paged_kv_write(case.k_cache, case.v_cache, kn, vn, slots),
+                    args.steps, args.warmup)
+    nbytes = 2 * 2 * T * H * D * 4
+    gbps = nbytes / (ms * 1e-3) / 1e9
+    return {"metric": "KV-cache write GB/s", "value": gbps, "unit": "GB/s", "n_gpus": 1,
+            "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms,
+            "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+            "data": "synthetic",
+            "config": {"workload": "kv_write_modernbert_f32", "tokens": T, "num_heads": H,
+                       "head_dim": D},
+            "roofline": {"bound": "hbm", "achieved": gbps, "peak": HBM_PEAK_GBPS,
+                         "unit": "GB/s", "frac": gbps / HBM_PEAK_GBPS, "traffic": None,
+                         "kernel": "pa_kv_write"},
+            "algorithmic_bytes_per_step": nbytes}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -364,6 +393,8 @@ def main():
         line = bench_prefill(args)
     elif args.workload in ("t5_small_self_decode_bf16", "t5_large_cross_decode_bf16"):
         line = bench_small_decode(args, args.workload)
+    elif args.workload == "kv_write_modernbert_f32":
+        line = bench_kv_write(args)
     elif args.workload == "copy_probe":
         line = bench_copy(args)
     else:

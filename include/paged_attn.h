@@ -211,6 +211,37 @@ pa_status_t paged_attn_prefill_relpos(void* out, const void* q, const void* k_ca
                                       pa_dtype_t dtype, void* stream);
 
 /*
+ * KV-cache write, the step that precedes decode: token t's keys and values
+ * (all heads) are stored at physical slot slot_mapping[t] = block * 16 +
+ * offset of the paged caches (layout above; the block tables themselves are
+ * the caller's). A negative slot skips the token. Slots must be distinct
+ * within one call (otherwise the surviving row is unspecified).
+ *
+ *   k_cache, v_cache  [num_blocks, num_kv_heads, 16, head_dim], dtype (written)
+ *   k_new, v_new      [num_tokens, num_heads, head_dim], dtype, 16-byte aligned
+ *   slot_mapping      int64 [num_tokens], device memory, 8-byte aligned
+ *   num_blocks        rows of the caches (PA_VALIDATE range-checks the slots)
+ * Errors: NULL_POINTER, INVALID_ARG, UNSUPPORTED, MISALIGNED, HIP.
+ * num_tokens == 0 returns PA_OK without launching.
+ */
+pa_status_t paged_kv_write(void* k_cache, void* v_cache, const void* k_new, const void* v_new,
+                           const int64_t* slot_mapping, int64_t num_tokens, int32_t num_heads,
+                           int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                           int64_t num_blocks, pa_dtype_t dtype, void* stream);
+
+/*
+ * Sliding-window eviction: the first logical block a decode query of a
+ * sequence with context_len tokens (query at context_len - 1) can read under
+ * sliding_window; every later decode step of the same sequence starts at or
+ * after it. Blocks before it will never be read again by paged_attn_decode
+ * with this window and may be freed or reused (their block-table entries are
+ * never read either) — the condition under which "[V1] Add sliding window
+ * support to Flex Attention backend" (end-to-end remark) lets in-window
+ * iteration skip evicted blocks. 0 when there is no window. No HIP call.
+ */
+int32_t pa_window_first_live_block(int32_t context_len, int32_t sliding_window);
+
+/*
  * Host-side range check of decode/prefill metadata held in HOST memory (the
  * check PA_VALIDATE=1 runs on copies): every L in [0, max_seq_len], every
  * block-table entry that backs a visible token in [0, num_blocks), and, when

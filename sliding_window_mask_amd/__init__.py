@@ -11,6 +11,8 @@ Functions mirror the C entry points:
   paged_attn_prefill(...)        encoder-only (bidirectional) or causal prefill
   paged_attn_decode_relpos(...)  decode with the T5 relative-position bias in-kernel
   paged_attn_prefill_relpos(...) prefill with the T5 relative-position bias in-kernel
+  paged_kv_write(...)            scatter new tokens' K/V into the paged caches
+  pa_window_first_live_block(...) first block a windowed decode still reads
   pa_decode_workspace_bytes(...)
   pa_decode_default_partition(...)
   pa_check_metadata(...)         host-side range check of lengths / tables
@@ -94,6 +96,11 @@ class PagedAttnLib:
         lib.paged_attn_prefill_relpos.argtypes = [P, P, P, P, P, P, P, P, I32, I32, I32, I32,
                                                   I32, F32, I32, I32, I32, I32, I32, I32, I32,
                                                   I64, I64, ctypes.c_int, P]
+        lib.paged_kv_write.restype = ctypes.c_int
+        lib.paged_kv_write.argtypes = [P, P, P, P, P, I64, I32, I32, I32, I32, I64,
+                                       ctypes.c_int, P]
+        lib.pa_window_first_live_block.restype = I32
+        lib.pa_window_first_live_block.argtypes = [I32, I32]
         lib.pa_check_metadata.restype = ctypes.c_int
         lib.pa_check_metadata.argtypes = [P, P, P, I32, I32, I32, I32, I32, I64, I64]
         self._lib = lib
@@ -220,6 +227,18 @@ class PagedAttnLib:
             _stream(stream)))
         return out
 
+    def paged_kv_write(self, k_cache, v_cache, k_new, v_new, slot_mapping, *, stream=None):
+        """Scatter k_new, v_new [T,H,D] into the paged caches at slot_mapping
+        (int64 [T], block * 16 + offset; negative = skip)."""
+        T, H, D = k_new.shape
+        self._check(self._lib.paged_kv_write(
+            _ptr(k_cache), _ptr(v_cache), _ptr(k_new), _ptr(v_new), _ptr(slot_mapping), T, H,
+            k_cache.shape[1], D, k_cache.shape[2], k_cache.shape[0], _dtype_code(k_cache),
+            _stream(stream)))
+
+    def pa_window_first_live_block(self, context_len, sliding_window) -> int:
+        return int(self._lib.pa_window_first_live_block(int(context_len), int(sliding_window)))
+
 
 _default = None
 
@@ -246,6 +265,14 @@ def paged_attn_decode_relpos(*args, **kwargs):
 
 def paged_attn_prefill_relpos(*args, **kwargs):
     return lib().paged_attn_prefill_relpos(*args, **kwargs)
+
+
+def paged_kv_write(*args, **kwargs):
+    return lib().paged_kv_write(*args, **kwargs)
+
+
+def pa_window_first_live_block(*args, **kwargs):
+    return lib().pa_window_first_live_block(*args, **kwargs)
 
 
 def pa_decode_workspace_bytes(*args, **kwargs):

@@ -45,10 +45,12 @@ int32_t default_partition(int32_t num_seqs, int32_t num_heads, int32_t max_seq_l
                           int32_t window) {
   const int32_t span = decode_span(max_seq_len, window);
   const int64_t pairs = (int64_t)num_seqs * num_heads;
-  // Long partitions stream best (fewer partial blocks, no merge pass); split
-  // only until there are >= 4096 workgroups (16 per CU), never below 128.
+  // Long partitions stream best (fewer partial blocks, no merge launch):
+  // split only until there are >= 512 workgroups (2 per CU), never below
+  // 128 tokens. Measured on MI355X: one partition per (sequence, head) is
+  // fastest from 512 pairs up (T5-small decode 14.6 us vs 19.1 us at P=128).
   int32_t P = pa::kMaxPartition;
-  while (P > 128 && pairs * ((span + P - 1) / P) < 4096) P /= 2;
+  while (P > 128 && pairs * ((span + P - 1) / P) < 512) P /= 2;
   if (span <= P) P = span > 0 ? round_up16(span) : pa::kBlockSize;  // one partition
   return P;
 }
@@ -474,6 +476,64 @@ pa_status_t paged_attn_prefill_relpos(void* out, const void* q, const void* k_ca
                       nullptr, &rel, sliding_window, causal, scale, num_seqs, num_heads,
                       num_kv_heads, head_dim, block_size, max_blocks_per_seq, max_seq_len,
                       num_blocks, total_q, dtype, stream);
+}
+
+int32_t pa_window_first_live_block(int32_t context_len, int32_t sliding_window) {
+  if (context_len <= 0 || sliding_window <= 0 || context_len <= sliding_window) return 0;
+  return (context_len - sliding_window) / pa::kBlockSize;
+}
+
+pa_status_t paged_kv_write(void* k_cache, void* v_cache, const void* k_new, const void* v_new,
+                           const int64_t* slot_mapping, int64_t num_tokens, int32_t num_heads,
+                           int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                           int64_t num_blocks, pa_dtype_t dtype, void* stream) {
+  if (dtype != PA_DTYPE_F32 && dtype != PA_DTYPE_BF16)
+    return fail(PA_ERR_UNSUPPORTED, "dtype %d is not supported (0 = fp32, 1 = bf16)", (int)dtype);
+  if (head_dim != 64 && head_dim != 128)
+    return fail(PA_ERR_UNSUPPORTED, "head_dim %d is not supported (64 or 128)", head_dim);
+  if (block_size != pa::kBlockSize)
+    return fail(PA_ERR_UNSUPPORTED, "block_size %d is not supported (16)", block_size);
+  if (num_heads < 1 || num_heads > 65535)
+    return fail(PA_ERR_INVALID_ARG, "num_heads %d out of range [1, 65535]", num_heads);
+  if (num_kv_heads != num_heads)
+    return fail(PA_ERR_UNSUPPORTED, "num_kv_heads (%d) must equal num_heads (%d)", num_kv_heads,
+                num_heads);
+  if (num_tokens < 0 || num_tokens > 0x7fffffff || num_blocks < 0)
+    return fail(PA_ERR_INVALID_ARG, "num_tokens %lld / num_blocks %lld out of range",
+                (long long)num_tokens, (long long)num_blocks);
+  if (num_tokens == 0) return ok();
+  if (!k_cache || !v_cache || !k_new || !v_new || !slot_mapping)
+    return fail(PA_ERR_NULL_POINTER, "a required pointer is NULL");
+  if (!aligned(k_cache, 16) || !aligned(v_cache, 16) || !aligned(k_new, 16) ||
+      !aligned(v_new, 16) || !aligned(slot_mapping, 8))
+    return fail(PA_ERR_MISALIGNED, "caches and new rows must be 16-byte aligned, "
+                "slot_mapping 8-byte aligned");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (validate_env()) {
+    std::vector<int64_t> hs(num_tokens);
+    hipError_t e = hipMemcpyAsync(hs.data(), slot_mapping, sizeof(int64_t) * num_tokens,
+                                  hipMemcpyDeviceToHost, s);
+    if (e == hipSuccess) e = hipStreamSynchronize(s);
+    if (e != hipSuccess)
+      return fail(PA_ERR_HIP, "PA_VALIDATE copy failed: %s", hipGetErrorString(e));
+    for (int64_t t = 0; t < num_tokens; ++t)
+      if (hs[t] >= num_blocks * pa::kBlockSize)
+        return fail(PA_ERR_INVALID_ARG, "slot_mapping[%lld] = %lld outside the %lld-slot pool",
+                    (long long)t, (long long)hs[t], (long long)(num_blocks * pa::kBlockSize));
+  }
+  pa::KvWriteArgs a{};
+  a.k_cache = k_cache;
+  a.v_cache = v_cache;
+  a.k_new = k_new;
+  a.v_new = v_new;
+  a.slot_mapping = slot_mapping;
+  a.num_tokens = num_tokens;
+  a.num_heads = num_heads;
+  a.head_dim = head_dim;
+  a.dtype = (int32_t)dtype;
+  hipError_t e = pa::launch_kv_write(a, s);
+  if (e != hipSuccess) return fail(PA_ERR_HIP, "kv write launch failed: %s", hipGetErrorString(e));
+  return ok();
 }
 
 }  // extern "C"

@@ -89,6 +89,17 @@ __device__ __forceinline__ float rel_bias(int rel, const RelPos& r, const float*
   return head_row[bucket];
 }
 
+struct KvWriteArgs {
+  void* k_cache;
+  void* v_cache;
+  const void* k_new;            // [num_tokens, H, D]
+  const void* v_new;
+  const int64_t* slot_mapping;  // [num_tokens], block * 16 + offset, < 0 = skip
+  int64_t num_tokens;
+  int32_t num_heads, head_dim, dtype;
+};
+
+hipError_t launch_kv_write(const KvWriteArgs& a, hipStream_t stream);
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream);
 

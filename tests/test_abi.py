@@ -200,3 +200,38 @@ def test_prefill_relpos_rejects_on_host():
                                             4, 1, -1, 0, 0.125, 2, 4, 4, 64, 16, 8, 128, 64, 10,
                                             0, None)
     assert st == 2     # max_distance must exceed the exact range (8 for 16 buckets a side)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(k=None), 1), (dict(slots=None), 1), (dict(slots=FAKE + 4), 4), (dict(kn=FAKE + 8), 4),
+    (dict(D=96), 3), (dict(Hkv=1), 3), (dict(bs=8), 3), (dict(T=-1), 2), (dict(dtype=2), 3),
+])
+def test_kv_write_rejects_on_host(kw, status):
+    lib = pa.lib()
+    a = dict(k=FAKE, v=FAKE, kn=FAKE, vn=FAKE, slots=FAKE, T=4, H=2, Hkv=2, D=64, bs=16, nb=8,
+             dtype=1, stream=None)
+    a.update(kw)
+    st = lib._lib.paged_kv_write(a["k"], a["v"], a["kn"], a["vn"], a["slots"], a["T"], a["H"],
+                                 a["Hkv"], a["D"], a["bs"], a["nb"], a["dtype"], a["stream"])
+    assert st == status, (st, lib.pa_last_error())
+
+
+def test_kv_write_empty_is_ok():
+    lib = pa.lib()
+    assert lib._lib.paged_kv_write(None, None, None, None, None, 0, 2, 2, 64, 16, 8, 1,
+                                   None) == 0
+
+
+def test_window_first_live_block():
+    lib = pa.lib()
+    f = lib.pa_window_first_live_block
+    assert f(100, -1) == 0 and f(0, 24) == 0 and f(24, 24) == 0
+    assert f(25, 24) == 0                      # first visible token 1 -> block 0
+    assert f(40, 24) == 1                      # first visible token 16 -> block 1
+    assert f(1000, 64) == (1000 - 64) // 16
+    # monotone in the context length: once a block is dead it stays dead
+    prev = 0
+    for L in range(0, 500):
+        cur = f(L, 37)
+        assert cur >= prev
+        prev = cur
