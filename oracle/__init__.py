@@ -63,6 +63,12 @@ def _load():
         lib.oracle_prefill_relpos_f64.restype = ctypes.c_int
         lib.oracle_prefill_relpos_f64.argtypes = [P, P, P, P, P, P, P, P, I32, I32, I32, I32,
                                                   I32, F64, I32, I32, I32, I32, I32, I32, I32]
+        lib.oracle_decode_ragged_f64.restype = ctypes.c_int
+        lib.oracle_decode_ragged_f64.argtypes = [P, P, P, P, P, P, P, P, I32, F64, I32, I32,
+                                                 I32, I32, I32, I32, I32]
+        lib.oracle_prefill_ragged_f64.restype = ctypes.c_int
+        lib.oracle_prefill_ragged_f64.argtypes = [P, P, P, P, P, P, P, P, P, I32, I32, F64, I32,
+                                                  I32, I32, I32, I32, I32, I32]
         lib.oracle_kv_write.restype = ctypes.c_int
         lib.oracle_kv_write.argtypes = [P, P, P, P, P, ctypes.c_int64, I32, I32, I32,
                                         ctypes.c_int64, I32]
@@ -230,3 +236,44 @@ def kv_write(k_cache, v_cache, k_new, v_new, slot_mapping):
     if rc != 0:
         raise ValueError("oracle_kv_write rejected its arguments")
     return kc, vc
+
+
+def decode_ragged(q, k_cache, v_cache, block_tables, context_lens, bias, bias_start,
+                  sliding_window, scale, max_seq_len):
+    """Float64 decode with a ragged bias: sequence b's rows [H][L_b] start at
+    bias[bias_start[b]]."""
+    dt = _kv_dtype(q)
+    qh, kh, vh = _host(q), _host(k_cache), _host(v_cache)
+    bt = _host(block_tables, np.int32)
+    cl = _host(context_lens, np.int32)
+    bb, bs0 = _host(bias, np.float32), _host(bias_start, np.int64)
+    B, H, D = qh.shape
+    out = np.zeros((B, H, D), dtype=np.float64)
+    rc = _load().oracle_decode_ragged_f64(
+        _ptr(out), _ptr(qh), _ptr(kh), _ptr(vh), _ptr(bt), _ptr(cl), _ptr(bb), _ptr(bs0),
+        int(sliding_window), float(scale), B, H, D, kh.shape[2], bt.shape[1],
+        int(max_seq_len), dt)
+    if rc != 0:
+        raise ValueError("oracle_decode_ragged_f64 rejected its arguments")
+    return out
+
+
+def prefill_ragged(q, k_cache, v_cache, block_tables, context_lens, query_start_loc, bias,
+                   bias_start, sliding_window, causal, scale, max_seq_len):
+    """Float64 prefill with a ragged bias: sequence b's rows [H][n_q][L_b]
+    start at bias[bias_start[b]]."""
+    dt = _kv_dtype(q)
+    qh, kh, vh = _host(q), _host(k_cache), _host(v_cache)
+    bt = _host(block_tables, np.int32)
+    cl = _host(context_lens, np.int32)
+    qsl = _host(query_start_loc, np.int32)
+    bb, bs0 = _host(bias, np.float32), _host(bias_start, np.int64)
+    TQ, H, D = qh.shape
+    out = np.zeros((TQ, H, D), dtype=np.float64)
+    rc = _load().oracle_prefill_ragged_f64(
+        _ptr(out), _ptr(qh), _ptr(kh), _ptr(vh), _ptr(bt), _ptr(cl), _ptr(qsl), _ptr(bb),
+        _ptr(bs0), int(sliding_window), int(causal), float(scale), cl.shape[0], H, D,
+        kh.shape[2], bt.shape[1], int(max_seq_len), dt)
+    if rc != 0:
+        raise ValueError("oracle_prefill_ragged_f64 rejected its arguments")
+    return out

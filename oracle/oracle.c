@@ -310,6 +310,82 @@ int oracle_prefill_relpos_f64(double* out, const void* q, const void* k_cache,
 }
 
 /* ------------------------------------------------------------------------
+ * Ragged bias layout: the variable-length alternative to padding the bias
+ * to max_seq_len that the custom-bias PR description names as a later
+ * optimisation. Sequence b's bias starts at element bias_start[b] of one
+ * packed buffer: decode rows [H][L_b] (a = bias[start + h*L_b + j]), prefill
+ * rows [H][n_q][L_b] (a = bias[start + (h*n_q + t)*L_b + j]).
+ * ---------------------------------------------------------------------- */
+int oracle_decode_ragged_f64(double* out, const void* q, const void* k_cache, const void* v_cache,
+                             const int32_t* block_tables, const int32_t* context_lens,
+                             const float* bias, const int64_t* bias_start,
+                             int32_t sliding_window, double scale, int32_t num_seqs,
+                             int32_t num_heads, int32_t head_dim, int32_t block_size,
+                             int32_t max_blocks_per_seq, int32_t max_seq_len, int32_t dtype) {
+  if (bad_scalars(num_seqs, num_heads, head_dim, block_size, max_blocks_per_seq, max_seq_len,
+                  sliding_window, dtype) || !bias || !bias_start)
+    return -1;
+  for (int32_t b = 0; b < num_seqs; ++b)
+    if (context_lens[b] < 0 || context_lens[b] > max_seq_len) return -1;
+  int64_t pairs = (int64_t)num_seqs * num_heads;
+#pragma omp parallel
+  {
+    double* s = (double*)malloc(sizeof(double) * (size_t)(max_seq_len > 0 ? max_seq_len : 1));
+#pragma omp for schedule(dynamic, 1)
+    for (int64_t bh = 0; bh < pairs; ++bh) {
+      int32_t b = (int32_t)(bh / num_heads), h = (int32_t)(bh % num_heads);
+      int32_t L = context_lens[b];
+      const float* bias_row = bias + bias_start[b] + (int64_t)h * L;
+      attend_row(out + bh * head_dim, q, bh * head_dim, k_cache, v_cache,
+                 block_tables + (int64_t)b * max_blocks_per_seq, bias_row, L - 1, L,
+                 sliding_window, 0, scale, h, num_heads, head_dim, block_size, dtype, s);
+    }
+    free(s);
+  }
+  return 0;
+}
+
+int oracle_prefill_ragged_f64(double* out, const void* q, const void* k_cache, const void* v_cache,
+                              const int32_t* block_tables, const int32_t* context_lens,
+                              const int32_t* query_start_loc, const float* bias,
+                              const int64_t* bias_start, int32_t sliding_window, int32_t causal,
+                              double scale, int32_t num_seqs, int32_t num_heads, int32_t head_dim,
+                              int32_t block_size, int32_t max_blocks_per_seq, int32_t max_seq_len,
+                              int32_t dtype) {
+  if (bad_scalars(num_seqs, num_heads, head_dim, block_size, max_blocks_per_seq, max_seq_len,
+                  sliding_window, dtype) || !bias || !bias_start)
+    return -1;
+  if (causal != 0 && causal != 1) return -1;
+  for (int32_t b = 0; b < num_seqs; ++b) {
+    int32_t nq = query_start_loc[b + 1] - query_start_loc[b];
+    if (context_lens[b] < 0 || context_lens[b] > max_seq_len || nq < 0 || nq > context_lens[b])
+      return -1;
+  }
+  int64_t pairs = (int64_t)num_seqs * num_heads;
+#pragma omp parallel
+  {
+    double* s = (double*)malloc(sizeof(double) * (size_t)(max_seq_len > 0 ? max_seq_len : 1));
+#pragma omp for schedule(dynamic, 1)
+    for (int64_t bh = 0; bh < pairs; ++bh) {
+      int32_t b = (int32_t)(bh / num_heads), h = (int32_t)(bh % num_heads);
+      int32_t L = context_lens[b];
+      int32_t q0 = query_start_loc[b];
+      int32_t nq = query_start_loc[b + 1] - q0;
+      for (int32_t t = 0; t < nq; ++t) {
+        int32_t p = L - nq + t;
+        int64_t row = ((int64_t)(q0 + t) * num_heads + h) * head_dim;
+        const float* bias_row = bias + bias_start[b] + ((int64_t)h * nq + t) * L;
+        attend_row(out + row, q, row, k_cache, v_cache,
+                   block_tables + (int64_t)b * max_blocks_per_seq, bias_row, p, L,
+                   sliding_window, causal, scale, h, num_heads, head_dim, block_size, dtype, s);
+      }
+    }
+    free(s);
+  }
+  return 0;
+}
+
+/* ------------------------------------------------------------------------
  * KV-cache write: the step before decode. Token t's keys and values (all
  * heads) go to physical slot slot_mapping[t] = block * block_size + offset
  * of the paged caches (the block-table layout of "Add Encoder-decoder model

@@ -92,6 +92,22 @@ int oracle_prefill_relpos_f64(double* out, const void* q, const void* k_cache,
                               int32_t head_dim, int32_t block_size, int32_t max_blocks_per_seq,
                               int32_t max_seq_len, int32_t dtype);
 
+/* Ragged bias layout: sequence b's bias starts at bias[bias_start[b]];
+ * decode rows [H][L_b], prefill rows [H][n_q][L_b]. Otherwise as above. */
+int oracle_decode_ragged_f64(double* out, const void* q, const void* k_cache, const void* v_cache,
+                             const int32_t* block_tables, const int32_t* context_lens,
+                             const float* bias, const int64_t* bias_start,
+                             int32_t sliding_window, double scale, int32_t num_seqs,
+                             int32_t num_heads, int32_t head_dim, int32_t block_size,
+                             int32_t max_blocks_per_seq, int32_t max_seq_len, int32_t dtype);
+int oracle_prefill_ragged_f64(double* out, const void* q, const void* k_cache, const void* v_cache,
+                              const int32_t* block_tables, const int32_t* context_lens,
+                              const int32_t* query_start_loc, const float* bias,
+                              const int64_t* bias_start, int32_t sliding_window, int32_t causal,
+                              double scale, int32_t num_seqs, int32_t num_heads, int32_t head_dim,
+                              int32_t block_size, int32_t max_blocks_per_seq, int32_t max_seq_len,
+                              int32_t dtype);
+
 /* Scatter num_tokens new key/value rows [num_tokens, num_heads, head_dim]
  * into the paged caches at physical slots slot_mapping[t] (block * block_size
  * + offset; negative = skip). Returns -1 on a slot outside the pool. */

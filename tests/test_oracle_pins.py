@@ -451,3 +451,48 @@ def test_kv_write_rejects_slots_outside_the_pool():
     with pytest.raises(ValueError):
         oracle.kv_write(k, k, torch.zeros(1, 1, 4), torch.zeros(1, 1, 4),
                         torch.tensor([2 * BS], dtype=torch.int64))
+
+
+# ----------------------------------------------------------------------------
+# ragged bias layout
+# ----------------------------------------------------------------------------
+def pack_decode_bias(dense, lens):
+    """[B,H,MS] padded -> packed [H][L_b] rows per sequence + start offsets."""
+    parts, starts, off = [], [], 0
+    for b, L in enumerate(lens):
+        parts.append(dense[b, :, :int(L)].reshape(-1))
+        starts.append(off)
+        off += dense.shape[1] * int(L)
+    return torch.cat(parts).contiguous(), torch.tensor(starts, dtype=torch.int64)
+
+
+def pack_prefill_bias(dense, lens, q_lens):
+    parts, starts, off = [], [], 0
+    for b, (L, nq) in enumerate(zip(lens, q_lens)):
+        L, nq = int(L), int(nq)
+        parts.append(dense[b, :, L - nq:L, :L].reshape(-1))
+        starts.append(off)
+        off += dense.shape[1] * nq * L
+    return torch.cat(parts).contiguous(), torch.tensor(starts, dtype=torch.int64)
+
+
+@pytest.mark.parametrize("window", [-1, 7])
+def test_decode_ragged_equals_padded_bit_exact(window):
+    case = small_decode(95, bias="normal", window=window, lens=[0, 1, 30, 45], max_seq_len=48)
+    packed, starts = pack_decode_bias(case.attn_bias, case.lens)
+    assert packed.numel() == case.num_heads * int(case.lens.sum())
+    got = oracle.decode_ragged(case.q, case.k_cache, case.v_cache, case.block_tables,
+                               case.context_lens, packed, starts, window, case.scale,
+                               case.max_seq_len)
+    np.testing.assert_array_equal(got, run_decode(case))
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_prefill_ragged_equals_padded_bit_exact(causal):
+    case = small_prefill(96, bias="normal", window=9, causal=causal, lens=[40, 17, 5],
+                         q_lens=[40, 3, 5])
+    packed, starts = pack_prefill_bias(case.attn_bias, case.lens, case.q_lens)
+    got = oracle.prefill_ragged(case.q, case.k_cache, case.v_cache, case.block_tables,
+                                case.context_lens, case.query_start_loc, packed, starts, 9,
+                                int(causal), case.scale, case.max_seq_len)
+    np.testing.assert_array_equal(got, run_prefill(case))
