@@ -201,6 +201,22 @@ def bench_decode(args):
             args.steps, args.warmup)
         var["t5_bias_in_kernel"] = {"ms_per_step": msr, "tokens_per_s": B / (msr * 1e-3),
                                     "GBps": bn / (msr * 1e-3) / 1e9}
+        # the same bias values in the packed (unpadded) layout
+        Lt = torch.from_numpy(case.lens.astype(np.int64))
+        starts = torch.zeros(B, dtype=torch.int64)
+        starts[1:] = torch.cumsum(Lt * H, 0)[:-1]
+        packed = torch.cat([case.attn_bias[b, :, :int(case.lens[b])].reshape(-1)
+                            for b in range(B)]).contiguous()
+        starts = starts.to("cuda")
+        msg = time_steps(lambda: lib.paged_attn_decode_ragged_bias(
+            case.q, case.k_cache, case.v_cache, case.block_tables, case.context_lens, packed,
+            starts, -1, case.scale, max_seq_len=case.max_seq_len, out=out, workspace=ws),
+            args.steps, args.warmup)
+        var["ragged_bias"] = {"ms_per_step": msg, "tokens_per_s": B / (msg * 1e-3),
+                              "GBps": nbytes / (msg * 1e-3) / 1e9,
+                              "bias_MiB_packed": packed.numel() * 4 / 2**20,
+                              "bias_MiB_padded": case.attn_bias.numel() * 4 / 2**20}
+        del packed
         if os.path.exists(pa.LIB_NOBIAS_PATH):
             nob = pa.PagedAttnLib(pa.LIB_NOBIAS_PATH)
             msb = time_steps(lambda: step(bias=None, which=nob), args.steps, args.warmup)

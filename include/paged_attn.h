@@ -211,6 +211,41 @@ pa_status_t paged_attn_prefill_relpos(void* out, const void* q, const void* k_ca
                                       pa_dtype_t dtype, void* stream);
 
 /*
+ * Ragged (unpadded) bias layout — the "variable len bias matrix" the custom
+ * bias PR description lists as a later optimisation of the padded layout.
+ * One packed fp32 buffer holds every sequence's bias back to back; sequence
+ * b's part starts at element bias_start[b]:
+ *   decode   rows [num_heads][L_b]:       a(b,h,j)   = attn_bias[bias_start[b] + h*L_b + j]
+ *   prefill  rows [num_heads][n_q][L_b]:  a(b,h,t,j) = attn_bias[bias_start[b] + (h*n_q + t)*L_b + j]
+ * (t = query index within the sequence, j = key position). attn_bias and
+ * bias_start (int64 [num_seqs], 8-byte aligned) are device memory and must
+ * not be NULL. Everything else as for paged_attn_decode / paged_attn_prefill.
+ */
+pa_status_t paged_attn_decode_ragged_bias(void* out, const void* q, const void* k_cache,
+                                          const void* v_cache, const int32_t* block_tables,
+                                          const int32_t* context_lens, const float* attn_bias,
+                                          const int64_t* bias_start, int32_t sliding_window,
+                                          float scale, int32_t num_seqs, int32_t num_heads,
+                                          int32_t num_kv_heads, int32_t head_dim,
+                                          int32_t block_size, int32_t max_blocks_per_seq,
+                                          int32_t max_seq_len, int64_t num_blocks,
+                                          pa_dtype_t dtype, int32_t partition_tokens,
+                                          void* workspace, size_t workspace_bytes,
+                                          void* stream);
+
+pa_status_t paged_attn_prefill_ragged_bias(void* out, const void* q, const void* k_cache,
+                                           const void* v_cache, const int32_t* block_tables,
+                                           const int32_t* context_lens,
+                                           const int32_t* query_start_loc,
+                                           const float* attn_bias, const int64_t* bias_start,
+                                           int32_t sliding_window, int32_t causal, float scale,
+                                           int32_t num_seqs, int32_t num_heads,
+                                           int32_t num_kv_heads, int32_t head_dim,
+                                           int32_t block_size, int32_t max_blocks_per_seq,
+                                           int32_t max_seq_len, int64_t num_blocks,
+                                           int64_t total_q, pa_dtype_t dtype, void* stream);
+
+/*
  * KV-cache write, the step that precedes decode: token t's keys and values
  * (all heads) are stored at physical slot slot_mapping[t] = block * 16 +
  * offset of the paged caches (layout above; the block tables themselves are

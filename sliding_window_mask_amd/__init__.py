@@ -11,6 +11,8 @@ Functions mirror the C entry points:
   paged_attn_prefill(...)        encoder-only (bidirectional) or causal prefill
   paged_attn_decode_relpos(...)  decode with the T5 relative-position bias in-kernel
   paged_attn_prefill_relpos(...) prefill with the T5 relative-position bias in-kernel
+  paged_attn_decode_ragged_bias(...), paged_attn_prefill_ragged_bias(...)
+                                 the same with an unpadded (packed) bias
   paged_kv_write(...)            scatter new tokens' K/V into the paged caches
   pa_window_first_live_block(...) first block a windowed decode still reads
   pa_decode_workspace_bytes(...)
@@ -96,6 +98,14 @@ class PagedAttnLib:
         lib.paged_attn_prefill_relpos.argtypes = [P, P, P, P, P, P, P, P, I32, I32, I32, I32,
                                                   I32, F32, I32, I32, I32, I32, I32, I32, I32,
                                                   I64, I64, ctypes.c_int, P]
+        lib.paged_attn_decode_ragged_bias.restype = ctypes.c_int
+        lib.paged_attn_decode_ragged_bias.argtypes = [P, P, P, P, P, P, P, P, I32, F32, I32,
+                                                      I32, I32, I32, I32, I32, I32, I64,
+                                                      ctypes.c_int, I32, P, SZ, P]
+        lib.paged_attn_prefill_ragged_bias.restype = ctypes.c_int
+        lib.paged_attn_prefill_ragged_bias.argtypes = [P, P, P, P, P, P, P, P, P, I32, I32, F32,
+                                                       I32, I32, I32, I32, I32, I32, I32, I64,
+                                                       I64, ctypes.c_int, P]
         lib.paged_kv_write.restype = ctypes.c_int
         lib.paged_kv_write.argtypes = [P, P, P, P, P, I64, I32, I32, I32, I32, I64,
                                        ctypes.c_int, P]
@@ -227,6 +237,42 @@ class PagedAttnLib:
             _stream(stream)))
         return out
 
+    def paged_attn_decode_ragged_bias(self, q, k_cache, v_cache, block_tables, context_lens,
+                                      attn_bias, bias_start, sliding_window, scale, *,
+                                      max_seq_len, out=None, workspace=None,
+                                      partition_tokens=0, stream=None):
+        """Decode with a packed bias: sequence b's rows [H][L_b] start at
+        attn_bias[bias_start[b]] (bias_start int64 [B])."""
+        B, H, D = q.shape
+        if out is None:
+            out = torch.empty_like(q)
+        if workspace is None:
+            workspace = self.workspace_for(q, max_seq_len, sliding_window, partition_tokens)
+        ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+        self._check(self._lib.paged_attn_decode_ragged_bias(
+            _ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables),
+            _ptr(context_lens), _ptr(attn_bias), _ptr(bias_start), int(sliding_window),
+            float(scale), B, H, k_cache.shape[1], D, k_cache.shape[2], block_tables.shape[1],
+            int(max_seq_len), k_cache.shape[0], _dtype_code(q), int(partition_tokens),
+            _ptr(workspace), ws_bytes, _stream(stream)))
+        return out
+
+    def paged_attn_prefill_ragged_bias(self, q, k_cache, v_cache, block_tables, context_lens,
+                                       query_start_loc, attn_bias, bias_start, sliding_window,
+                                       causal, scale, *, max_seq_len, out=None, stream=None):
+        """Prefill with a packed bias: sequence b's rows [H][n_q][L_b] start at
+        attn_bias[bias_start[b]]."""
+        TQ, H, D = q.shape
+        if out is None:
+            out = torch.empty_like(q)
+        self._check(self._lib.paged_attn_prefill_ragged_bias(
+            _ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables),
+            _ptr(context_lens), _ptr(query_start_loc), _ptr(attn_bias), _ptr(bias_start),
+            int(sliding_window), int(bool(causal)), float(scale), context_lens.shape[0], H,
+            k_cache.shape[1], D, k_cache.shape[2], block_tables.shape[1], int(max_seq_len),
+            k_cache.shape[0], TQ, _dtype_code(q), _stream(stream)))
+        return out
+
     def paged_kv_write(self, k_cache, v_cache, k_new, v_new, slot_mapping, *, stream=None):
         """Scatter k_new, v_new [T,H,D] into the paged caches at slot_mapping
         (int64 [T], block * 16 + offset; negative = skip)."""
@@ -265,6 +311,14 @@ def paged_attn_decode_relpos(*args, **kwargs):
 
 def paged_attn_prefill_relpos(*args, **kwargs):
     return lib().paged_attn_prefill_relpos(*args, **kwargs)
+
+
+def paged_attn_decode_ragged_bias(*args, **kwargs):
+    return lib().paged_attn_decode_ragged_bias(*args, **kwargs)
+
+
+def paged_attn_prefill_ragged_bias(*args, **kwargs):
+    return lib().paged_attn_prefill_ragged_bias(*args, **kwargs)
 
 
 def paged_kv_write(*args, **kwargs):

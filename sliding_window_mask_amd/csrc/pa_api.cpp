@@ -288,8 +288,9 @@ namespace {
 
 pa_status_t decode_impl(void* out, const void* q, const void* k_cache, const void* v_cache,
                         const int32_t* block_tables, const int32_t* context_lens,
-                        const float* attn_bias, const pa::RelPos* rel, int32_t sliding_window,
-                        float scale, int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
+                        const float* attn_bias, const int64_t* bias_start,
+                        const pa::RelPos* rel, int32_t sliding_window, float scale,
+                        int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
                         int32_t head_dim, int32_t block_size, int32_t max_blocks_per_seq,
                         int32_t max_seq_len, int64_t num_blocks, pa_dtype_t dtype,
                         int32_t partition_tokens, void* workspace, size_t workspace_bytes,
@@ -299,6 +300,10 @@ pa_status_t decode_impl(void* out, const void* q, const void* k_cache, const voi
                                 head_dim, block_size, max_blocks_per_seq, max_seq_len,
                                 num_blocks, dtype);
   if (st != PA_OK) return st;
+#ifdef PA_NO_BIAS
+  if (attn_bias)
+    return fail(PA_ERR_UNSUPPORTED, "this comparison build has no materialised-bias decode");
+#endif
   if (partition_tokens < 0 || partition_tokens % pa::kBlockSize != 0 ||
       partition_tokens > pa::kMaxPartition)
     return fail(PA_ERR_INVALID_ARG, "partition_tokens %d: use 0 or a multiple of 16 in "
@@ -329,6 +334,7 @@ pa_status_t decode_impl(void* out, const void* q, const void* k_cache, const voi
   a.block_tables = block_tables;
   a.context_lens = context_lens;
   a.attn_bias = attn_bias;
+  a.bias_start = bias_start;
   a.window = sliding_window;
   a.scale_log2 = (float)((double)scale * 1.4426950408889634074);
   a.num_seqs = num_seqs;
@@ -354,7 +360,8 @@ pa_status_t decode_impl(void* out, const void* q, const void* k_cache, const voi
 pa_status_t prefill_impl(void* out, const void* q, const void* k_cache, const void* v_cache,
                          const int32_t* block_tables, const int32_t* context_lens,
                          const int32_t* query_start_loc, const float* attn_bias,
-                         const pa::RelPos* rel, int32_t sliding_window, int32_t causal,
+                         const int64_t* bias_start, const pa::RelPos* rel,
+                         int32_t sliding_window, int32_t causal,
                          float scale, int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
                          int32_t head_dim, int32_t block_size, int32_t max_blocks_per_seq,
                          int32_t max_seq_len, int64_t num_blocks, int64_t total_q,
@@ -389,6 +396,7 @@ pa_status_t prefill_impl(void* out, const void* q, const void* k_cache, const vo
   a.context_lens = context_lens;
   a.query_start_loc = query_start_loc;
   a.attn_bias = attn_bias;
+  a.bias_start = bias_start;
   a.window = sliding_window;
   a.causal = causal;
   a.scale_log2 = (float)((double)scale * 1.4426950408889634074);
@@ -418,7 +426,7 @@ pa_status_t paged_attn_decode(void* out, const void* q, const void* k_cache,
                               int32_t partition_tokens, void* workspace,
                               size_t workspace_bytes, void* stream) {
   return decode_impl(out, q, k_cache, v_cache, block_tables, context_lens, attn_bias, nullptr,
-                     sliding_window, scale, num_seqs, num_heads, num_kv_heads, head_dim,
+                     nullptr, sliding_window, scale, num_seqs, num_heads, num_kv_heads, head_dim,
                      block_size, max_blocks_per_seq, max_seq_len, num_blocks, dtype,
                      partition_tokens, workspace, workspace_bytes, stream);
 }
@@ -437,8 +445,8 @@ pa_status_t paged_attn_decode_relpos(void* out, const void* q, const void* k_cac
   pa::RelPos rel{};
   pa_status_t st = make_relpos(rel_table, num_buckets, max_distance, bidirectional, &rel);
   if (st != PA_OK) return st;
-  return decode_impl(out, q, k_cache, v_cache, block_tables, context_lens, nullptr, &rel,
-                     sliding_window, scale, num_seqs, num_heads, num_kv_heads, head_dim,
+  return decode_impl(out, q, k_cache, v_cache, block_tables, context_lens, nullptr, nullptr,
+                     &rel, sliding_window, scale, num_seqs, num_heads, num_kv_heads, head_dim,
                      block_size, max_blocks_per_seq, max_seq_len, num_blocks, dtype,
                      partition_tokens, workspace, workspace_bytes, stream);
 }
@@ -453,7 +461,8 @@ pa_status_t paged_attn_prefill(void* out, const void* q, const void* k_cache,
                                int64_t num_blocks, int64_t total_q, pa_dtype_t dtype,
                                void* stream) {
   return prefill_impl(out, q, k_cache, v_cache, block_tables, context_lens, query_start_loc,
-                      attn_bias, nullptr, sliding_window, causal, scale, num_seqs, num_heads,
+                      attn_bias, nullptr, nullptr, sliding_window, causal, scale, num_seqs,
+                      num_heads,
                       num_kv_heads, head_dim, block_size, max_blocks_per_seq, max_seq_len,
                       num_blocks, total_q, dtype, stream);
 }
@@ -473,9 +482,52 @@ pa_status_t paged_attn_prefill_relpos(void* out, const void* q, const void* k_ca
   pa_status_t st = make_relpos(rel_table, num_buckets, max_distance, bidirectional, &rel);
   if (st != PA_OK) return st;
   return prefill_impl(out, q, k_cache, v_cache, block_tables, context_lens, query_start_loc,
-                      nullptr, &rel, sliding_window, causal, scale, num_seqs, num_heads,
+                      nullptr, nullptr, &rel, sliding_window, causal, scale, num_seqs,
+                      num_heads,
                       num_kv_heads, head_dim, block_size, max_blocks_per_seq, max_seq_len,
                       num_blocks, total_q, dtype, stream);
+}
+
+pa_status_t paged_attn_decode_ragged_bias(void* out, const void* q, const void* k_cache,
+                                          const void* v_cache, const int32_t* block_tables,
+                                          const int32_t* context_lens, const float* attn_bias,
+                                          const int64_t* bias_start, int32_t sliding_window,
+                                          float scale, int32_t num_seqs, int32_t num_heads,
+                                          int32_t num_kv_heads, int32_t head_dim,
+                                          int32_t block_size, int32_t max_blocks_per_seq,
+                                          int32_t max_seq_len, int64_t num_blocks,
+                                          pa_dtype_t dtype, int32_t partition_tokens,
+                                          void* workspace, size_t workspace_bytes,
+                                          void* stream) {
+  if (num_seqs > 0 && (!attn_bias || !bias_start))
+    return fail(PA_ERR_NULL_POINTER, "attn_bias and bias_start are required");
+  if (bias_start && !aligned(bias_start, 8))
+    return fail(PA_ERR_MISALIGNED, "bias_start must be 8-byte aligned");
+  return decode_impl(out, q, k_cache, v_cache, block_tables, context_lens, attn_bias, bias_start,
+                     nullptr, sliding_window, scale, num_seqs, num_heads, num_kv_heads, head_dim,
+                     block_size, max_blocks_per_seq, max_seq_len, num_blocks, dtype,
+                     partition_tokens, workspace, workspace_bytes, stream);
+}
+
+pa_status_t paged_attn_prefill_ragged_bias(void* out, const void* q, const void* k_cache,
+                                           const void* v_cache, const int32_t* block_tables,
+                                           const int32_t* context_lens,
+                                           const int32_t* query_start_loc,
+                                           const float* attn_bias, const int64_t* bias_start,
+                                           int32_t sliding_window, int32_t causal, float scale,
+                                           int32_t num_seqs, int32_t num_heads,
+                                           int32_t num_kv_heads, int32_t head_dim,
+                                           int32_t block_size, int32_t max_blocks_per_seq,
+                                           int32_t max_seq_len, int64_t num_blocks,
+                                           int64_t total_q, pa_dtype_t dtype, void* stream) {
+  if (num_seqs > 0 && (!attn_bias || !bias_start))
+    return fail(PA_ERR_NULL_POINTER, "attn_bias and bias_start are required");
+  if (bias_start && !aligned(bias_start, 8))
+    return fail(PA_ERR_MISALIGNED, "bias_start must be 8-byte aligned");
+  return prefill_impl(out, q, k_cache, v_cache, block_tables, context_lens, query_start_loc,
+                      attn_bias, bias_start, nullptr, sliding_window, causal, scale, num_seqs,
+                      num_heads, num_kv_heads, head_dim, block_size, max_blocks_per_seq,
+                      max_seq_len, num_blocks, total_q, dtype, stream);
 }
 
 int32_t pa_window_first_live_block(int32_t context_len, int32_t sliding_window) {

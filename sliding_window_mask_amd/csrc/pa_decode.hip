@@ -240,7 +240,10 @@ pa_decode_partition(DecodeArgs a) {
   // ---- K pass: raw dot products into s_lds ----
   // (bias entries of this thread's first tokens are requested first, so they
   // arrive while the keys stream in)
-  const float* bias_row = BIAS == 1 ? a.attn_bias + row * a.max_seq_len : nullptr;
+  const float* bias_row =
+      BIAS != 1 ? nullptr
+                : (a.bias_start ? a.attn_bias + a.bias_start[b] + (int64_t)h * L   // ragged
+                                : a.attn_bias + row * a.max_seq_len);               // padded
   const int ntok = nblk * kBlockSize;
   float bpre[kBiasPre];
 #pragma unroll

@@ -41,6 +41,8 @@ struct DecodeArgs {
   const int32_t* block_tables;
   const int32_t* context_lens;
   const float* attn_bias;     // may be null
+  const int64_t* bias_start;  // null: bias padded [B,H,max_seq_len]; else sequence b's
+                              // rows [H][L_b] start at attn_bias + bias_start[b]
   int32_t window;             // -1 or >= 1
   float scale_log2;           // scale * log2(e): scores are kept in base 2
   int32_t num_seqs, num_heads, head_dim, max_blocks, max_seq_len;
@@ -62,6 +64,8 @@ struct PrefillArgs {
   const int32_t* context_lens;
   const int32_t* query_start_loc;
   const float* attn_bias;     // may be null
+  const int64_t* bias_start;  // null: bias padded [B,H,MS,MS]; else sequence b's rows
+                              // [H][n_q][L_b] start at attn_bias + bias_start[b]
   int32_t window;             // -1 or >= 1
   int32_t causal;             // 0 or 1
   float scale_log2;

@@ -245,10 +245,14 @@ pa_prefill_f32(PrefillArgs a) {
     l_run[q] = 0.0f;
     // rows past n_q point at the tile's first row and are masked, so every
     // bias read is in bounds
-    bias_row[q] = BIAS == 1 ? a.attn_bias + (((int64_t)b * H + h) * a.max_seq_len +
-                                            (row_ok[q] ? p[q] : pos0 + t_first)) *
-                                               a.max_seq_len
-                           : nullptr;
+    const int tb_row = row_ok[q] ? t[q] : t_first;   // query index within the sequence
+    if (BIAS != 1)
+      bias_row[q] = nullptr;
+    else if (a.bias_start)                           // ragged rows [H][n_q][L]
+      bias_row[q] = a.attn_bias + a.bias_start[b] + ((int64_t)h * nq + tb_row) * L;
+    else                                             // padded [B, H, MS, MS]
+      bias_row[q] = a.attn_bias +
+                    (((int64_t)b * H + h) * a.max_seq_len + pos0 + tb_row) * a.max_seq_len;
   }
 
   // ---- prologue: tile 0 into LDS buffer 0, tile 1 in flight, table of tile 2 ----

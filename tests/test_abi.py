@@ -235,3 +235,25 @@ def test_window_first_live_block():
         cur = f(L, 37)
         assert cur >= prev
         prev = cur
+
+
+def test_ragged_bias_requires_pointers():
+    lib = pa.lib()
+    st = lib._lib.paged_attn_decode_ragged_bias(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None,
+                                                -1, 0.125, 4, 4, 4, 64, 16, 8, 128, 64, 0, 0,
+                                                None, 0, None)
+    assert st == 1
+    st = lib._lib.paged_attn_decode_ragged_bias(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                                                FAKE + 4, -1, 0.125, 4, 4, 4, 64, 16, 8, 128,
+                                                64, 0, 0, None, 0, None)
+    assert st == 4
+    st = lib._lib.paged_attn_prefill_ragged_bias(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None,
+                                                 FAKE, -1, 0, 0.125, 2, 4, 4, 64, 16, 8, 128,
+                                                 64, 10, 0, None)
+    assert st == 1
+
+
+def test_no_bias_build_rejects_a_bias():
+    nob = pa.PagedAttnLib(pa.LIB_NOBIAS_PATH)
+    st = call_decode(nob, decode_args(bias=FAKE))
+    assert st == 3, nob.pa_last_error()
