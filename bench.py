@@ -11,6 +11,7 @@ Prints ONE JSON line. Options:
   --steps K       timed steps (default 20)
   --warmup W      untimed warm-up steps (default 5)
   --workload X    large_biased_decode_bf16 (default) | modernbert_prefill_f32 |
+                  modernbert_prefill_bf16 |
                   t5_small_self_decode_bf16 | t5_large_cross_decode_bf16 (cold-cache
                   median of single calls) | kv_write_modernbert_f32 | copy_probe (a plain device copy of
                   known size, for calibrating the rocprofv3 byte counters)
@@ -246,9 +247,19 @@ def prefill_flops(lens, H, D, window):
     return int(4 * D * H * np.sum(pairs))
 
 
-def bench_prefill(args):
-    layers = [workloads.modernbert_prefill_f32(l, device="cuda")
-              for l in range(workloads.MODERNBERT_LAYERS)]
+BF16_MFMA_PEAK_TFLOPS = 2500.0
+
+
+def bench_prefill(args, dtype=torch.float32):
+    if dtype == torch.float32:
+        layers = [workloads.modernbert_prefill_f32(l, device="cuda")
+                  for l in range(workloads.MODERNBERT_LAYERS)]
+    else:
+        layers = [workloads.prefill_case(4, num_seqs=32, num_heads=12, head_dim=64,
+                                         lens=(64, 1024), max_seq_len=1024, dtype=dtype,
+                                         sliding_window=workloads.modernbert_window(l),
+                                         device="cuda", layer_seed=[4, l])
+                  for l in range(workloads.MODERNBERT_LAYERS)]
     torch.cuda.synchronize()
     outs = [torch.empty_like(c.q) for c in layers]
     lib = pa.lib()
@@ -264,17 +275,19 @@ def bench_prefill(args):
     flops = sum(prefill_flops(c.lens, 12, 64, c.sliding_window) for c in layers)
     tflops = flops / (ms * 1e-3) / 1e12
     tokens = int(c0.lens.sum())
+    peak = FP32_MFMA_PEAK_TFLOPS if dtype == torch.float32 else BF16_MFMA_PEAK_TFLOPS
+    tag = "f32" if dtype == torch.float32 else "bf16"
     line = {
         "metric": "encoder prefill tokens/s (12 layers) and MFMA TFLOP/s", "value":
         tokens / (ms * 1e-3), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak",
-        "vs_baseline": None, "dtype": "f32", "data": "synthetic",
-        "config": {"workload": "modernbert_prefill_f32", "layers": 12, "num_seqs": 32,
+        "vs_baseline": None, "dtype": tag, "data": "synthetic",
+        "config": {"workload": "modernbert_prefill_" + tag, "layers": 12, "num_seqs": 32,
                    "num_heads": 12, "head_dim": 64, "context_lens": "uniform [64, 1024]",
                    "windows": [workloads.modernbert_window(l) for l in range(12)]},
-        "roofline": {"bound": "mfma", "achieved": tflops, "peak": FP32_MFMA_PEAK_TFLOPS,
-                     "unit": "TFLOP/s", "frac": tflops / FP32_MFMA_PEAK_TFLOPS,
-                     "traffic": None, "kernel": "pa_prefill_f32 (12 launches per step)"},
+        "roofline": {"bound": "mfma", "achieved": tflops, "peak": peak,
+                     "unit": "TFLOP/s", "frac": tflops / peak,
+                     "traffic": None, "kernel": "pa_prefill_%s (12 launches per step)" % tag},
         "algorithmic_flops_per_step": flops,
     }
     return line
@@ -407,6 +420,8 @@ def main():
         line = bench_decode(args)
     elif args.workload == "modernbert_prefill_f32":
         line = bench_prefill(args)
+    elif args.workload == "modernbert_prefill_bf16":
+        line = bench_prefill(args, torch.bfloat16)
     elif args.workload in ("t5_small_self_decode_bf16", "t5_large_cross_decode_bf16"):
         line = bench_small_decode(args, args.workload)
     elif args.workload == "kv_write_modernbert_f32":

@@ -145,7 +145,8 @@ pa_status_t paged_attn_decode(void* out, const void* q, const void* k_cache,
  *                   0 <= n_q <= L must hold
  *   attn_bias       [num_seqs, num_heads, max_seq_len, max_seq_len] fp32, or NULL
  *   causal          0 or 1
- *   dtype           PA_DTYPE_F32 or PA_DTYPE_BF16
+ *   dtype           PA_DTYPE_F32 or PA_DTYPE_BF16 (bf16: bf16 MFMA with fp32
+ *                   accumulation; the softmax weights enter P.V as bf16)
  *   Other arguments as for paged_attn_decode. No workspace is needed.
  * Errors: NULL_POINTER, INVALID_ARG, UNSUPPORTED, MISALIGNED, HIP.
  */

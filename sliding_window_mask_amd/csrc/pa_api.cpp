@@ -378,8 +378,6 @@ pa_status_t prefill_impl(void* out, const void* q, const void* k_cache, const vo
   if (!query_start_loc) return fail(PA_ERR_NULL_POINTER, "query_start_loc is NULL");
   if (!aligned(query_start_loc, 4))
     return fail(PA_ERR_MISALIGNED, "query_start_loc must be 4-byte aligned");
-  if (dtype != PA_DTYPE_F32)
-    return fail(PA_ERR_UNSUPPORTED, "prefill supports fp32 only in this version");
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (validate_env()) {
     st = validate_device(block_tables, context_lens, query_start_loc, sliding_window, causal,
@@ -407,7 +405,7 @@ pa_status_t prefill_impl(void* out, const void* q, const void* k_cache, const vo
   a.max_seq_len = max_seq_len;
   a.dtype = (int32_t)dtype;
   if (rel) a.rel = *rel;
-  hipError_t e = pa::launch_prefill(a, s);
+  hipError_t e = dtype == PA_DTYPE_F32 ? pa::launch_prefill_f32(a, s) : pa::launch_prefill_bf16(a, s);
   if (e != hipSuccess) return fail(PA_ERR_HIP, "prefill launch failed: %s", hipGetErrorString(e));
   return ok();
 }

@@ -75,6 +75,32 @@ struct PrefillArgs {
   RelPos rel;                 // used when rel.table is set (attn_bias is then null)
 };
 
+// Visible key interval [lo, hi) for query positions [p0, p1] of a sequence
+// of length L (caller guarantees p0 <= p1 < L): all keys, keys up to the
+// last query for a causal prompt, and with a window W only |p - j| < W.
+__device__ __forceinline__ void prefill_key_range(int p0, int p1, int L, int window, int causal,
+                                                  int& lo, int& hi) {
+  lo = 0;
+  hi = causal ? p1 + 1 : L;
+  if (window > 0) {
+    lo = max(0, p0 - window + 1);
+    if (!causal) hi = min(L, p1 + window);
+  }
+}
+
+constexpr int kXcds = 8;   // XCDs of an MI355X
+
+// Workgroup id -> (query tile, sequence * heads + head) such that every query
+// tile of one (sequence, head) runs on the same XCD: the dispatcher deals
+// consecutive workgroup ids round-robin over the XCDs, so ids n with the same
+// n % 8 share an XCD and its L2. The grid has ceil(pairs / 8) * 8 * num_qtiles
+// workgroups; ids whose pair is past the end return.
+__device__ __forceinline__ void prefill_tile_of(int n, int num_qtiles, int& pair, int& tile) {
+  const int slot = n / kXcds;
+  pair = (slot / num_qtiles) * kXcds + n % kXcds;
+  tile = slot % num_qtiles;
+}
+
 // Bucket of a non-negative distance within one direction (see RelPos).
 __device__ __forceinline__ int rel_half_bucket(int n, const RelPos& r) {
   if (n < r.max_exact) return n;
@@ -105,6 +131,7 @@ struct KvWriteArgs {
 
 hipError_t launch_kv_write(const KvWriteArgs& a, hipStream_t stream);
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
-hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream);
+hipError_t launch_prefill_f32(const PrefillArgs& a, hipStream_t stream);
+hipError_t launch_prefill_bf16(const PrefillArgs& a, hipStream_t stream);
 
 }  // namespace pa

@@ -58,7 +58,6 @@ constexpr int kWaves = kThreads / 64;
 #define PA_PREFILL_PAD 4
 #endif
 constexpr int kPad = PA_PREFILL_PAD;   // floats of padding per LDS row
-constexpr int kXcds = 8;        // XCDs of an MI355X
 
 // Keys per LDS tile: 32 at D = 64, 16 at D = 128 (two K + V buffers take
 // 34 KiB of LDS, so LDS does not cap occupancy below the register limit).
@@ -70,18 +69,6 @@ constexpr int key_tile() { return D == 64 ? PA_PREFILL_KTILE64 : 16; }
 
 __device__ __forceinline__ float4_t mfma16x16x4(float a, float b, float4_t c) {
   return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
-}
-
-// Visible key interval [lo, hi) for query positions [p0, p1] of a sequence of
-// length L (caller guarantees p0 <= p1 < L).
-__device__ __forceinline__ void key_range(int p0, int p1, int L, int window, int causal,
-                                          int& lo, int& hi) {
-  lo = 0;
-  hi = causal ? p1 + 1 : L;
-  if (window > 0) {
-    lo = max(0, p0 - window + 1);
-    if (!causal) hi = min(L, p1 + window);
-  }
 }
 
 // BIAS: 0 none, 1 materialised attn_bias[b, h, p, j], 2 T5 relative-position
@@ -103,9 +90,8 @@ pa_prefill_f32(PrefillArgs a) {
   // ---- XCD-aware workgroup numbering ----
   const int H = a.num_heads;
   const int n = blockIdx.x;
-  const int slot = n / kXcds;
-  const int pair = (slot / a.num_qtiles) * kXcds + n % kXcds;
-  const int tile = slot % a.num_qtiles;
+  int pair, tile;
+  prefill_tile_of(n, a.num_qtiles, pair, tile);
   if (pair >= a.num_seqs * H) return;
   const int b = pair / H;
   const int h = pair % H;
@@ -126,12 +112,12 @@ pa_prefill_f32(PrefillArgs a) {
   // workgroup and wave query ranges (positions), clamped to valid rows
   const int wg_last = min(t_first + kQT, nq) - 1;
   int wg_lo, wg_hi;
-  key_range(pos0 + t_first, pos0 + wg_last, L, a.window, CAUSAL, wg_lo, wg_hi);
+  prefill_key_range(pos0 + t_first, pos0 + wg_last, L, a.window, CAUSAL, wg_lo, wg_hi);
   const int w_first = t_first + wave * kWaveRows;
   const bool wave_active = w_first < nq;
   int wv_lo = 0, wv_hi = 0;
   if (wave_active)
-    key_range(pos0 + w_first, pos0 + min(w_first + kWaveRows, nq) - 1, L, a.window, CAUSAL,
+    prefill_key_range(pos0 + w_first, pos0 + min(w_first + kWaveRows, nq) - 1, L, a.window, CAUSAL,
               wv_lo, wv_hi);
 
   // per query group: first/last position, whether all 16 rows are valid,
@@ -454,8 +440,7 @@ hipError_t launch_d(PrefillArgs a, hipStream_t stream) {
 
 }  // namespace
 
-hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream) {
-  if (a.dtype != 0) return hipErrorInvalidValue;   // host API rejects bf16 first
+hipError_t launch_prefill_f32(const PrefillArgs& a, hipStream_t stream) {
   return a.head_dim == 64 ? launch_d<64, PA_PREFILL_GROUPS>(a, stream)
                           : launch_d<128, 1>(a, stream);
 }

@@ -131,7 +131,7 @@ def prefill_call(lib, **kw):
 
 @pytest.mark.parametrize("kw,status", [
     (dict(qsl=None), 1), (dict(causal=2), 2), (dict(tq=-1), 2), (dict(window=0), 2),
-    (dict(D=80), 3), (dict(dtype=1), 3), (dict(qsl=FAKE + 2), 4), (dict(k=None), 1),
+    (dict(D=80), 3), (dict(dtype=2), 3), (dict(qsl=FAKE + 2), 4), (dict(k=None), 1),
 ])
 def test_prefill_rejects_on_host(kw, status):
     lib = pa.lib()

@@ -1,0 +1,96 @@
+"""GPU parity of the bf16 MFMA prefill (v_mfma_f32_16x16x32_bf16) against the
+float64 oracle on the same bf16-rounded inputs: lengths, windows, causal
+masks, partial query sets, materialised / ragged / T5 biases, and a
+ModernBERT-shaped layer in bf16 checked on sampled sequences."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+from gpu_helpers import (BS, assert_close, gpu_prefill, log, oracle_prefill, sample_prefill,
+                         to_device, to_host)
+
+import sliding_window_mask_amd as pa
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+BF = torch.bfloat16
+
+
+def small(seed, lens, D=64, H=3, window=-1, causal=False, bias=None, q_lens=None, msl=None):
+    msl = msl or max(16, -(-max(lens) // 16) * 16)
+    return workloads.prefill_case(seed, num_seqs=len(lens), num_heads=H, head_dim=D, lens=lens,
+                                  max_seq_len=msl, dtype=BF, bias=bias, sliding_window=window,
+                                  causal=causal, q_lens=q_lens)
+
+
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("window", [-1, 1, 3, 16, 64])
+@pytest.mark.parametrize("causal", [False, True])
+def test_small_prefill_bf16(D, window, causal):
+    lens = [1, 15, 16, 17, 31, 32, 33, 63, 64, 65, 130]
+    case = to_device(small(900 + D + window, lens, D=D, window=window, causal=causal))
+    out = gpu_prefill(case)
+    assert out.dtype == BF
+    assert_close(out, oracle_prefill(case), BF, "bf16 D=%d W=%d causal=%s" % (D, window, causal))
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("window", [-1, 9])
+def test_prefill_bf16_with_bias(causal, window):
+    case = to_device(small(910, [5, 33, 70, 129], window=window, causal=causal, bias="normal",
+                           msl=144))
+    assert_close(gpu_prefill(case), oracle_prefill(case), BF, "bf16 bias")
+
+
+def test_prefill_bf16_partial_queries():
+    case = to_device(small(920, [40, 17, 100, 130], q_lens=[4, 17, 1, 70], window=21,
+                           causal=True, msl=144))
+    assert_close(gpu_prefill(case), oracle_prefill(case), BF, "bf16 partial q")
+
+
+def test_prefill_bf16_window_one_returns_own_value():
+    case = to_device(small(930, [1, 20, 77], window=1))
+    out = gpu_prefill(case).cpu()
+    qsl = case.query_start_loc.cpu()
+    for b in range(3):
+        for t in range(int(case.lens[b])):
+            v = case.v_cache[case.block_tables[b, t // BS].long(), :, t % BS, :].cpu()
+            assert torch.equal(out[int(qsl[b]) + t].view(torch.int16), v.view(torch.int16))
+
+
+@pytest.mark.parametrize("bidir,causal", [(1, False), (0, True)])
+def test_prefill_bf16_relpos(bidir, causal):
+    case = to_device(small(940, [70, 200, 333], causal=causal, msl=336))
+    table = (torch.randn(3, 32, generator=torch.Generator().manual_seed(4)) * 0.5).to(DEV)
+    out = pa.paged_attn_prefill_relpos(case.q, case.k_cache, case.v_cache, case.block_tables,
+                                       case.context_lens, case.query_start_loc, table, 32, 128,
+                                       bidir, -1, causal, case.scale,
+                                       max_seq_len=case.max_seq_len)
+    torch.cuda.synchronize()
+    h = to_host(case)
+    ref = oracle.prefill_relpos(h.q, h.k_cache, h.v_cache, h.block_tables, h.context_lens,
+                                h.query_start_loc, table.cpu(), 32, 128, bidir, -1, int(causal),
+                                h.scale, h.max_seq_len)
+    assert_close(out, ref, BF, "bf16 relpos")
+
+
+def test_prefill_bf16_deterministic():
+    case = to_device(small(950, [300, 511, 64], window=64, msl=512))
+    a = gpu_prefill(case)
+    assert torch.equal(gpu_prefill(case).view(torch.int16), a.view(torch.int16))
+
+
+@pytest.mark.parametrize("layer", [0, 1])
+def test_modernbert_shaped_bf16_layer_sampled(layer):
+    log("bf16 modernbert-shaped layer %d" % layer)
+    case = workloads.prefill_case(4, num_seqs=32, num_heads=12, head_dim=64, lens=(64, 1024),
+                                  max_seq_len=1024, dtype=BF,
+                                  sliding_window=workloads.modernbert_window(layer),
+                                  device=DEV, layer_seed=[4, layer])
+    out = gpu_prefill(case)
+    L = case.lens
+    seqs = sorted(set([int(np.argmax(L)), int(np.argmin(L)), 5, 17]))
+    sub = sample_prefill(case, seqs)
+    assert_close(out[sub.rows.to(DEV)], oracle_prefill(sub), BF, "bf16 layer %d" % layer)
