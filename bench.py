@@ -71,10 +71,21 @@ def read_traffic(workload, kernel_src):
         return None
 
 
+SETTLE_S = 0.3     # untimed run time before the timed steps, for the clocks to ramp
+
+
 def time_steps(fn, steps, warmup):
+    """W untimed warmup steps, then more untimed steps until SETTLE_S seconds
+    of warmup have passed (an idle MI355X ramps its clocks over the first
+    ~0.1 s of sustained work; short steps otherwise get timed at low clock),
+    then exactly `steps` timed steps between two events."""
+    t0 = time.perf_counter()
     for _ in range(warmup):
         fn()
     torch.cuda.synchronize()
+    while time.perf_counter() - t0 < SETTLE_S:
+        fn()
+        torch.cuda.synchronize()
     start = torch.cuda.Event(enable_timing=True)
     end = torch.cuda.Event(enable_timing=True)
     start.record()

@@ -5,13 +5,25 @@
 // bias), for bf16 q / K / V / out, on v_mfma_f32_16x16x32_bf16: bf16 products
 // accumulated in fp32. The softmax runs in fp32; the weights P are rounded to
 // bf16 for the P.V contraction and the row sums are taken over the same
-// rounded weights, so out = sum(P~ V) / sum(P~) is an exact weighted mean.
+// rounded weights (one more MFMA, against an all-ones operand), so
+// out = sum(P~ V) / sum(P~) is an exact weighted mean.
 //
-// One workgroup of 4 wave64s per (64-query tile, head, sequence), numbered
-// so that all query tiles of a (sequence, head) share an XCD. Keys are
-// walked in 32-key tiles through a double-buffered LDS ring (tile k+2 in
-// flight from memory while tile k is multiplied, block-table entries one
-// tile further ahead).
+// Scores stay unscaled (q.k + a) until the exponent, where the scale enters
+// through one fma: p = 2^(x * scale * log2(e) - m). The running max is then
+// taken on unscaled scores, which needs a positive multiplier: a negative
+// scale is folded into q and the bias (both negated, multiplier |scale|), and
+// a zero scale, under which every visible score is 0, into q = 0 with no bias
+// and multiplier 1.
+//
+// One workgroup per (64-query tile, head, sequence), numbered so that all
+// query tiles of a (sequence, head) share an XCD. Each wave owns kSub
+// sub-tiles of 16 queries and multiplies every K and V operand it reads from
+// LDS into all of them. The default is 4 waves x 1 sub-tile; 2 waves x 2
+// sub-tiles (PA_PREFILL_BF16_SUB64=2, head_dim 64) halves the LDS reads per
+// MFMA but needs ~130 VGPRs, and measured slower on the ModernBERT-shaped
+// layers (3-4 waves per SIMD instead of 5). Keys are walked in 32-key tiles through a
+// double-buffered LDS ring (tile k+2 in flight from memory while tile k is
+// multiplied, block-table entries one tile further ahead).
 //
 // Operand layout (16x16x32, lane l, g = l / 16, c = l % 16; every lane feeds
 // 8 bf16 of A and B, and lanes of one group g contract the same 8 positions):
@@ -33,31 +45,54 @@ namespace {
 typedef float float4_t __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 
-constexpr int kThreads = 256;
-constexpr int kQT = 64;         // queries per workgroup (16 per wave)
+#ifndef PA_PREFILL_BF16_VEARLY
+#define PA_PREFILL_BF16_VEARLY 0
+#endif
+#ifndef PA_PREFILL_BF16_SUB64
+#define PA_PREFILL_BF16_SUB64 1     // 16-query sub-tiles per wave, head_dim 64
+#endif
+
+constexpr int kQT = 64;         // queries per workgroup
 constexpr int kKT = 32;         // keys per tile (one 32-deep P.V contraction)
 constexpr int kVRow = kKT + 4;  // V^T row stride (bf16)
+
+template <int D>
+struct Cfg {
+  static constexpr int kSub = D == 64 ? PA_PREFILL_BF16_SUB64 : 1;
+  static constexpr int kWaves = kQT / (16 * kSub);
+  static constexpr int kThreads = 64 * kWaves;
+};
 
 __device__ __forceinline__ float4_t mfma_bf16(const bf16x8_t& a, const bf16x8_t& b,
                                               float4_t c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
-__device__ __forceinline__ float bf16_bits_to_f32(uint32_t bits16) {
-  return __uint_as_float(bits16 << 16);
+template <int N>
+struct IntC {
+  static constexpr int value = N;
+};
+
+// IEEE maximum (NaN-propagating): maps onto v_maximum3_f32 with no operand
+// canonicalisation, which fmaxf needs on raw MFMA results.
+__device__ __forceinline__ float vmax(float x, float y) {
+  return __builtin_elementwise_maximum(x, y);
 }
 
 // BIAS: 0 none, 1 materialised (padded or ragged) fp32 bias, 2 T5 relative
 // position bias from a bucket table.
 template <int D, int BIAS, bool CAUSAL, bool WINDOW>
-__global__ void __launch_bounds__(kThreads)
+__global__ void __launch_bounds__(Cfg<D>::kThreads)
 pa_prefill_bf16(PrefillArgs a) {
+  constexpr int kSub = Cfg<D>::kSub;
+  constexpr int kThreads = Cfg<D>::kThreads;
   constexpr int kKRow = D + 8;                 // K row stride in LDS (bf16)
   constexpr int kSteps = D / 32;               // 8-element steps per lane group
   constexpr int kNDT = D / 16;                 // 16-dim output slices
   constexpr int kKLoads = kKT * D / 8 / kThreads;        // 16-byte K loads per thread
   constexpr int kVUnits = (D / 2) * (kKT / 4) / kThreads;  // (2 dims x 4 keys) units
   static_assert(kKLoads >= 1 && kVUnits >= 1, "tile shape");
+  static_assert(D == 64 || D == 128, "head_dim");
 
   const int H = a.num_heads;
   int pair, tile;
@@ -68,7 +103,7 @@ pa_prefill_bf16(PrefillArgs a) {
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform
   const int c = lane & 15;
   const int g = lane >> 4;
 
@@ -82,30 +117,48 @@ pa_prefill_bf16(PrefillArgs a) {
   const int wg_last = min(t_first + kQT, nq) - 1;
   int wg_lo, wg_hi;
   prefill_key_range(pos0 + t_first, pos0 + wg_last, L, a.window, CAUSAL, wg_lo, wg_hi);
-  const int w_first = t_first + wave * 16;
+  const int w_first = t_first + wave * 16 * kSub;
   const bool wave_active = w_first < nq;
-  const int w_last = min(w_first + 16, nq) - 1;
-  const bool wave_full = w_last == w_first + 15;
   int wv_lo = 0, wv_hi = 0;
-  if (wave_active) prefill_key_range(pos0 + w_first, pos0 + w_last, L, a.window, CAUSAL, wv_lo, wv_hi);
-  const int wp0 = pos0 + w_first, wp1 = pos0 + w_last;
+  if (wave_active)
+    prefill_key_range(pos0 + w_first, pos0 + min(w_first + 16 * kSub, nq) - 1, L, a.window,
+                      CAUSAL, wv_lo, wv_hi);
 
-  const int t = w_first + c;
-  const bool row_ok = t < nq;
-  const int p = pos0 + t;
-  const float cs = a.scale_log2;
+  // exponent multiplier (> 0) and the sign the unscaled scores carry
+  const float cs = a.scale_log2 == 0.0f ? 1.0f : fabsf(a.scale_log2);
+  const float bmul = a.scale_log2 == 0.0f ? 0.0f : (a.scale_log2 < 0.0f ? -1.0f : 1.0f);
 
-  // Q operand: kSteps x 8 bf16 (rows past n_q are zero)
-  bf16x8_t qv[kSteps];
-  {
-    const int tq = row_ok ? t : t_first;
+  // per sub-tile: query row of lane c, its position, whether it exists; the
+  // sub-tile's first / last position and whether all 16 rows exist (uniform)
+  int t_row[kSub], p_row[kSub], sp0[kSub], sp1[kSub];
+  bool row_ok[kSub], sub_full[kSub];
+#pragma unroll
+  for (int sb = 0; sb < kSub; ++sb) {
+    const int f = w_first + 16 * sb;
+    t_row[sb] = f + c;
+    row_ok[sb] = t_row[sb] < nq;
+    p_row[sb] = pos0 + t_row[sb];
+    sp0[sb] = pos0 + f;
+    sp1[sb] = pos0 + min(f + 15, nq - 1);
+    sub_full[sb] = f + 15 < nq;
+  }
+
+  // Q operands: kSteps x 8 bf16 per sub-tile (rows past n_q, and every row
+  // under a zero scale, are zero; a negative scale flips the sign bits)
+  bf16x8_t qv[kSub][kSteps];
+#pragma unroll
+  for (int sb = 0; sb < kSub; ++sb) {
+    const int tq = row_ok[sb] ? t_row[sb] : t_first;
+    const bool qzero = !row_ok[sb] || bmul == 0.0f;
+    const uint32_t qsign = bmul < 0.0f ? 0x80008000u : 0u;
     const uint4* qrow = reinterpret_cast<const uint4*>(
         static_cast<const uint16_t*>(a.q) + ((int64_t)(q0 + tq) * H + h) * D + (D / 4) * g);
 #pragma unroll
     for (int st = 0; st < kSteps; ++st) {
       uint4 v = qrow[st];
-      if (!row_ok) v = make_uint4(0u, 0u, 0u, 0u);
-      qv[st] = __builtin_bit_cast(bf16x8_t, v);
+      v = qzero ? make_uint4(0u, 0u, 0u, 0u)
+                : make_uint4(v.x ^ qsign, v.y ^ qsign, v.z ^ qsign, v.w ^ qsign);
+      qv[sb][st] = __builtin_bit_cast(bf16x8_t, v);
     }
   }
 
@@ -116,7 +169,7 @@ pa_prefill_bf16(PrefillArgs a) {
   if constexpr (BIAS == 2) {
     const float* head_row = a.rel.table + (int64_t)h * a.rel.num_buckets;
     for (int i = tid; i <= 2 * rel_md; i += kThreads)
-      rel_lds[i] = rel_bias(i - rel_md, a.rel, head_row) * cs;
+      rel_lds[i] = bmul == 0.0f ? 0.0f : rel_bias(i - rel_md, a.rel, head_row) * bmul;
   }
 
   const uint16_t* kc = static_cast<const uint16_t*>(a.k_cache);
@@ -135,9 +188,18 @@ pa_prefill_bf16(PrefillArgs a) {
     }
   };
   // global -> registers: K as 16-byte row pieces, V as 4-byte (2-dim) pieces
-  // of 4 consecutive keys, repacked below into V^T rows
-  uint4 kst[kKLoads];
-  uint32_t vst[kVUnits][4];
+  // of 4 consecutive keys, repacked below into V^T rows. A cache block holds
+  // 2D pieces of either kind, a multiple of 64, so each wave's pieces of one
+  // load lie in one block: the address is a uniform block base plus a
+  // per-lane offset that is the same for every tile. Rows at or past L are
+  // read from the sequence's last block, or from block 0 for a block past it
+  // (both in the pool): K there only feeds scores the mask drops, and V is
+  // zeroed so that a zero weight never meets a NaN.
+  // (vectors rather than arrays, so that they stay in registers)
+  typedef uint32_t kst_t __attribute__((ext_vector_type(4 * kKLoads)));
+  typedef uint32_t vst_t __attribute__((ext_vector_type(4 * kVUnits)));
+  kst_t kst;
+  vst_t vst;
   auto fetch = [&](int tk) {
     const int base = kstart + tk * kKT;
     const bool tail = base + kKT > L;
@@ -145,21 +207,29 @@ pa_prefill_bf16(PrefillArgs a) {
     for (int i = 0; i < kKLoads; ++i) {
       const int e = i * kThreads + tid;        // 16-byte piece index in the tile
       const int r = e / (D / 8), col = (e % (D / 8)) * 8;
-      const int j = base + r;
-      const int64_t off = (((int64_t)tb[r / kBlockSize] * H + h) * kBlockSize + j % kBlockSize) * D + col;
-      kst[i] = (!tail || j < L) ? *reinterpret_cast<const uint4*>(kc + off)
-                                : make_uint4(0u, 0u, 0u, 0u);
+      const int sel = (i * kThreads + wave * 64) / (D / 8) / kBlockSize;
+      const uint16_t* blk = kc + ((int64_t)tb[sel] * H + h) * (kBlockSize * D);
+      const uint4 v = *reinterpret_cast<const uint4*>(blk + (uint32_t)((r % kBlockSize) * D + col));
+      kst[4 * i] = v.x;
+      kst[4 * i + 1] = v.y;
+      kst[4 * i + 2] = v.z;
+      kst[4 * i + 3] = v.w;
     }
 #pragma unroll
     for (int u = 0; u < kVUnits; ++u) {
       const int e = u * kThreads + tid;
       const int dp = e % (D / 2), kg = e / (D / 2);   // dims 2dp, 2dp+1; keys 4kg..4kg+3
+      const int sel = (u * kThreads + wave * 64) / (D / 2) / (kBlockSize / 4);
+      const uint16_t* blk = vc + ((int64_t)tb[sel] * H + h) * (kBlockSize * D);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int r = 4 * kg + i;
-        const int j = base + r;
-        const int64_t off = (((int64_t)tb[r / kBlockSize] * H + h) * kBlockSize + j % kBlockSize) * D + 2 * dp;
-        vst[u][i] = (!tail || j < L) ? *reinterpret_cast<const uint32_t*>(vc + off) : 0u;
+        vst[4 * u + i] = *reinterpret_cast<const uint32_t*>(
+            blk + (uint32_t)((r % kBlockSize) * D + 2 * dp));
+      }
+      if (tail) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) vst[4 * u + i] = base + 4 * kg + i < L ? vst[4 * u + i] : 0u;
       }
     }
   };
@@ -168,33 +238,48 @@ pa_prefill_bf16(PrefillArgs a) {
     for (int i = 0; i < kKLoads; ++i) {
       const int e = i * kThreads + tid;
       const int r = e / (D / 8), col = (e % (D / 8)) * 8;
-      *reinterpret_cast<uint4*>(&k_lds[buf][r * kKRow + col]) = kst[i];
+      *reinterpret_cast<uint4*>(&k_lds[buf][r * kKRow + col]) =
+          make_uint4(kst[4 * i], kst[4 * i + 1], kst[4 * i + 2], kst[4 * i + 3]);
     }
 #pragma unroll
     for (int u = 0; u < kVUnits; ++u) {
       const int e = u * kThreads + tid;
       const int dp = e % (D / 2), kg = e / (D / 2);
       // low halves = dim 2dp of keys 4kg..4kg+3, high halves = dim 2dp+1
-      const uint2 lo = make_uint2(__builtin_amdgcn_perm(vst[u][1], vst[u][0], 0x05040100u),
-                                  __builtin_amdgcn_perm(vst[u][3], vst[u][2], 0x05040100u));
-      const uint2 hi = make_uint2(__builtin_amdgcn_perm(vst[u][1], vst[u][0], 0x07060302u),
-                                  __builtin_amdgcn_perm(vst[u][3], vst[u][2], 0x07060302u));
+      const uint32_t x0 = vst[4 * u], x1 = vst[4 * u + 1], x2 = vst[4 * u + 2],
+                     x3 = vst[4 * u + 3];
+      const uint2 lo = make_uint2(__builtin_amdgcn_perm(x1, x0, 0x05040100u),
+                                  __builtin_amdgcn_perm(x3, x2, 0x05040100u));
+      const uint2 hi = make_uint2(__builtin_amdgcn_perm(x1, x0, 0x07060302u),
+                                  __builtin_amdgcn_perm(x3, x2, 0x07060302u));
       *reinterpret_cast<uint2*>(&v_lds[buf][(2 * dp) * kVRow + 4 * kg]) = lo;
       *reinterpret_cast<uint2*>(&v_lds[buf][(2 * dp + 1) * kVRow + 4 * kg]) = hi;
     }
   };
 
-  float4_t acc[kNDT];
+  float4_t acc[kSub][kNDT];
+  // row sums: lacc[sb][r] = sum of the rounded weights of query c (every r)
+  float4_t lacc[kSub];
+  float m_ref[kSub], neg_m[kSub];   // running reference (base 2), and -m_ref once finite
+  const float* bias_row[kSub];
 #pragma unroll
-  for (int dt = 0; dt < kNDT; ++dt) acc[dt] = float4_t{0, 0, 0, 0};
-  float m_ref = -INFINITY, l_run = 0.0f;
-  const int tb_row = row_ok ? t : t_first;
-  const float* bias_row = nullptr;
-  if (BIAS == 1)
-    bias_row = a.bias_start
-                   ? a.attn_bias + a.bias_start[b] + ((int64_t)h * nq + tb_row) * L
-                   : a.attn_bias + (((int64_t)b * H + h) * a.max_seq_len + pos0 + tb_row) *
-                                       a.max_seq_len;
+  for (int sb = 0; sb < kSub; ++sb) {
+#pragma unroll
+    for (int dt = 0; dt < kNDT; ++dt) acc[sb][dt] = float4_t{0, 0, 0, 0};
+    lacc[sb] = float4_t{0, 0, 0, 0};
+    m_ref[sb] = -INFINITY;
+    neg_m[sb] = 0.0f;
+    bias_row[sb] = nullptr;
+    if (BIAS == 1) {
+      const int tb_row = row_ok[sb] ? t_row[sb] : t_first;
+      bias_row[sb] = a.bias_start
+                         ? a.attn_bias + a.bias_start[b] + ((int64_t)h * nq + tb_row) * L
+                         : a.attn_bias + (((int64_t)b * H + h) * a.max_seq_len + pos0 + tb_row) *
+                                             a.max_seq_len;
+    }
+  }
+  bf16x8_t ones = __builtin_bit_cast(
+      bf16x8_t, make_uint4(0x3f803f80u, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u));
 
   if (ntiles > 0) {
     load_table(0);
@@ -208,85 +293,112 @@ pa_prefill_bf16(PrefillArgs a) {
   }
   __syncthreads();
 
-  for (int tk = 0; tk < ntiles; ++tk) {
-    const int buf = tk & 1;
+  // one key tile; the LDS buffer is a compile-time constant so that every
+  // LDS address is a per-lane base plus an immediate
+  auto tile_step = [&](int tk, auto buf_c) {
+    constexpr int buf = decltype(buf_c)::value;
+    asm("" : "+v"(ones));   // keep the all-ones operand resident, not rebuilt per tile
     const int base = kstart + tk * kKT;
     if (wave_active && base < wv_hi && base + kKT > wv_lo) {
-      // ---- S^T for the two 16-key chunks ----
-      float4_t s[2] = {float4_t{0, 0, 0, 0}, float4_t{0, 0, 0, 0}};
+      // ---- S^T for the two 16-key chunks of every sub-tile ----
+      float4_t s[kSub][2];
+#pragma unroll
+      for (int sb = 0; sb < kSub; ++sb) s[sb][0] = s[sb][1] = float4_t{0, 0, 0, 0};
 #pragma unroll
       for (int st = 0; st < kSteps; ++st) {
 #pragma unroll
         for (int ch = 0; ch < 2; ++ch) {
           const uint4 kv = *reinterpret_cast<const uint4*>(
               &k_lds[buf][(ch * 16 + c) * kKRow + (D / 4) * g + 8 * st]);
-          s[ch] = mfma_bf16(__builtin_bit_cast(bf16x8_t, kv), qv[st], s[ch]);
+#pragma unroll
+          for (int sb = 0; sb < kSub; ++sb)
+            s[sb][ch] = mfma_bf16(__builtin_bit_cast(bf16x8_t, kv), qv[sb][st], s[sb][ch]);
         }
       }
-      // ---- scale, bias, mask (base-2 scores) ----
+      // V^T operands of this tile (read early, while the softmax runs, when
+      // PA_PREFILL_BF16_VEARLY is set)
+      uint4 vv[kNDT];
+      auto read_v = [&]() {
 #pragma unroll
-      for (int ch = 0; ch < 2; ++ch) {
-        const int c0 = base + ch * 16;
-        const int j0 = c0 + 4 * g;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          float x = s[ch][r] * cs;
-          if constexpr (BIAS == 1) x = x + bias_row[min(j0 + r, L - 1)] * cs;
-          if constexpr (BIAS == 2) x = x + rel_lds[min(max(j0 + r - p, -rel_md), rel_md) + rel_md];
-          s[ch][r] = x;
+        for (int dt = 0; dt < kNDT; ++dt) {
+          const uint16_t* vrow = &v_lds[buf][(16 * dt + c) * kVRow + 4 * g];
+          const uint2 v0 = *reinterpret_cast<const uint2*>(vrow);
+          const uint2 v1 = *reinterpret_cast<const uint2*>(vrow + 16);
+          vv[dt] = make_uint4(v0.x, v0.y, v1.x, v1.y);
         }
-        bool whole = wave_full && c0 + 16 <= L;
-        if constexpr (CAUSAL) whole = whole && c0 + 15 <= wp0;
-        if constexpr (WINDOW) whole = whole && wp1 - c0 < a.window && c0 + 15 - wp0 < a.window;
-        if (!whole) {
+      };
+      if (PA_PREFILL_BF16_VEARLY) read_v();
+      bf16x8_t pw[kSub];
 #pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const int j = j0 + r;
-            bool vis = row_ok && j < L;
-            if constexpr (CAUSAL) vis = vis && j <= p;
-            if constexpr (WINDOW) vis = vis && abs(p - j) < a.window;
-            s[ch][r] = vis ? s[ch][r] : -INFINITY;
+      for (int sb = 0; sb < kSub; ++sb) {
+        // ---- bias and mask (unscaled scores) ----
+#pragma unroll
+        for (int ch = 0; ch < 2; ++ch) {
+          const int c0 = base + ch * 16;
+          const int j0 = c0 + 4 * g;
+          if constexpr (BIAS == 1) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+              s[sb][ch][r] = fmaf(bias_row[sb][min(j0 + r, L - 1)], bmul, s[sb][ch][r]);
+          }
+          if constexpr (BIAS == 2) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+              s[sb][ch][r] += rel_lds[min(max(j0 + r - p_row[sb], -rel_md), rel_md) + rel_md];
+          }
+          bool whole = sub_full[sb] && c0 + 16 <= L;
+          if constexpr (CAUSAL) whole = whole && c0 + 15 <= sp0[sb];
+          if constexpr (WINDOW)
+            whole = whole && sp1[sb] - c0 < a.window && c0 + 15 - sp0[sb] < a.window;
+          if (!whole) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+              const int j = j0 + r;
+              bool vis = row_ok[sb] && j < L;
+              if constexpr (CAUSAL) vis = vis && j <= p_row[sb];
+              if constexpr (WINDOW) vis = vis && abs(p_row[sb] - j) < a.window;
+              s[sb][ch][r] = vis ? s[sb][ch][r] : -INFINITY;
+            }
           }
         }
-      }
-      // ---- online softmax with a lazily moved reference (as in fp32) ----
-      float mt = fmaxf(fmaxf(fmaxf(s[0][0], s[0][1]), fmaxf(s[0][2], s[0][3])),
-                       fmaxf(fmaxf(s[1][0], s[1][1]), fmaxf(s[1][2], s[1][3])));
-      {
-        const auto x16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(mt),
-                                                          __float_as_uint(mt), false, false);
-        mt = fmaxf(__uint_as_float(x16[0]), __uint_as_float(x16[1]));
-        const auto x32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(mt),
-                                                          __float_as_uint(mt), false, false);
-        mt = fmaxf(__uint_as_float(x32[0]), __uint_as_float(x32[1]));
-      }
-      const bool move = mt > m_ref + 8.0f;
-      if (__builtin_amdgcn_ballot_w64(move) != 0) {
-        const float alpha = move ? __builtin_amdgcn_exp2f(m_ref - mt) : 1.0f;
-        m_ref = move ? mt : m_ref;
-        l_run *= alpha;
+        // ---- online softmax with a lazily moved reference (as in fp32), in
+        // base-2 units: m_ref is a scaled score ----
+        float mt = vmax(vmax(vmax(s[sb][0][0], s[sb][0][1]), vmax(s[sb][0][2], s[sb][0][3])),
+                        vmax(vmax(s[sb][1][0], s[sb][1][1]), vmax(s[sb][1][2], s[sb][1][3])));
+        {
+          const auto x16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(mt),
+                                                            __float_as_uint(mt), false, false);
+          mt = vmax(__uint_as_float(x16[0]), __uint_as_float(x16[1]));
+          const auto x32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(mt),
+                                                            __float_as_uint(mt), false, false);
+          mt = vmax(__uint_as_float(x32[0]), __uint_as_float(x32[1])) * cs;
+        }
+        const bool move = mt > m_ref[sb] + 8.0f;
+        if (__builtin_amdgcn_ballot_w64(move) != 0) {
+          const float alpha = move ? __builtin_amdgcn_exp2f(m_ref[sb] - mt) : 1.0f;
+          m_ref[sb] = move ? mt : m_ref[sb];
+          neg_m[sb] = move ? -mt : neg_m[sb];
+          lacc[sb] *= alpha;
 #pragma unroll
-        for (int dt = 0; dt < kNDT; ++dt) acc[dt] *= alpha;
-      }
-      const float m_use = (m_ref == -INFINITY) ? 0.0f : m_ref;
-      bf16x8_t pw;
+          for (int dt = 0; dt < kNDT; ++dt) acc[sb][dt] *= alpha;
+        }
 #pragma unroll
-      for (int ch = 0; ch < 2; ++ch) {
+        for (int ch = 0; ch < 2; ++ch) {
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const __bf16 pb = (__bf16)__builtin_amdgcn_exp2f(s[ch][r] - m_use);
-          pw[4 * ch + r] = pb;
-          l_run += bf16_bits_to_f32(__builtin_bit_cast(uint16_t, pb));
+          for (int r = 0; r < 4; ++r)
+            pw[sb][4 * ch + r] =
+                (__bf16)__builtin_amdgcn_exp2f(fmaf(s[sb][ch][r], cs, neg_m[sb]));
         }
       }
-      // ---- O^T += V^T P^T over the tile's 32 keys ----
+      if (!PA_PREFILL_BF16_VEARLY) read_v();
+      // ---- O^T += V^T P^T over the tile's 32 keys, row sums alongside ----
+#pragma unroll
+      for (int sb = 0; sb < kSub; ++sb) lacc[sb] = mfma_bf16(ones, pw[sb], lacc[sb]);
 #pragma unroll
       for (int dt = 0; dt < kNDT; ++dt) {
-        const uint16_t* vrow = &v_lds[buf][(16 * dt + c) * kVRow + 4 * g];
-        const uint2 v0 = *reinterpret_cast<const uint2*>(vrow);
-        const uint2 v1 = *reinterpret_cast<const uint2*>(vrow + 16);
-        const uint4 vv = make_uint4(v0.x, v0.y, v1.x, v1.y);
-        acc[dt] = mfma_bf16(__builtin_bit_cast(bf16x8_t, vv), pw, acc[dt]);
+#pragma unroll
+        for (int sb = 0; sb < kSub; ++sb)
+          acc[sb][dt] = mfma_bf16(__builtin_bit_cast(bf16x8_t, vv[dt]), pw[sb], acc[sb][dt]);
       }
     }
     if (tk + 1 < ntiles) stash(buf ^ 1);
@@ -295,40 +407,42 @@ pa_prefill_bf16(PrefillArgs a) {
       if (tk + 3 < ntiles) load_table(tk + 3);
     }
     __syncthreads();
+  };
+  for (int tk = 0; tk < ntiles; tk += 2) {
+    tile_step(tk, IntC<0>{});
+    if (tk + 1 < ntiles) tile_step(tk + 1, IntC<1>{});
   }
 
   // ---- epilogue: out = O / l, rounded to bf16 ----
-  float l_tot = l_run;
-  l_tot += __shfl_xor(l_tot, 16);
-  l_tot += __shfl_xor(l_tot, 32);
-  if (!row_ok) return;
-  const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
-  uint16_t* orow = static_cast<uint16_t*>(a.out) + ((int64_t)(q0 + t) * H + h) * D;
 #pragma unroll
-  for (int dt = 0; dt < kNDT; ++dt) {
-    typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
-    bf16x4_t o = {(__bf16)(acc[dt][0] * inv), (__bf16)(acc[dt][1] * inv),
-                  (__bf16)(acc[dt][2] * inv), (__bf16)(acc[dt][3] * inv)};
-    *reinterpret_cast<bf16x4_t*>(orow + 16 * dt + 4 * g) = o;
+  for (int sb = 0; sb < kSub; ++sb) {
+    if (!row_ok[sb]) continue;
+    const float l_tot = lacc[sb][0];
+    const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
+    uint16_t* orow = static_cast<uint16_t*>(a.out) + ((int64_t)(q0 + t_row[sb]) * H + h) * D;
+#pragma unroll
+    for (int dt = 0; dt < kNDT; ++dt) {
+      typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
+      bf16x4_t o = {(__bf16)(acc[sb][dt][0] * inv), (__bf16)(acc[sb][dt][1] * inv),
+                    (__bf16)(acc[sb][dt][2] * inv), (__bf16)(acc[sb][dt][3] * inv)};
+      *reinterpret_cast<bf16x4_t*>(orow + 16 * dt + 4 * g) = o;
+    }
   }
 }
 
 template <int D, int BIAS>
 void launch_mask(const PrefillArgs& a, dim3 grid, hipStream_t stream) {
+  const dim3 block(Cfg<D>::kThreads);
   if (a.causal) {
     if (a.window > 0)
-      hipLaunchKernelGGL((pa_prefill_bf16<D, BIAS, true, true>), grid, dim3(kThreads), 0,
-                         stream, a);
+      hipLaunchKernelGGL((pa_prefill_bf16<D, BIAS, true, true>), grid, block, 0, stream, a);
     else
-      hipLaunchKernelGGL((pa_prefill_bf16<D, BIAS, true, false>), grid, dim3(kThreads), 0,
-                         stream, a);
+      hipLaunchKernelGGL((pa_prefill_bf16<D, BIAS, true, false>), grid, block, 0, stream, a);
   } else {
     if (a.window > 0)
-      hipLaunchKernelGGL((pa_prefill_bf16<D, BIAS, false, true>), grid, dim3(kThreads), 0,
-                         stream, a);
+      hipLaunchKernelGGL((pa_prefill_bf16<D, BIAS, false, true>), grid, block, 0, stream, a);
     else
-      hipLaunchKernelGGL((pa_prefill_bf16<D, BIAS, false, false>), grid, dim3(kThreads), 0,
-                         stream, a);
+      hipLaunchKernelGGL((pa_prefill_bf16<D, BIAS, false, false>), grid, block, 0, stream, a);
   }
 }
 

@@ -123,10 +123,11 @@ def small_decode(seed, dtype=torch.float32, bias="normal", window=-1, lens=(1, 4
 
 
 def small_prefill(seed, dtype=torch.float32, bias="normal", window=-1, causal=False,
-                  lens=(1, 40), q_lens=None, H=2, D=8, B=3, max_seq_len=48):
+                  lens=(1, 40), q_lens=None, H=2, D=8, B=3, max_seq_len=48, scale=None):
     return workloads.prefill_case(seed, num_seqs=B, num_heads=H, head_dim=D, lens=lens,
                                   max_seq_len=max_seq_len, dtype=dtype, bias=bias,
-                                  sliding_window=window, causal=causal, q_lens=q_lens)
+                                  sliding_window=window, causal=causal, q_lens=q_lens,
+                                  scale=scale)
 
 
 # ----------------------------------------------------------------------------
@@ -289,6 +290,47 @@ def test_constant_bias_equals_no_bias():
     case = small_decode(58, bias=None)
     c = torch.full((4, 3, 48), 3.75)
     np.testing.assert_allclose(run_decode(case, bias=c), run_decode(case), rtol=0, atol=1e-12)
+
+
+def test_zero_scale_is_the_mean_of_visible_values():
+    # scale 0 makes every visible score 0 whatever q and the bias hold, so each
+    # output is the plain average of the V rows the query may see
+    case = small_decode(61, window=7, lens=(1, 40), scale=0.0)
+    out = run_decode(case)
+    for b in range(case.num_seqs):
+        L = int(case.lens[b])
+        V = unpage(case.v_cache, case.block_tables[b], L)              # [H, L, D]
+        np.testing.assert_allclose(out[b], V[:, max(0, L - 7):L].mean(1).numpy(),
+                                   rtol=0, atol=1e-12)
+    pc = small_prefill(62, causal=True, window=5, scale=0.0)
+    pout = run_prefill(pc)
+    qsl = pc.query_start_loc
+    for b in range(pc.num_seqs):
+        L = int(pc.lens[b])
+        V = unpage(pc.v_cache, pc.block_tables[b], L)
+        for t in range(int(qsl[b + 1] - qsl[b])):
+            p = L - int(qsl[b + 1] - qsl[b]) + t
+            np.testing.assert_allclose(pout[int(qsl[b]) + t], V[:, max(0, p - 4):p + 1].mean(1),
+                                       rtol=0, atol=1e-12)
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+def test_negative_scale(dtype):
+    # a negative scale weights low scores most; (q, A, -s) and (-q, -A, s)
+    # give every key the same score, so the two agree bit for bit, and both
+    # match SDPA called with the negative scale
+    case = small_decode(63, dtype=dtype, window=9, lens=(1, 45), scale=-0.3)
+    out = run_decode(case)
+    np.testing.assert_allclose(out, sdpa_decode(case), rtol=0, atol=1e-12)
+    flipped = oracle.decode(-case.q, case.k_cache, case.v_cache, case.block_tables,
+                            case.context_lens, -case.attn_bias, 9, -case.scale, case.max_seq_len)
+    np.testing.assert_array_equal(out, flipped)
+    pc = small_prefill(64, dtype=dtype, causal=True, window=6, scale=-0.3)
+    pout = run_prefill(pc)
+    np.testing.assert_allclose(pout, sdpa_prefill(pc), rtol=0, atol=1e-12)
+    pflip = oracle.prefill(-pc.q, pc.k_cache, pc.v_cache, pc.block_tables, pc.context_lens,
+                           pc.query_start_loc, -pc.attn_bias, 6, 1, -pc.scale, pc.max_seq_len)
+    np.testing.assert_array_equal(pout, pflip)
 
 
 def test_empty_and_fully_masked_rows_are_zero():
