@@ -71,6 +71,17 @@ __device__ __forceinline__ float4_t mfma16x16x4(float a, float b, float4_t c) {
   return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
 }
 
+template <int N>
+struct IntC {
+  static constexpr int value = N;
+};
+
+// IEEE maximum (NaN-propagating): maps onto v_maximum3_f32 with no operand
+// canonicalisation, which fmaxf needs on raw MFMA results.
+__device__ __forceinline__ float vmax(float x, float y) {
+  return __builtin_elementwise_maximum(x, y);
+}
+
 // BIAS: 0 none, 1 materialised attn_bias[b, h, p, j], 2 T5 relative-position
 // bias from a bucket table (a.rel).
 template <int D, int NG, int BIAS, bool CAUSAL, bool WINDOW>
@@ -98,7 +109,7 @@ pa_prefill_f32(PrefillArgs a) {
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform
   const int c = lane & 15;
   const int g = lane >> 4;
 
@@ -183,8 +194,12 @@ pa_prefill_f32(PrefillArgs a) {
       tb[i] = blk < nblk_seq ? table[blk] : 0;
     }
   };
-  // global -> registers: one tile of K and V (zeros for keys >= L). The
-  // block base is uniform; only the sequence's last tile needs the key check.
+  // global -> registers: one tile of K and V. One load instruction covers
+  // whole rows of one cache block, so its address is a uniform block base
+  // plus a per-lane offset that is the same for every tile. Rows at or past
+  // L are read from the sequence's last block, or from block 0 for a block
+  // past it (both in the pool): K there only feeds scores the mask drops,
+  // and V is zeroed so that a zero weight never meets a NaN.
   float4_t kst[kLoads], vst[kLoads];
   auto fetch = [&](int tk) {
     const int base = kstart + tk * kKTile;
@@ -195,14 +210,10 @@ pa_prefill_f32(PrefillArgs a) {
       const int col = (tid % (D / 4)) * 4;
       const int64_t blk_off = ((int64_t)tb[(i * kRowsPerLoad) / kBlockSize] * H + h) *
                               (kBlockSize * D);
-      const int in_blk = ((base + r) % kBlockSize) * D + col;
-      if (!tail || base + r < L) {
-        kst[i] = *reinterpret_cast<const float4_t*>(kc + blk_off + in_blk);
-        vst[i] = *reinterpret_cast<const float4_t*>(vc + blk_off + in_blk);
-      } else {
-        kst[i] = float4_t{0, 0, 0, 0};
-        vst[i] = float4_t{0, 0, 0, 0};
-      }
+      const uint32_t in_blk = (uint32_t)((r % kBlockSize) * D + col);
+      kst[i] = *reinterpret_cast<const float4_t*>(kc + blk_off + in_blk);
+      vst[i] = *reinterpret_cast<const float4_t*>(vc + blk_off + in_blk);
+      if (tail && base + r >= L) vst[i] = float4_t{0, 0, 0, 0};
     }
   };
   auto stash = [&](int buf) {
@@ -223,11 +234,12 @@ pa_prefill_f32(PrefillArgs a) {
   // Online softmax with a lazily moved reference: weights are 2^(s - m_ref);
   // m_ref only moves (rescaling acc and l) when a row's max exceeds it by
   // more than 2^8, so weights stay <= 256 and the rescale is rare.
-  float m_ref[NG], l_run[NG];
+  float m_ref[NG], neg_m[NG], l_run[NG];   // neg_m = -m_ref once m_ref is finite
   const float* bias_row[NG];
 #pragma unroll
   for (int q = 0; q < NG; ++q) {
     m_ref[q] = -INFINITY;
+    neg_m[q] = 0.0f;
     l_run[q] = 0.0f;
     // rows past n_q point at the tile's first row and are masked, so every
     // bias read is in bounds
@@ -254,30 +266,59 @@ pa_prefill_f32(PrefillArgs a) {
   }
   __syncthreads();
 
-  for (int tk = 0; tk < ntiles; ++tk) {
-    const int buf = tk & 1;
+  // one key tile; the LDS buffer is a compile-time constant so that every
+  // LDS address is a per-lane base plus an immediate
+  auto tile_step = [&](int tk, auto buf_c) {
+    constexpr int buf = decltype(buf_c)::value;
     const int base = kstart + tk * kKTile;
     if (wave_active && base < wv_hi && base + kKTile > wv_lo) {
       const float* k_lds = kv_lds[buf][0];
       const float* v_lds = kv_lds[buf][1];
 
+      // 16-key chunks that no row of the wave can see (window edges, causal
+      // diagonal) skip both products: bit ch of `live` (uniform)
+      int live = (1 << kChunks) - 1;
+      if constexpr ((WINDOW || CAUSAL) && kChunks == 2) {
+        live = 0;
+#pragma unroll
+        for (int ch = 0; ch < kChunks; ++ch) {
+          const int c0 = base + ch * 16;
+          live |= (c0 < wv_hi && c0 + 16 > wv_lo) ? 1 << ch : 0;
+        }
+      }
       // ---- S^T = K Q^T (base-2 scores); each K operand feeds every group ----
       float4_t s[NG][kChunks];
 #pragma unroll
       for (int q = 0; q < NG; ++q)
 #pragma unroll
         for (int ch = 0; ch < kChunks; ++ch) s[q][ch] = float4_t{0, 0, 0, 0};
+      auto qk = [&](auto live_c) {
+        constexpr int lv = decltype(live_c)::value;
 #pragma unroll
-      for (int i = 0; i < kDQ; i += 4) {
+        for (int i = 0; i < kDQ; i += 4) {
 #pragma unroll
-        for (int ch = 0; ch < kChunks; ++ch) {
-          const float4_t kv =
-              *reinterpret_cast<const float4_t*>(&k_lds[(ch * 16 + c) * kRow + kDQ * g + i]);
+          for (int ch = 0; ch < kChunks; ++ch) {
+            if (((lv >> ch) & 1) != 0) {   // folded once the loop is unrolled
+              const float4_t kv = *reinterpret_cast<const float4_t*>(
+                  &k_lds[(ch * 16 + c) * kRow + kDQ * g + i]);
 #pragma unroll
-          for (int e = 0; e < 4; ++e)
+              for (int e = 0; e < 4; ++e)
 #pragma unroll
-            for (int q = 0; q < NG; ++q) s[q][ch] = mfma16x16x4(kv[e], qreg[q][i + e], s[q][ch]);
+                for (int q = 0; q < NG; ++q)
+                  s[q][ch] = mfma16x16x4(kv[e], qreg[q][i + e], s[q][ch]);
+            }
+          }
         }
+      };
+      if constexpr (kChunks == 2) {
+        if (live == 3)
+          qk(IntC<3>{});
+        else if (live == 1)
+          qk(IntC<1>{});
+        else
+          qk(IntC<2>{});
+      } else {
+        qk(IntC<(1 << kChunks) - 1>{});
       }
 
 #pragma unroll
@@ -286,6 +327,10 @@ pa_prefill_f32(PrefillArgs a) {
         for (int ch = 0; ch < kChunks; ++ch) {
           const int c0 = base + ch * 16;
           const int j0 = c0 + 4 * g;
+          if (!((live >> ch) & 1)) {
+            s[q][ch] = float4_t{-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+            continue;
+          }
           // bias (added as a * scale * log2(e): the same sum as (q.k + a) * scale)
           if constexpr (BIAS == 1) {
 #pragma unroll
@@ -316,17 +361,17 @@ pa_prefill_f32(PrefillArgs a) {
         }
 
         // ---- row max over the tile: 4 values per chunk, then lanes c + 16 g ----
-        float mt = -INFINITY;
+        float mt = vmax(vmax(s[q][0][0], s[q][0][1]), vmax(s[q][0][2], s[q][0][3]));
 #pragma unroll
-        for (int ch = 0; ch < kChunks; ++ch)
-          mt = fmaxf(fmaxf(mt, fmaxf(s[q][ch][0], s[q][ch][1])), fmaxf(s[q][ch][2], s[q][ch][3]));
+        for (int ch = 1; ch < kChunks; ++ch)
+          mt = vmax(mt, vmax(vmax(s[q][ch][0], s[q][ch][1]), vmax(s[q][ch][2], s[q][ch][3])));
         {
           const auto x16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(mt),
                                                             __float_as_uint(mt), false, false);
-          mt = fmaxf(__uint_as_float(x16[0]), __uint_as_float(x16[1]));
+          mt = vmax(__uint_as_float(x16[0]), __uint_as_float(x16[1]));
           const auto x32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(mt),
                                                             __float_as_uint(mt), false, false);
-          mt = fmaxf(__uint_as_float(x32[0]), __uint_as_float(x32[1]));
+          mt = vmax(__uint_as_float(x32[0]), __uint_as_float(x32[1]));
         }
         const bool move = mt > m_ref[q] + 8.0f;        // false while mt = -inf
         if (__builtin_amdgcn_ballot_w64(move) != 0) {
@@ -335,16 +380,16 @@ pa_prefill_f32(PrefillArgs a) {
           // gives alpha = 0 on an empty accumulator
           const float alpha = move ? __builtin_amdgcn_exp2f(m_ref[q] - mt) : 1.0f;
           m_ref[q] = move ? mt : m_ref[q];
+          neg_m[q] = move ? -mt : neg_m[q];
           l_run[q] *= alpha;
 #pragma unroll
           for (int dt = 0; dt < kNDT; ++dt) acc[q][dt] *= alpha;
         }
-        const float m_use = (m_ref[q] == -INFINITY) ? 0.0f : m_ref[q];
 #pragma unroll
         for (int ch = 0; ch < kChunks; ++ch) {
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
-            const float pr = __builtin_amdgcn_exp2f(s[q][ch][r] - m_use);
+            const float pr = __builtin_amdgcn_exp2f(s[q][ch][r] + neg_m[q]);
             s[q][ch][r] = pr;
             l_run[q] += pr;
           }
@@ -354,6 +399,7 @@ pa_prefill_f32(PrefillArgs a) {
       // ---- O^T += V^T P^T; each V operand feeds every group ----
 #pragma unroll
       for (int ch = 0; ch < kChunks; ++ch) {
+        if (!((live >> ch) & 1)) continue;      // all its weights are 0
 #pragma unroll
         for (int kk = 0; kk < 4; ++kk) {
           const float* vrow = &v_lds[(ch * 16 + 4 * g + kk) * kRow + kNDT * c];
@@ -378,6 +424,10 @@ pa_prefill_f32(PrefillArgs a) {
       if (tk + 3 < ntiles) load_table(tk + 3);
     }
     __syncthreads();
+  };
+  for (int tk = 0; tk < ntiles; tk += 2) {
+    tile_step(tk, IntC<0>{});
+    if (tk + 1 < ntiles) tile_step(tk + 1, IntC<1>{});
   }
 
   // ---- epilogue: out = O / l ----

@@ -300,21 +300,43 @@ pa_prefill_bf16(PrefillArgs a) {
     asm("" : "+v"(ones));   // keep the all-ones operand resident, not rebuilt per tile
     const int base = kstart + tk * kKT;
     if (wave_active && base < wv_hi && base + kKT > wv_lo) {
+      // 16-key chunks that no row of the wave can see (window edges, causal
+      // diagonal) skip their S^T products: bit ch of `live` (uniform)
+      int live = 3;
+      if constexpr (WINDOW || CAUSAL) {
+        live = 0;
+#pragma unroll
+        for (int ch = 0; ch < 2; ++ch) {
+          const int c0 = base + ch * 16;
+          live |= (c0 < wv_hi && c0 + 16 > wv_lo) ? 1 << ch : 0;
+        }
+      }
       // ---- S^T for the two 16-key chunks of every sub-tile ----
       float4_t s[kSub][2];
 #pragma unroll
       for (int sb = 0; sb < kSub; ++sb) s[sb][0] = s[sb][1] = float4_t{0, 0, 0, 0};
+      auto qk = [&](auto live_c) {
+        constexpr int lv = decltype(live_c)::value;
 #pragma unroll
-      for (int st = 0; st < kSteps; ++st) {
+        for (int st = 0; st < kSteps; ++st) {
 #pragma unroll
-        for (int ch = 0; ch < 2; ++ch) {
-          const uint4 kv = *reinterpret_cast<const uint4*>(
-              &k_lds[buf][(ch * 16 + c) * kKRow + (D / 4) * g + 8 * st]);
+          for (int ch = 0; ch < 2; ++ch) {
+            if (((lv >> ch) & 1) != 0) {   // folded once the loop is unrolled
+              const uint4 kv = *reinterpret_cast<const uint4*>(
+                  &k_lds[buf][(ch * 16 + c) * kKRow + (D / 4) * g + 8 * st]);
 #pragma unroll
-          for (int sb = 0; sb < kSub; ++sb)
-            s[sb][ch] = mfma_bf16(__builtin_bit_cast(bf16x8_t, kv), qv[sb][st], s[sb][ch]);
+              for (int sb = 0; sb < kSub; ++sb)
+                s[sb][ch] = mfma_bf16(__builtin_bit_cast(bf16x8_t, kv), qv[sb][st], s[sb][ch]);
+            }
+          }
         }
-      }
+      };
+      if (live == 3)
+        qk(IntC<3>{});
+      else if (live == 1)
+        qk(IntC<1>{});
+      else
+        qk(IntC<2>{});
       // V^T operands of this tile (read early, while the softmax runs, when
       // PA_PREFILL_BF16_VEARLY is set)
       uint4 vv[kNDT];
@@ -336,6 +358,10 @@ pa_prefill_bf16(PrefillArgs a) {
         for (int ch = 0; ch < 2; ++ch) {
           const int c0 = base + ch * 16;
           const int j0 = c0 + 4 * g;
+          if (!((live >> ch) & 1)) {
+            s[sb][ch] = float4_t{-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+            continue;
+          }
           if constexpr (BIAS == 1) {
 #pragma unroll
             for (int r = 0; r < 4; ++r)
