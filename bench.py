@@ -132,24 +132,33 @@ def cpu_baseline_decode(case, out_gpu):
     oracle.build(force=False)
     rng = np.random.default_rng(12345)
 
-    def run(n):
+    target_s = 15.0
+
+    def run(n, min_s=0.0):
+        """Oracle on n sequences, repeated (same inputs) until min_s seconds."""
         seqs = np.sort(rng.choice(case.num_seqs, size=n, replace=False))
         s = compact_sample(case, seqs)
-        t0 = time.perf_counter()
-        ref = oracle.decode(s["q"], s["k"], s["v"], s["bt"], s["cl"], s["bias"],
-                            case.sliding_window, case.scale, case.max_seq_len)
-        dt = time.perf_counter() - t0
+        reps, t0 = 0, time.perf_counter()
+        while True:
+            ref = oracle.decode(s["q"], s["k"], s["v"], s["bt"], s["cl"], s["bias"],
+                                case.sliding_window, case.scale, case.max_seq_len)
+            reps += 1
+            dt = time.perf_counter() - t0
+            if dt >= min_s or reps >= 100:
+                break
         g = out_gpu[torch.as_tensor(seqs, device=out_gpu.device)].float().cpu().double().numpy()
-        return n, dt, float(np.max(np.abs(g - ref))), seqs
+        return n, reps, dt, float(np.max(np.abs(g - ref)))
 
-    n, dt, _, _ = run(4)                                  # rate estimate
-    target_s = 15.0
+    n, _, dt, _ = run(4)                                  # rate estimate
     n = int(min(case.num_seqs, max(4, math.floor(target_s / max(dt / n, 1e-6)))))
-    n, dt, err, seqs = run(n)
-    return {"value": n / dt, "unit": "tokens/s", "cores": oracle.num_threads(),
+    # the whole workload can take well under the target: repeat it, so the
+    # rate comes from ~10 s of CPU work
+    n, reps, dt, err = run(n, min_s=10.0 if n == case.num_seqs else 0.0)
+    return {"value": n * reps / dt, "unit": "tokens/s", "cores": oracle.num_threads(),
             "kind": "oracle",
             "sample": "%d of the %d sequences (all 32 heads, their full contexts), "
-                      "float64 C loop over the block table, %.1f s" % (n, case.num_seqs, dt),
+                      "float64 C loop over the block table, %d pass(es) in %.1f s"
+                      % (n, case.num_seqs, reps, dt),
             "gpu_vs_oracle_max_abs_err_on_sample": err}
 
 
