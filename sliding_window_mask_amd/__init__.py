@@ -56,6 +56,53 @@ def _ptr(t):
     return None if t is None else ctypes.c_void_p(t.data_ptr())
 
 
+def _tensor(t, name, device, dtypes=None, shape=None, ndim=None):
+    """Check one tensor argument before its pointer crosses the ABI: a device
+    (HIP) tensor on `device`, contiguous, of one of `dtypes`, with `shape`
+    (None entries unchecked) or `ndim` dimensions. The kernels read raw
+    pointers with the documented row-major layout, so a host tensor or a
+    strided view would be read as garbage (or fault); it is rejected here."""
+    if not isinstance(t, torch.Tensor):
+        raise TypeError("%s must be a torch.Tensor, got %s" % (name, type(t).__name__))
+    if t.device.type != "cuda" or (device is not None and t.device != device):
+        raise ValueError("%s must be a tensor on %s, got %s" % (name, device or "the GPU",
+                                                               t.device))
+    if dtypes is not None and t.dtype not in dtypes:
+        raise TypeError("%s must be %s, got %s" % (name, " or ".join(map(str, dtypes)),
+                                                   t.dtype))
+    if shape is not None:
+        ok = t.dim() == len(shape) and all(w is None or t.shape[i] == w
+                                           for i, w in enumerate(shape))
+        if not ok:
+            raise ValueError("%s must have shape %s, got %s"
+                             % (name, tuple("*" if w is None else w for w in shape),
+                                tuple(t.shape)))
+    elif ndim is not None and t.dim() != ndim:
+        raise ValueError("%s must have %d dimensions, got %d" % (name, ndim, t.dim()))
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+
+
+_FLOAT_DTYPES = (torch.float32, torch.bfloat16)
+
+
+def _check_attention_args(q, k_cache, v_cache, block_tables, context_lens, out,
+                          query_start_loc=None, num_seqs=None):
+    """Common checks of decode/prefill tensors; returns q's device."""
+    _tensor(q, "q", None, _FLOAT_DTYPES, ndim=3)
+    dev = q.device
+    _, H, D = q.shape
+    _tensor(k_cache, "k_cache", dev, (q.dtype,), shape=(None, None, None, D))
+    _tensor(v_cache, "v_cache", dev, (q.dtype,), shape=tuple(k_cache.shape))
+    B = num_seqs if num_seqs is not None else q.shape[0]
+    _tensor(block_tables, "block_tables", dev, (torch.int32,), shape=(B, None))
+    _tensor(context_lens, "context_lens", dev, (torch.int32,), shape=(B,))
+    if query_start_loc is not None:
+        _tensor(query_start_loc, "query_start_loc", dev, (torch.int32,), shape=(B + 1,))
+    _tensor(out, "out", dev, (q.dtype,), shape=tuple(q.shape))
+    return dev
+
+
 def _stream(stream):
     if stream is None:
         return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
@@ -168,11 +215,17 @@ class PagedAttnLib:
         k_cache, v_cache [num_blocks,H,16,D]; block_tables int32 [B,max_blocks];
         context_lens int32 [B]; attn_bias fp32 [B,H,max_seq_len] or None.
         Cross-attention: pass the encoder table and lengths, sliding_window -1."""
+        _tensor(q, "q", None, _FLOAT_DTYPES, ndim=3)
         B, H, D = q.shape
         if out is None:
             out = torch.empty_like(q)
+        dev = _check_attention_args(q, k_cache, v_cache, block_tables, context_lens, out)
+        if attn_bias is not None:
+            _tensor(attn_bias, "attn_bias", dev, (torch.float32,), shape=(B, H, max_seq_len))
         if workspace is None:
             workspace = self.workspace_for(q, max_seq_len, sliding_window, partition_tokens)
+        else:
+            _tensor(workspace, "workspace", dev, ndim=1)
         ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
         self._check(self._lib.paged_attn_decode(
             _ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables),
@@ -189,9 +242,16 @@ class PagedAttnLib:
 
         query_start_loc int32 [B+1]; attn_bias fp32 [B,H,max_seq_len,max_seq_len]
         or None; causal False for encoder-only bidirectional attention."""
+        _tensor(q, "q", None, _FLOAT_DTYPES, ndim=3)
         TQ, H, D = q.shape
         if out is None:
             out = torch.empty_like(q)
+        B = context_lens.shape[0] if isinstance(context_lens, torch.Tensor) else 0
+        dev = _check_attention_args(q, k_cache, v_cache, block_tables, context_lens, out,
+                                    query_start_loc, B)
+        if attn_bias is not None:
+            _tensor(attn_bias, "attn_bias", dev, (torch.float32,),
+                    shape=(B, H, max_seq_len, max_seq_len))
         self._check(self._lib.paged_attn_prefill(
             _ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables),
             _ptr(context_lens), _ptr(query_start_loc), _ptr(attn_bias), int(sliding_window),
@@ -206,11 +266,16 @@ class PagedAttnLib:
                                  workspace=None, partition_tokens=0, stream=None):
         """Decode with the T5 relative-position bias computed in the kernel from
         rel_table [H, num_buckets] (fp32); see include/paged_attn.h."""
+        _tensor(q, "q", None, _FLOAT_DTYPES, ndim=3)
         B, H, D = q.shape
         if out is None:
             out = torch.empty_like(q)
+        dev = _check_attention_args(q, k_cache, v_cache, block_tables, context_lens, out)
+        _tensor(rel_table, "rel_table", dev, (torch.float32,), shape=(H, num_buckets))
         if workspace is None:
             workspace = self.workspace_for(q, max_seq_len, sliding_window, partition_tokens)
+        else:
+            _tensor(workspace, "workspace", dev, ndim=1)
         ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
         self._check(self._lib.paged_attn_decode_relpos(
             _ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables),
@@ -225,9 +290,14 @@ class PagedAttnLib:
                                   bidirectional, sliding_window, causal, scale, *, max_seq_len,
                                   out=None, stream=None):
         """Prefill with the T5 relative-position bias computed in the kernel."""
+        _tensor(q, "q", None, _FLOAT_DTYPES, ndim=3)
         TQ, H, D = q.shape
         if out is None:
             out = torch.empty_like(q)
+        B = context_lens.shape[0] if isinstance(context_lens, torch.Tensor) else 0
+        dev = _check_attention_args(q, k_cache, v_cache, block_tables, context_lens, out,
+                                    query_start_loc, B)
+        _tensor(rel_table, "rel_table", dev, (torch.float32,), shape=(H, num_buckets))
         self._check(self._lib.paged_attn_prefill_relpos(
             _ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables),
             _ptr(context_lens), _ptr(query_start_loc), _ptr(rel_table), int(num_buckets),
@@ -243,11 +313,17 @@ class PagedAttnLib:
                                       partition_tokens=0, stream=None):
         """Decode with a packed bias: sequence b's rows [H][L_b] start at
         attn_bias[bias_start[b]] (bias_start int64 [B])."""
+        _tensor(q, "q", None, _FLOAT_DTYPES, ndim=3)
         B, H, D = q.shape
         if out is None:
             out = torch.empty_like(q)
+        dev = _check_attention_args(q, k_cache, v_cache, block_tables, context_lens, out)
+        _tensor(attn_bias, "attn_bias", dev, (torch.float32,), ndim=1)
+        _tensor(bias_start, "bias_start", dev, (torch.int64,), shape=(B,))
         if workspace is None:
             workspace = self.workspace_for(q, max_seq_len, sliding_window, partition_tokens)
+        else:
+            _tensor(workspace, "workspace", dev, ndim=1)
         ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
         self._check(self._lib.paged_attn_decode_ragged_bias(
             _ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables),
@@ -262,9 +338,15 @@ class PagedAttnLib:
                                        causal, scale, *, max_seq_len, out=None, stream=None):
         """Prefill with a packed bias: sequence b's rows [H][n_q][L_b] start at
         attn_bias[bias_start[b]]."""
+        _tensor(q, "q", None, _FLOAT_DTYPES, ndim=3)
         TQ, H, D = q.shape
         if out is None:
             out = torch.empty_like(q)
+        B = context_lens.shape[0] if isinstance(context_lens, torch.Tensor) else 0
+        dev = _check_attention_args(q, k_cache, v_cache, block_tables, context_lens, out,
+                                    query_start_loc, B)
+        _tensor(attn_bias, "attn_bias", dev, (torch.float32,), ndim=1)
+        _tensor(bias_start, "bias_start", dev, (torch.int64,), shape=(B,))
         self._check(self._lib.paged_attn_prefill_ragged_bias(
             _ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables),
             _ptr(context_lens), _ptr(query_start_loc), _ptr(attn_bias), _ptr(bias_start),
@@ -276,7 +358,13 @@ class PagedAttnLib:
     def paged_kv_write(self, k_cache, v_cache, k_new, v_new, slot_mapping, *, stream=None):
         """Scatter k_new, v_new [T,H,D] into the paged caches at slot_mapping
         (int64 [T], block * 16 + offset; negative = skip)."""
+        _tensor(k_cache, "k_cache", None, _FLOAT_DTYPES, ndim=4)
+        dev = k_cache.device
+        _tensor(v_cache, "v_cache", dev, (k_cache.dtype,), shape=tuple(k_cache.shape))
+        _tensor(k_new, "k_new", dev, (k_cache.dtype,), shape=(None, None, k_cache.shape[3]))
         T, H, D = k_new.shape
+        _tensor(v_new, "v_new", dev, (k_cache.dtype,), shape=(T, H, D))
+        _tensor(slot_mapping, "slot_mapping", dev, (torch.int64,), shape=(T,))
         self._check(self._lib.paged_kv_write(
             _ptr(k_cache), _ptr(v_cache), _ptr(k_new), _ptr(v_new), _ptr(slot_mapping), T, H,
             k_cache.shape[1], D, k_cache.shape[2], k_cache.shape[0], _dtype_code(k_cache),

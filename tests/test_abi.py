@@ -257,3 +257,22 @@ def test_no_bias_build_rejects_a_bias():
     nob = pa.PagedAttnLib(pa.LIB_NOBIAS_PATH)
     st = call_decode(nob, decode_args(bias=FAKE))
     assert st == 3, nob.pa_last_error()
+
+
+def test_binding_rejects_host_tensors_before_any_call():
+    # CPU tensors would reach the kernels as host pointers: the binding
+    # refuses them (and non-tensors) before the library is called
+    lib = pa.lib()
+    q = torch.zeros(2, 4, 64)
+    cache = torch.zeros(8, 4, 16, 64)
+    bt = torch.zeros(2, 4, dtype=torch.int32)
+    cl = torch.ones(2, dtype=torch.int32)
+    with pytest.raises(ValueError, match="q must be a tensor on"):
+        lib.paged_attn_decode(q, cache, cache, bt, cl, None, -1, 0.125, max_seq_len=64)
+    with pytest.raises(ValueError, match="q must be a tensor on"):
+        lib.paged_attn_prefill(q, cache, cache, bt, cl, torch.tensor([0, 1, 2], dtype=torch.int32),
+                               None, -1, False, 0.125, max_seq_len=64)
+    with pytest.raises(TypeError, match="q must be a torch.Tensor"):
+        lib.paged_attn_decode([0.0], cache, cache, bt, cl, None, -1, 0.125, max_seq_len=64)
+    with pytest.raises(ValueError, match="k_cache must be a tensor on"):
+        lib.paged_kv_write(cache, cache, q, q, torch.zeros(2, dtype=torch.int64))
