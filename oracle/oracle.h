@@ -29,6 +29,12 @@
  *     (n_q = L for an encoder, so query t is at position t);
  *   - an empty row (L = 0) or a row whose every score is -inf gives 0;
  *   - a null bias pointer means A = 0 exactly.
+ * Parity unpinned for the readings themselves: no page prints an example that
+ * tells bias-before-scale from bias-after-scale, the query position, or the
+ * window's edge (|p - j| < W against <= W), nor the T5 bucket boundaries
+ * between the exact range and the maximum distance. The tests pin that this
+ * code computes what the readings say (library cross-checks, closed forms,
+ * special cases), not the readings.
  *
  * Layouts (row-major, element type chosen by `dtype`: 0 = fp32, 1 = bf16 given
  * as raw 16-bit patterns):
