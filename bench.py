@@ -6,6 +6,12 @@ block permutation). One step = one paged_attn_decode call = one decode step of
 one attention layer for all 256 sequences; throughput is decode tokens/s
 (sequences served per second) and the achieved HBM bandwidth of the call.
 
+Timing: W untimed warm-up steps, further untimed steps until 0.3 s of warm-up
+have passed (the GPU's clocks ramp over the first ~0.1 s of load), then exactly
+K steps between two HIP events on the stream the library launches on, with a
+device synchronisation on both sides. The CPU baseline times the float64
+oracle on the same workload (repeated to ~10 s of CPU work).
+
 Prints ONE JSON line. Options:
   --gpus N        only 1 is supported (the path runs on one GPU)
   --steps K       timed steps (default 20)
