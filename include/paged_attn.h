@@ -148,6 +148,10 @@ pa_status_t paged_attn_decode(void* out, const void* q, const void* k_cache,
  *   dtype           PA_DTYPE_F32 or PA_DTYPE_BF16 (bf16: bf16 MFMA with fp32
  *                   accumulation; the softmax weights enter P.V as bf16)
  *   Other arguments as for paged_attn_decode. No workspace is needed.
+ *   total_q = 0 computes nothing and returns PA_OK after the scalar checks;
+ *   then no device pointer is read and any of them may be NULL (the same
+ *   holds for the ragged-bias variant below; the relpos variant still checks
+ *   its bucket table).
  * Errors: NULL_POINTER, INVALID_ARG, UNSUPPORTED, MISALIGNED, HIP.
  */
 pa_status_t paged_attn_prefill(void* out, const void* q, const void* k_cache,
@@ -220,7 +224,8 @@ pa_status_t paged_attn_prefill_relpos(void* out, const void* q, const void* k_ca
  *   prefill  rows [num_heads][n_q][L_b]:  a(b,h,t,j) = attn_bias[bias_start[b] + (h*n_q + t)*L_b + j]
  * (t = query index within the sequence, j = key position). attn_bias and
  * bias_start (int64 [num_seqs], 8-byte aligned) are device memory and must
- * not be NULL. Everything else as for paged_attn_decode / paged_attn_prefill.
+ * not be NULL (except for a prefill with total_q = 0). Everything else as for
+ * paged_attn_decode / paged_attn_prefill.
  */
 pa_status_t paged_attn_decode_ragged_bias(void* out, const void* q, const void* k_cache,
                                           const void* v_cache, const int32_t* block_tables,

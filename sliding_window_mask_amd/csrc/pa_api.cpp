@@ -366,15 +366,19 @@ pa_status_t prefill_impl(void* out, const void* q, const void* k_cache, const vo
                          int32_t head_dim, int32_t block_size, int32_t max_blocks_per_seq,
                          int32_t max_seq_len, int64_t num_blocks, int64_t total_q,
                          pa_dtype_t dtype, void* stream) {
-  pa_status_t st = check_common(out, q, k_cache, v_cache, block_tables, context_lens, attn_bias,
-                                sliding_window, scale, num_seqs, num_heads, num_kv_heads,
-                                head_dim, block_size, max_blocks_per_seq, max_seq_len,
-                                num_blocks, dtype);
-  if (st != PA_OK) return st;
-  if (causal != 0 && causal != 1) return fail(PA_ERR_INVALID_ARG, "causal must be 0 or 1");
+  if (num_seqs < 0 || num_seqs > 65535)
+    return fail(PA_ERR_INVALID_ARG, "num_seqs %d out of range [0, 65535]", num_seqs);
   if (total_q < 0 || total_q > INT32_MAX)
     return fail(PA_ERR_INVALID_ARG, "total_q %lld out of range", (long long)total_q);
-  if (num_seqs == 0) return ok();
+  // no queries: scalars are still checked, but no pointer is needed (an empty
+  // tensor's data pointer may be NULL)
+  pa_status_t st = check_common(out, q, k_cache, v_cache, block_tables, context_lens, attn_bias,
+                                sliding_window, scale, total_q == 0 ? 0 : num_seqs, num_heads,
+                                num_kv_heads, head_dim, block_size, max_blocks_per_seq,
+                                max_seq_len, num_blocks, dtype);
+  if (st != PA_OK) return st;
+  if (causal != 0 && causal != 1) return fail(PA_ERR_INVALID_ARG, "causal must be 0 or 1");
+  if (num_seqs == 0 || total_q == 0) return ok();
   if (!query_start_loc) return fail(PA_ERR_NULL_POINTER, "query_start_loc is NULL");
   if (!aligned(query_start_loc, 4))
     return fail(PA_ERR_MISALIGNED, "query_start_loc must be 4-byte aligned");
@@ -518,7 +522,7 @@ pa_status_t paged_attn_prefill_ragged_bias(void* out, const void* q, const void*
                                            int32_t block_size, int32_t max_blocks_per_seq,
                                            int32_t max_seq_len, int64_t num_blocks,
                                            int64_t total_q, pa_dtype_t dtype, void* stream) {
-  if (num_seqs > 0 && (!attn_bias || !bias_start))
+  if (num_seqs > 0 && total_q > 0 && (!attn_bias || !bias_start))
     return fail(PA_ERR_NULL_POINTER, "attn_bias and bias_start are required");
   if (bias_start && !aligned(bias_start, 8))
     return fail(PA_ERR_MISALIGNED, "bias_start must be 8-byte aligned");

@@ -139,6 +139,22 @@ def test_prefill_rejects_on_host(kw, status):
     assert st == status, (st, lib.pa_last_error())
 
 
+def test_prefill_without_queries_needs_no_pointers():
+    # an empty packed query tensor may have a NULL data pointer; nothing is
+    # computed, but the scalar arguments are still checked
+    lib = pa.lib()
+    none = dict(out=None, q=None, k=None, v=None, bt=None, cl=None, qsl=None)
+    assert prefill_call(lib, tq=0, **none) == 0, lib.pa_last_error()
+    assert prefill_call(lib, tq=0, D=80, **none) == 3
+    assert prefill_call(lib, tq=0, causal=2, **none) == 2
+    assert prefill_call(lib, tq=0, window=0, **none) == 2
+    assert prefill_call(lib, tq=1, **dict(none, k=FAKE, v=FAKE, bt=FAKE, cl=FAKE)) == 1
+    st = lib._lib.paged_attn_prefill_ragged_bias(None, None, None, None, None, None, None, None,
+                                                 None, -1, 0, 0.125, 2, 4, 4, 64, 16, 8, 128,
+                                                 64, 0, 0, None)
+    assert st == 0, lib.pa_last_error()
+
+
 def test_check_metadata_host():
     lib = pa.lib()
     bt = torch.tensor([[3, 1, 0], [2, 3, 9]], dtype=torch.int32)

@@ -92,7 +92,7 @@ def _randn(shape, gen, device, dtype, chunk_rows=None):
     """fp32 standard normals rounded to `dtype`, drawn in chunks along dim 0."""
     out = torch.empty(shape, dtype=dtype, device=device)
     n = shape[0]
-    step = n if chunk_rows is None else max(1, chunk_rows)
+    step = max(1, n) if chunk_rows is None else max(1, chunk_rows)   # n = 0: empty
     for s in range(0, n, step):
         e = min(n, s + step)
         out[s:e] = torch.randn((e - s,) + tuple(shape[1:]), generator=gen, device=device,
