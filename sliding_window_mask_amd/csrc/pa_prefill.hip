@@ -204,8 +204,6 @@ pa_prefill_f32(PrefillArgs a) {
   // and V is zeroed so that a zero weight never meets a NaN.
   float4_t kst[kLoads], vst[kLoads];
   auto fetch = [&](int tk) {
-    const int base = kstart + tk * kKTile;
-    const bool tail = base + kKTile > L;
 #pragma unroll
     for (int i = 0; i < kLoads; ++i) {
       const int r = i * kRowsPerLoad + tid / (D / 4);
@@ -215,16 +213,31 @@ pa_prefill_f32(PrefillArgs a) {
       const uint32_t in_blk = (uint32_t)((r % kBlockSize) * D + col);
       kst[i] = *reinterpret_cast<const float4_t*>(kc + blk_off + in_blk);
       vst[i] = *reinterpret_cast<const float4_t*>(vc + blk_off + in_blk);
-      if (tail && base + r >= L) vst[i] = float4_t{0, 0, 0, 0};
     }
   };
-  auto stash = [&](int buf) {
+  // V rows at or past L are zeroed here, when the registers are stored, not
+  // in fetch: a select right after the loads would make every wave wait for
+  // them at once instead of a tile later
+  auto stash = [&](int buf, int tk) {
 #pragma unroll
     for (int i = 0; i < kLoads; ++i) {
       const int r = i * kRowsPerLoad + tid / (D / 4);
       const int col = (tid % (D / 4)) * 4;
       *reinterpret_cast<float4_t*>(&kv_lds[buf][0][r * kRow + col]) = kst[i];
       *reinterpret_cast<float4_t*>(&kv_lds[buf][1][r * kRow + col]) = vst[i];
+    }
+    const int base = kstart + tk * kKTile;
+    if (base + kKTile > L) {   // uniform: only a sequence's last tile
+      // the zero is made here, not hoisted into a register held across the loop
+      float z;
+      asm volatile("v_mov_b32 %0, 0" : "=v"(z));
+#pragma unroll
+      for (int i = 0; i < kLoads; ++i) {
+        const int r = i * kRowsPerLoad + tid / (D / 4);
+        const int col = (tid % (D / 4)) * 4;
+        if (base + r >= L)
+          *reinterpret_cast<float4_t*>(&kv_lds[buf][1][r * kRow + col]) = float4_t{z, z, z, z};
+      }
     }
   };
 
@@ -259,7 +272,7 @@ pa_prefill_f32(PrefillArgs a) {
   if (ntiles > 0) {
     load_table(0);
     fetch(0);
-    stash(0);
+    stash(0, 0);
     if (ntiles > 1) {
       load_table(1);
       fetch(1);
@@ -420,7 +433,7 @@ pa_prefill_f32(PrefillArgs a) {
       }
     }
     // refill: tile tk+1 (in registers) -> the other buffer, tile tk+2 -> registers
-    if (tk + 1 < ntiles) stash(buf ^ 1);
+    if (tk + 1 < ntiles) stash(buf ^ 1, tk + 1);
     if (tk + 2 < ntiles) {
       fetch(tk + 2);
       if (tk + 3 < ntiles) load_table(tk + 3);
