@@ -102,6 +102,21 @@ def time_steps(fn, steps, warmup):
     return start.elapsed_time(end) / steps          # ms per step
 
 
+def per_call_ms(fn, n):
+    """Distribution of single-call times (each call between its own pair of
+    events, after the timed region): median, p10, p90."""
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(n)]
+    for s, e in ev:
+        s.record()
+        fn()
+        e.record()
+    torch.cuda.synchronize()
+    t = np.array([s.elapsed_time(e) for s, e in ev])
+    return {"calls": n, "median": float(np.median(t)), "p10": float(np.percentile(t, 10)),
+            "p90": float(np.percentile(t, 90))}
+
+
 # ----------------------------------------------------------------------------
 # decode
 # ----------------------------------------------------------------------------
@@ -160,11 +175,22 @@ def cpu_baseline_decode(case, out_gpu):
     # the whole workload can take well under the target: repeat it, so the
     # rate comes from ~10 s of CPU work
     n, reps, dt, err = run(n, min_s=10.0 if n == case.num_seqs else 0.0)
-    return {"value": n * reps / dt, "unit": "tokens/s", "cores": oracle.num_threads(),
+    threads = oracle.num_threads()
+    # the same oracle on one thread, on a smaller sample (~5 s)
+    n1 = max(1, min(case.num_seqs, int(5.0 * n * reps / dt / max(threads, 1))))
+    oracle.set_num_threads(1)
+    try:
+        n1, reps1, dt1, _ = run(n1)
+    finally:
+        oracle.set_num_threads(threads)
+    return {"value": n * reps / dt, "unit": "tokens/s", "cores": threads,
             "kind": "oracle",
             "sample": "%d of the %d sequences (all 32 heads, their full contexts), "
                       "float64 C loop over the block table, %d pass(es) in %.1f s"
                       % (n, case.num_seqs, reps, dt),
+            "single_thread": {"value": n1 * reps1 / dt1, "unit": "tokens/s", "cores": 1,
+                              "sample": "%d sequences, %d pass(es) in %.1f s"
+                                        % (n1, reps1, dt1)},
             "gpu_vs_oracle_max_abs_err_on_sample": err}
 
 
@@ -209,6 +235,7 @@ def bench_decode(args):
                      "kernel": "paged_attn_decode call: pa_decode_partition" +
                                ("" if ws is None else " + pa_decode_merge")},
     }
+    line["per_call_ms"] = per_call_ms(step, max(args.steps, 20))
     if not args.no_variants:
         var = {}
         msw = time_steps(lambda: step(window=1024), args.steps, args.warmup)

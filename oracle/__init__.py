@@ -73,12 +73,20 @@ def _load():
         lib.oracle_kv_write.argtypes = [P, P, P, P, P, ctypes.c_int64, I32, I32, I32,
                                         ctypes.c_int64, I32]
         lib.oracle_num_threads.restype = ctypes.c_int
+        lib.oracle_set_num_threads.restype = None
+        lib.oracle_set_num_threads.argtypes = [ctypes.c_int]
         _lib = lib
     return _lib
 
 
 def num_threads() -> int:
     return int(_load().oracle_num_threads())
+
+
+def set_num_threads(n: int) -> None:
+    """Threads for the following oracle calls (timing only; every row is
+    computed the same way whatever the count)."""
+    _load().oracle_set_num_threads(int(n))
 
 
 def _host(a, dtype=None):

@@ -123,6 +123,8 @@ int oracle_kv_write(void* k_cache, void* v_cache, const void* k_new, const void*
 
 /* Number of OpenMP threads the oracle uses (for reporting). */
 int oracle_num_threads(void);
+/* Threads the following calls use (n >= 1; timing only, results do not depend on it). */
+void oracle_set_num_threads(int n);
 
 #ifdef __cplusplus
 }

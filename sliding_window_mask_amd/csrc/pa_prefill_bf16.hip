@@ -33,10 +33,16 @@
 // * O^T = V^T P^T over the tile's 32 keys: element e of lane group g is key
 //   4g + e (e < 4, first chunk) or 16 + 4g + e - 4 (second chunk), so the
 //   P operand is exactly the lane's own 8 softmax weights. The V operand
-//   needs 8 keys of one dim; V is therefore staged into LDS transposed,
-//   V^T[dim][key] (row stride 36 bf16: conflict-free 8-byte reads and
-//   writes), and lane l reads V^T[16 dt + c][4g .. 4g+3] and [16 + 4g ..].
-//   Lane l ends holding O^T[dim 16 dt + 4g + r][query c].
+//   needs 8 keys of one dim, a column of the row-major V tile: gfx950's
+//   transposing LDS read (ds_read_b64_tr_b16) provides it. Within each group
+//   of 16 lanes it treats the 16 8-byte pieces the lanes point at as a 16x4
+//   matrix M of 16-bit values and returns M[a][e], M[a+4][e], M[a+8][e],
+//   M[a+12][e] to lane 4a + e. Lane j of group g therefore points at key
+//   4g + j/4, dims 16 dt + 4 (j%4) .. +3, and receives keys 4g .. 4g+3 of dim
+//   16 dt + j; a second read 16 rows further gives keys 16 + 4g .. 16 + 4g + 3.
+//   V rows are padded to D + 16 bf16, so the 16 rows one read touches fall in
+//   distinct bank windows (the 2-cycle minimum for 512 bytes). Lane l ends
+//   holding O^T[dim 16 dt + 4g + r][query c].
 #include "pa_internal.h"
 
 namespace pa {
@@ -54,7 +60,7 @@ typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 
 constexpr int kQT = 64;         // queries per workgroup
 constexpr int kKT = 32;         // keys per tile (one 32-deep P.V contraction)
-constexpr int kVRow = kKT + 4;  // V^T row stride (bf16)
+typedef short i16x4_t __attribute__((ext_vector_type(4)));
 
 template <int D>
 struct Cfg {
@@ -90,8 +96,8 @@ pa_prefill_bf16(PrefillArgs a) {
   constexpr int kSteps = D / 32;               // 8-element steps per lane group
   constexpr int kNDT = D / 16;                 // 16-dim output slices
   constexpr int kKLoads = kKT * D / 8 / kThreads;        // 16-byte K loads per thread
-  constexpr int kVUnits = (D / 2) * (kKT / 4) / kThreads;  // (2 dims x 4 keys) units
-  static_assert(kKLoads >= 1 && kVUnits >= 1, "tile shape");
+  constexpr int kVRow = D + 16;                // V row stride in LDS (bf16)
+  static_assert(kKLoads >= 1, "tile shape");
   static_assert(D == 64 || D == 128, "head_dim");
 
   const int H = a.num_heads;
@@ -163,7 +169,7 @@ pa_prefill_bf16(PrefillArgs a) {
   }
 
   __shared__ uint16_t k_lds[2][kKT * kKRow];   // K tile, row-major [key][dim]
-  __shared__ uint16_t v_lds[2][D * kVRow];     // V tile, transposed [dim][key]
+  __shared__ uint16_t v_lds[2][kKT * kVRow];   // V tile, row-major [key][dim]
   __shared__ float rel_lds[BIAS == 2 ? 2 * kMaxRelDistance + 1 : 1];
   const int rel_md = BIAS == 2 ? a.rel.max_distance : 0;
   if constexpr (BIAS == 2) {
@@ -187,49 +193,42 @@ pa_prefill_bf16(PrefillArgs a) {
       tb[i] = blk < nblk_seq ? table[blk] : 0;
     }
   };
-  // global -> registers: K as 16-byte row pieces, V as 4-byte (2-dim) pieces
-  // of 4 consecutive keys, repacked below into V^T rows. A cache block holds
-  // 2D pieces of either kind, a multiple of 64, so each wave's pieces of one
-  // load lie in one block: the address is a uniform block base plus a
+  // global -> registers: K and V as 16-byte row pieces (8 dims of one key).
+  // A cache block holds 2D pieces, a multiple of 64, so each wave's pieces of
+  // one load lie in one block: the address is a uniform block base plus a
   // per-lane offset that is the same for every tile. Rows at or past L are
   // read from the sequence's last block, or from block 0 for a block past it
   // (both in the pool): K there only feeds scores the mask drops, and V is
   // zeroed so that a zero weight never meets a NaN.
   // (vectors rather than arrays, so that they stay in registers)
-  typedef uint32_t kst_t __attribute__((ext_vector_type(4 * kKLoads)));
-  typedef uint32_t vst_t __attribute__((ext_vector_type(4 * kVUnits)));
-  kst_t kst;
-  vst_t vst;
+  typedef uint32_t st_t __attribute__((ext_vector_type(4 * kKLoads)));
+  st_t kst, vst;
   auto fetch = [&](int tk) {
     const int base = kstart + tk * kKT;
-    const bool tail = base + kKT > L;
 #pragma unroll
     for (int i = 0; i < kKLoads; ++i) {
       const int e = i * kThreads + tid;        // 16-byte piece index in the tile
       const int r = e / (D / 8), col = (e % (D / 8)) * 8;
       const int sel = (i * kThreads + wave * 64) / (D / 8) / kBlockSize;
-      const uint16_t* blk = kc + ((int64_t)tb[sel] * H + h) * (kBlockSize * D);
-      const uint4 v = *reinterpret_cast<const uint4*>(blk + (uint32_t)((r % kBlockSize) * D + col));
-      kst[4 * i] = v.x;
-      kst[4 * i + 1] = v.y;
-      kst[4 * i + 2] = v.z;
-      kst[4 * i + 3] = v.w;
+      const int64_t blk = ((int64_t)tb[sel] * H + h) * (kBlockSize * D);
+      const uint32_t off = (uint32_t)((r % kBlockSize) * D + col);
+      const uint4 kv = *reinterpret_cast<const uint4*>(kc + blk + off);
+      const uint4 vv = *reinterpret_cast<const uint4*>(vc + blk + off);
+      kst[4 * i] = kv.x;
+      kst[4 * i + 1] = kv.y;
+      kst[4 * i + 2] = kv.z;
+      kst[4 * i + 3] = kv.w;
+      vst[4 * i] = vv.x;
+      vst[4 * i + 1] = vv.y;
+      vst[4 * i + 2] = vv.z;
+      vst[4 * i + 3] = vv.w;
     }
+    if (base + kKT > L) {   // uniform: only a sequence's last tile
 #pragma unroll
-    for (int u = 0; u < kVUnits; ++u) {
-      const int e = u * kThreads + tid;
-      const int dp = e % (D / 2), kg = e / (D / 2);   // dims 2dp, 2dp+1; keys 4kg..4kg+3
-      const int sel = (u * kThreads + wave * 64) / (D / 2) / (kBlockSize / 4);
-      const uint16_t* blk = vc + ((int64_t)tb[sel] * H + h) * (kBlockSize * D);
+      for (int i = 0; i < kKLoads; ++i) {
+        const int r = (i * kThreads + tid) / (D / 8);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int r = 4 * kg + i;
-        vst[4 * u + i] = *reinterpret_cast<const uint32_t*>(
-            blk + (uint32_t)((r % kBlockSize) * D + 2 * dp));
-      }
-      if (tail) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) vst[4 * u + i] = base + 4 * kg + i < L ? vst[4 * u + i] : 0u;
+        for (int w = 0; w < 4; ++w) vst[4 * i + w] = base + r < L ? vst[4 * i + w] : 0u;
       }
     }
   };
@@ -240,20 +239,8 @@ pa_prefill_bf16(PrefillArgs a) {
       const int r = e / (D / 8), col = (e % (D / 8)) * 8;
       *reinterpret_cast<uint4*>(&k_lds[buf][r * kKRow + col]) =
           make_uint4(kst[4 * i], kst[4 * i + 1], kst[4 * i + 2], kst[4 * i + 3]);
-    }
-#pragma unroll
-    for (int u = 0; u < kVUnits; ++u) {
-      const int e = u * kThreads + tid;
-      const int dp = e % (D / 2), kg = e / (D / 2);
-      // low halves = dim 2dp of keys 4kg..4kg+3, high halves = dim 2dp+1
-      const uint32_t x0 = vst[4 * u], x1 = vst[4 * u + 1], x2 = vst[4 * u + 2],
-                     x3 = vst[4 * u + 3];
-      const uint2 lo = make_uint2(__builtin_amdgcn_perm(x1, x0, 0x05040100u),
-                                  __builtin_amdgcn_perm(x3, x2, 0x05040100u));
-      const uint2 hi = make_uint2(__builtin_amdgcn_perm(x1, x0, 0x07060302u),
-                                  __builtin_amdgcn_perm(x3, x2, 0x07060302u));
-      *reinterpret_cast<uint2*>(&v_lds[buf][(2 * dp) * kVRow + 4 * kg]) = lo;
-      *reinterpret_cast<uint2*>(&v_lds[buf][(2 * dp + 1) * kVRow + 4 * kg]) = hi;
+      *reinterpret_cast<uint4*>(&v_lds[buf][r * kVRow + col]) =
+          make_uint4(vst[4 * i], vst[4 * i + 1], vst[4 * i + 2], vst[4 * i + 3]);
     }
   };
 
@@ -341,12 +328,18 @@ pa_prefill_bf16(PrefillArgs a) {
       // PA_PREFILL_BF16_VEARLY is set)
       uint4 vv[kNDT];
       auto read_v = [&]() {
+        // lane j of group g points at key 4g + j/4, dims 16dt + 4(j%4) .. +3;
+        // the transposing read hands lane j keys 4g .. 4g+3 of dim 16dt + j
+        // (and, 16 rows further, keys 16 + 4g .. 16 + 4g + 3)
+        typedef __attribute__((address_space(3))) i16x4_t lds_i16x4_t;
 #pragma unroll
         for (int dt = 0; dt < kNDT; ++dt) {
-          const uint16_t* vrow = &v_lds[buf][(16 * dt + c) * kVRow + 4 * g];
-          const uint2 v0 = *reinterpret_cast<const uint2*>(vrow);
-          const uint2 v1 = *reinterpret_cast<const uint2*>(vrow + 16);
-          vv[dt] = make_uint4(v0.x, v0.y, v1.x, v1.y);
+          const uint16_t* p = &v_lds[buf][(4 * g + (c >> 2)) * kVRow + 16 * dt + 4 * (c & 3)];
+          const uint2 lo = __builtin_bit_cast(
+              uint2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)p));
+          const uint2 hi = __builtin_bit_cast(
+              uint2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(p + 16 * kVRow)));
+          vv[dt] = make_uint4(lo.x, lo.y, hi.x, hi.y);
         }
       };
       if (PA_PREFILL_BF16_VEARLY) read_v();

@@ -538,3 +538,19 @@ def test_prefill_ragged_equals_padded_bit_exact(causal):
                                 case.context_lens, case.query_start_loc, packed, starts, 9,
                                 int(causal), case.scale, case.max_seq_len)
     np.testing.assert_array_equal(got, run_prefill(case))
+
+
+def test_thread_count_does_not_change_results():
+    # the CPU baseline times the oracle at its default thread count and on one
+    # thread; every row is computed the same way either way
+    case = small_decode(61, lens=(10, 90), B=16, max_seq_len=96)
+    ref = run_decode(case)
+    n = oracle.num_threads()
+    oracle.set_num_threads(1)
+    try:
+        assert oracle.num_threads() == 1
+        one = run_decode(case)
+    finally:
+        oracle.set_num_threads(n)
+    assert oracle.num_threads() == n
+    np.testing.assert_array_equal(one, ref)
