@@ -133,20 +133,26 @@ pa_prefill_f32(PrefillArgs a) {
     prefill_key_range(pos0 + w_first, pos0 + min(w_first + kWaveRows, nq) - 1, L, a.window, CAUSAL,
               wv_lo, wv_hi);
 
-  // per query group: first/last position, whether all 16 rows are valid,
-  // this lane's row
-  int gp0[NG], gp1[NG], t[NG], p[NG];
-  bool gfull[NG], row_ok[NG];
+  // per query group: first/last existing position, this lane's row. Masking
+  // of partly visible chunks: with d = p - j for key j = c0 + 4g + r,
+  // d = dq - c0 - r, and the key is visible iff dlo < d (j < L, causal
+  // j <= p, window p - j > -W) and, with a window, d < W.
+  int gp0[NG], gp1[NG], t[NG], p[NG], dq[NG], dlo[NG];
+  bool row_ok[NG];
 #pragma unroll
   for (int q = 0; q < NG; ++q) {
     const int first = w_first + 16 * q;
     const int last = min(first + 16, nq) - 1;
     gp0[q] = pos0 + first;
     gp1[q] = pos0 + last;
-    gfull[q] = last == first + 15;
     t[q] = first + c;
     row_ok[q] = t[q] < nq;
     p[q] = pos0 + t[q];
+    dq[q] = p[q] - 4 * g;
+    int lo = p[q] - L;
+    if constexpr (CAUSAL) lo = max(lo, -1);
+    if constexpr (WINDOW) lo = max(lo, -a.window);
+    dlo[q] = lo;
   }
 
   // Q operands: D/4 contiguous floats per lane, pre-multiplied by
@@ -357,19 +363,21 @@ pa_prefill_f32(PrefillArgs a) {
             for (int r = 0; r < 4; ++r)
               s[q][ch][r] = s[q][ch][r] + rel_lds[min(max(j0 + r - p[q], -rel_md), rel_md) + rel_md];
           }
-          // per-element mask only where some row of the group does not see
-          // the whole chunk (sequence end, window edges, diagonal)
-          bool whole = gfull[q] && c0 + 16 <= L;
+          // per-element mask only where some existing row of the group does
+          // not see the whole chunk (sequence end, window edges, diagonal).
+          // Rows past n_q are not masked: their q is zero, they see no key at
+          // or past L, and their outputs are never stored.
+          bool whole = c0 + 16 <= L;
           if constexpr (CAUSAL) whole = whole && c0 + 15 <= gp0[q];
           if constexpr (WINDOW)
             whole = whole && gp1[q] - c0 < a.window && c0 + 15 - gp0[q] < a.window;
           if (!whole) {
+            const int d0 = dq[q] - c0;
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-              const int j = j0 + r;
-              bool vis = row_ok[q] && j < L;
-              if constexpr (CAUSAL) vis = vis && j <= p[q];
-              if constexpr (WINDOW) vis = vis && abs(p[q] - j) < a.window;
+              const int d = d0 - r;
+              bool vis = d > dlo[q];
+              if constexpr (WINDOW) vis = vis && d < a.window;
               s[q][ch][r] = vis ? s[q][ch][r] : -INFINITY;
             }
           }

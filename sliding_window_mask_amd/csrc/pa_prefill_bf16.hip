@@ -135,9 +135,12 @@ pa_prefill_bf16(PrefillArgs a) {
   const float bmul = a.scale_log2 == 0.0f ? 0.0f : (a.scale_log2 < 0.0f ? -1.0f : 1.0f);
 
   // per sub-tile: query row of lane c, its position, whether it exists; the
-  // sub-tile's first / last position and whether all 16 rows exist (uniform)
-  int t_row[kSub], p_row[kSub], sp0[kSub], sp1[kSub];
-  bool row_ok[kSub], sub_full[kSub];
+  // sub-tile's first / last existing position (uniform). Masking of partly
+  // visible chunks: with d = p - j for key j = c0 + 4g + r, d = dq - c0 - r,
+  // and the key is visible iff dlo < d (j < L, causal j <= p, window
+  // p - j > -W) and, with a window, d < W.
+  int t_row[kSub], p_row[kSub], sp0[kSub], sp1[kSub], dq[kSub], dlo[kSub];
+  bool row_ok[kSub];
 #pragma unroll
   for (int sb = 0; sb < kSub; ++sb) {
     const int f = w_first + 16 * sb;
@@ -146,7 +149,11 @@ pa_prefill_bf16(PrefillArgs a) {
     p_row[sb] = pos0 + t_row[sb];
     sp0[sb] = pos0 + f;
     sp1[sb] = pos0 + min(f + 15, nq - 1);
-    sub_full[sb] = f + 15 < nq;
+    dq[sb] = p_row[sb] - 4 * g;
+    int lo = p_row[sb] - L;
+    if constexpr (CAUSAL) lo = max(lo, -1);
+    if constexpr (WINDOW) lo = max(lo, -a.window);
+    dlo[sb] = lo;
   }
 
   // Q operands: kSteps x 8 bf16 per sub-tile (rows past n_q, and every row
@@ -365,17 +372,19 @@ pa_prefill_bf16(PrefillArgs a) {
             for (int r = 0; r < 4; ++r)
               s[sb][ch][r] += rel_lds[min(max(j0 + r - p_row[sb], -rel_md), rel_md) + rel_md];
           }
-          bool whole = sub_full[sb] && c0 + 16 <= L;
+          // rows past n_q are not masked: their q is zero, they see no key
+          // at or past L, and their outputs are never stored
+          bool whole = c0 + 16 <= L;
           if constexpr (CAUSAL) whole = whole && c0 + 15 <= sp0[sb];
           if constexpr (WINDOW)
             whole = whole && sp1[sb] - c0 < a.window && c0 + 15 - sp0[sb] < a.window;
           if (!whole) {
+            const int d0 = dq[sb] - c0;
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-              const int j = j0 + r;
-              bool vis = row_ok[sb] && j < L;
-              if constexpr (CAUSAL) vis = vis && j <= p_row[sb];
-              if constexpr (WINDOW) vis = vis && abs(p_row[sb] - j) < a.window;
+              const int d = d0 - r;
+              bool vis = d > dlo[sb];
+              if constexpr (WINDOW) vis = vis && d < a.window;
               s[sb][ch][r] = vis ? s[sb][ch][r] : -INFINITY;
             }
           }
