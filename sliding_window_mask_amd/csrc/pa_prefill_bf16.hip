@@ -51,9 +51,6 @@ namespace {
 typedef float float4_t __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 
-#ifndef PA_PREFILL_BF16_VEARLY
-#define PA_PREFILL_BF16_VEARLY 0
-#endif
 #ifndef PA_PREFILL_BF16_SUB64
 #define PA_PREFILL_BF16_SUB64 1     // 16-query sub-tiles per wave, head_dim 64
 #endif
@@ -331,8 +328,8 @@ pa_prefill_bf16(PrefillArgs a) {
         qk(IntC<1>{});
       else
         qk(IntC<2>{});
-      // V^T operands of this tile (read early, while the softmax runs, when
-      // PA_PREFILL_BF16_VEARLY is set)
+      // V^T operands of this tile (read after the softmax: reading them before
+      // it measured slower)
       uint4 vv[kNDT];
       auto read_v = [&]() {
         // lane j of group g points at key 4g + j/4, dims 16dt + 4(j%4) .. +3;
@@ -349,7 +346,6 @@ pa_prefill_bf16(PrefillArgs a) {
           vv[dt] = make_uint4(lo.x, lo.y, hi.x, hi.y);
         }
       };
-      if (PA_PREFILL_BF16_VEARLY) read_v();
       bf16x8_t pw[kSub];
 #pragma unroll
       for (int sb = 0; sb < kSub; ++sb) {
@@ -418,7 +414,7 @@ pa_prefill_bf16(PrefillArgs a) {
                 (__bf16)__builtin_amdgcn_exp2f(fmaf(s[sb][ch][r], cs, neg_m[sb]));
         }
       }
-      if (!PA_PREFILL_BF16_VEARLY) read_v();
+      read_v();
       // ---- O^T += V^T P^T over the tile's 32 keys, row sums alongside ----
 #pragma unroll
       for (int sb = 0; sb < kSub; ++sb) lacc[sb] = mfma_bf16(ones, pw[sb], lacc[sb]);
