@@ -90,15 +90,74 @@ __device__ __forceinline__ void prefill_key_range(int p0, int p1, int L, int win
 
 constexpr int kXcds = 8;   // XCDs of an MI355X
 
-// Workgroup id -> (query tile, sequence * heads + head) such that every query
-// tile of one (sequence, head) runs on the same XCD: the dispatcher deals
-// consecutive workgroup ids round-robin over the XCDs, so ids n with the same
-// n % 8 share an XCD and its L2. The grid has ceil(pairs / 8) * 8 * num_qtiles
-// workgroups; ids whose pair is past the end return.
-__device__ __forceinline__ void prefill_tile_of(int n, int num_qtiles, int& pair, int& tile) {
+constexpr int kRankMaxSeqs = 63;   // batches ranked by length inside the kernel
+
+// Workgroup id -> (sequence b, head h, query tile), the sequence's length L
+// and its packed query rows q0 .. q0 + nq - 1; false for ids past the last
+// (sequence, head) pair (uniform over the workgroup). The grid has
+// ceil(pairs / 8) * 8 * num_qtiles workgroups. Every query tile of one
+// (sequence, head) runs on the same XCD: the dispatcher deals consecutive
+// workgroup ids round-robin over the XCDs, so ids n with the same n % 8 share
+// an XCD and its L2.
+// Without a window, a workgroup's work grows with its sequence's length, so
+// for batches of at most 63 sequences the pairs are dealt longest sequence
+// first (ties by index): the longest workgroups start first and the launch
+// does not end on a few long ones still running. Wave 0 reads every length
+// and query offset in one coalesced load (lane j: sequence j), ranks the
+// sequences by the distinct keys (L << 6) | (63 - j) (vector compares
+// against keys broadcast from LDS, four per read; needs max_seq_len < 2^25)
+// and hands its sequence's values to the other waves through LDS (one
+// barrier). Windowed launches (bounded work per workgroup) and larger
+// batches keep index order.
+__device__ __forceinline__ bool prefill_work_of(int n, const PrefillArgs& a, int& b, int& h,
+                                                int& tile, int& L, int& q0, int& nq) {
+  const int H = a.num_heads;
+  const int B = a.num_seqs;
   const int slot = n / kXcds;
-  pair = (slot / num_qtiles) * kXcds + n % kXcds;
-  tile = slot % num_qtiles;
+  const int pr = (slot / a.num_qtiles) * kXcds + n % kXcds;   // pair in dispatch order
+  tile = slot % a.num_qtiles;
+  if (pr >= B * H) return false;
+  const int r = pr / H;   // rank of the sequence in dispatch order
+  h = pr % H;
+  if (B <= kRankMaxSeqs && a.window <= 0 && a.max_seq_len < (1 << 25)) {
+    __shared__ int picked[4];
+    __shared__ __attribute__((aligned(16))) unsigned keys[64];
+    if (threadIdx.x < 64) {
+      const int lane = threadIdx.x;
+      const int Lj = lane < B ? a.context_lens[lane] : 0;
+      const int Qj = lane <= B ? a.query_start_loc[lane] : 0;
+      // distinct for lanes < B (lengths are validated to [0, max_seq_len]);
+      // the zero keys of lanes >= B are below all of them
+      const unsigned kj = lane < B ? ((unsigned)Lj << 6) | (63u - (unsigned)lane) : 0u;
+      keys[lane] = kj;   // read back by this wave only: LDS order within a wave
+      int rank = 0;      // keys above lane's
+      for (int i = 0; i < B; i += 4) {
+        const uint4 k4 = *reinterpret_cast<const uint4*>(&keys[i]);
+        rank += (k4.x > kj ? 1 : 0) + (k4.y > kj ? 1 : 0) + (k4.z > kj ? 1 : 0) +
+                (k4.w > kj ? 1 : 0);
+      }
+      // ranks are a permutation of 0 .. B-1: exactly one lane holds r
+      const int sb = (int)__builtin_ctzll(__builtin_amdgcn_ballot_w64(lane < B && rank == r));
+      if (lane == 0) {
+        const int qb = __builtin_amdgcn_readlane(Qj, sb);
+        picked[0] = sb;
+        picked[1] = __builtin_amdgcn_readlane(Lj, sb);
+        picked[2] = qb;
+        picked[3] = __builtin_amdgcn_readlane(Qj, sb + 1) - qb;
+      }
+    }
+    __syncthreads();
+    b = __builtin_amdgcn_readfirstlane(picked[0]);
+    L = __builtin_amdgcn_readfirstlane(picked[1]);
+    q0 = __builtin_amdgcn_readfirstlane(picked[2]);
+    nq = __builtin_amdgcn_readfirstlane(picked[3]);
+  } else {
+    b = r;
+    L = a.context_lens[b];
+    q0 = a.query_start_loc[b];
+    nq = a.query_start_loc[b + 1] - q0;
+  }
+  return true;
 }
 
 // Bucket of a non-negative distance within one direction (see RelPos).

@@ -14,7 +14,9 @@
 // query tile of one (sequence, head) lands on the same XCD (the hardware
 // deals consecutive workgroup ids round-robin over the 8 XCDs): the K/V of a
 // sequence is then pulled into one XCD's L2 and re-read from there by all of
-// its query tiles.
+// its query tiles. Without a window, and for batches of up to 63 sequences,
+// the (sequence, head) pairs are dealt longest sequence first, so that the
+// launch does not end on a few long workgroups that started last.
 //
 // The workgroup walks the keys its rows can see in tiles of 16 keys. Tiles are gathered through the block table into a double-buffered
 // LDS ring (rows padded by 4 floats against bank conflicts) with one barrier
@@ -100,14 +102,10 @@ pa_prefill_f32(PrefillArgs a) {
   constexpr int kQT = kWaves * kWaveRows;            // query rows per workgroup
   static_assert(kLoads >= 1 && kRowsPerLoad <= 16 && 16 % kRowsPerLoad == 0, "tile shape");
 
-  // ---- XCD-aware workgroup numbering ----
+  // ---- XCD-aware workgroup numbering, longest sequences first ----
   const int H = a.num_heads;
-  const int n = blockIdx.x;
-  int pair, tile;
-  prefill_tile_of(n, a.num_qtiles, pair, tile);
-  if (pair >= a.num_seqs * H) return;
-  const int b = pair / H;
-  const int h = pair % H;
+  int b, h, tile, L, q0, nq;
+  if (!prefill_work_of(blockIdx.x, a, b, h, tile, L, q0, nq)) return;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -115,9 +113,6 @@ pa_prefill_f32(PrefillArgs a) {
   const int c = lane & 15;
   const int g = lane >> 4;
 
-  const int L = a.context_lens[b];
-  const int q0 = a.query_start_loc[b];
-  const int nq = a.query_start_loc[b + 1] - q0;
   const int t_first = tile * kQT;
   if (t_first >= nq) return;
   const int pos0 = L - nq;                 // position of query 0

@@ -16,7 +16,8 @@
 // and multiplier 1.
 //
 // One workgroup per (64-query tile, head, sequence), numbered so that all
-// query tiles of a (sequence, head) share an XCD. Each wave owns kSub
+// query tiles of a (sequence, head) share an XCD, longest sequences first
+// (launches without a window, batches of up to 63 sequences). Each wave owns kSub
 // sub-tiles of 16 queries and multiplies every K and V operand it reads from
 // LDS into all of them. The default is 4 waves x 1 sub-tile; 2 waves x 2
 // sub-tiles (PA_PREFILL_BF16_SUB64=2, head_dim 64) halves the LDS reads per
@@ -98,11 +99,8 @@ pa_prefill_bf16(PrefillArgs a) {
   static_assert(D == 64 || D == 128, "head_dim");
 
   const int H = a.num_heads;
-  int pair, tile;
-  prefill_tile_of(blockIdx.x, a.num_qtiles, pair, tile);
-  if (pair >= a.num_seqs * H) return;
-  const int b = pair / H;
-  const int h = pair % H;
+  int b, h, tile, L, q0, nq;
+  if (!prefill_work_of(blockIdx.x, a, b, h, tile, L, q0, nq)) return;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -110,9 +108,6 @@ pa_prefill_bf16(PrefillArgs a) {
   const int c = lane & 15;
   const int g = lane >> 4;
 
-  const int L = a.context_lens[b];
-  const int q0 = a.query_start_loc[b];
-  const int nq = a.query_start_loc[b + 1] - q0;
   const int t_first = tile * kQT;
   if (t_first >= nq) return;
   const int pos0 = L - nq;

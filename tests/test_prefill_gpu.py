@@ -71,6 +71,23 @@ def test_prefill_empty_sequences():
     assert_close(gpu_prefill(case), oracle_prefill(case), torch.float32, "empty")
 
 
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+@pytest.mark.parametrize("B", [1, 62, 63, 64, 100])
+@pytest.mark.parametrize("window,causal", [(-1, False), (-1, True), (24, False)])
+def test_prefill_batch_sizes_around_length_ranking(B, dtype, window, causal):
+    # without a window and for up to 63 sequences the kernels deal workgroups
+    # to sequences longest first (ties broken by index), otherwise in index
+    # order: both orders, many tied lengths and empty sequences must give the
+    # oracle's results
+    lens = np.random.default_rng(700 + B).choice([0, 1, 16, 17, 40, 40, 40, 90], size=B)
+    case = to_device(workloads.prefill_case(710 + B, num_seqs=B, num_heads=2, head_dim=64,
+                                            lens=lens.tolist(), max_seq_len=96, dtype=dtype,
+                                            sliding_window=window, causal=causal))
+    log("ranking B=%d dtype=%s W=%d causal=%s" % (B, dtype, window, causal))
+    assert_close(gpu_prefill(case), oracle_prefill(case), dtype,
+                 "B=%d dtype=%s W=%d causal=%s" % (B, dtype, window, causal))
+
+
 def test_prefill_deterministic():
     case = to_device(small(650, [300, 511, 64], window=64, msl=512))
     a = gpu_prefill(case)
