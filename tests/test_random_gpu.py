@@ -85,3 +85,103 @@ def test_prefill_last_query_equals_decode(dtype, D, window):
     log("prefill(n_q=1) vs decode D=%d W=%d dtype=%s: %.3e" % (D, window, dtype, err))
     assert err <= TOL[dtype]
     assert_close(dec, oracle_decode(dc, bias=None), dtype, "decode")
+
+
+def pack(dense, lens, q_lens=None):
+    """Packed (ragged) copy of a padded bias: decode rows [H][L_b], prefill
+    rows [H][n_q][L_b] (the last n_q positions), back to back, with offsets."""
+    parts, starts, off = [], [], 0
+    for b, L in enumerate(lens):
+        L = int(L)
+        if q_lens is None:
+            part = dense[b, :, :L]
+        else:
+            nq = int(q_lens[b])
+            part = dense[b, :, L - nq:L, :L]
+        parts.append(part.reshape(-1))
+        starts.append(off)
+        off += part.numel()
+    packed = torch.cat(parts) if parts else torch.zeros(0)
+    return packed.contiguous(), torch.tensor(starts, dtype=torch.int64)
+
+
+@pytest.mark.parametrize("seed", range(16))
+def test_random_relpos(seed):
+    # in-kernel T5 bias over random bucket tables, both kernels' dtypes and head dims
+    d = draw(6000 + seed)
+    r = d["rng"]
+    nb = int(r.choice([4, 8, 16, 32]))
+    md = int(r.choice([nb, 2 * nb, 128, 1000]))
+    bidir = int(r.integers(0, 2))
+    msl = -(-d["maxlen"] // BS) * BS
+    lens = r.integers(0, d["maxlen"] + 1, size=d["B"])
+    table = torch.from_numpy(r.standard_normal((d["H"], nb)).astype(np.float32) * 2.0)
+    log("random relpos %d: %s nb=%d md=%d bidir=%d" % (
+        seed, {k: v for k, v in d.items() if k != "rng"}, nb, md, bidir))
+    dc = to_device(workloads.decode_case(6100 + seed, num_seqs=d["B"], num_heads=d["H"],
+                                         head_dim=d["D"], lens=lens.tolist(), max_seq_len=msl,
+                                         dtype=d["dtype"], bias=None,
+                                         sliding_window=d["window"]))
+    out = pa.paged_attn_decode_relpos(dc.q, dc.k_cache, dc.v_cache, dc.block_tables,
+                                      dc.context_lens, table.to("cuda"), nb, md, bidir,
+                                      d["window"], dc.scale, max_seq_len=msl,
+                                      partition_tokens=d["partition"])
+    h = to_host(dc)
+    ref = oracle.decode_relpos(h.q, h.k_cache, h.v_cache, h.block_tables, h.context_lens,
+                               table, nb, md, bidir, d["window"], h.scale, msl)
+    assert_close(out, ref, d["dtype"], "random relpos decode %d" % seed)
+    q_lens = [int(r.integers(0, L + 1)) for L in lens]
+    pc = to_device(workloads.prefill_case(6200 + seed, num_seqs=d["B"], num_heads=d["H"],
+                                          head_dim=d["D"], lens=lens.tolist(), max_seq_len=msl,
+                                          dtype=d["dtype"], bias=None,
+                                          sliding_window=d["window"], causal=d["causal"],
+                                          q_lens=q_lens))
+    out = pa.paged_attn_prefill_relpos(pc.q, pc.k_cache, pc.v_cache, pc.block_tables,
+                                       pc.context_lens, pc.query_start_loc, table.to("cuda"),
+                                       nb, md, bidir, d["window"], d["causal"], pc.scale,
+                                       max_seq_len=msl)
+    h = to_host(pc)
+    ref = oracle.prefill_relpos(h.q, h.k_cache, h.v_cache, h.block_tables, h.context_lens,
+                                h.query_start_loc, table, nb, md, bidir, d["window"],
+                                int(d["causal"]), h.scale, msl)
+    assert_close(out, ref, d["dtype"], "random relpos prefill %d" % seed)
+
+
+@pytest.mark.parametrize("seed", range(16))
+def test_random_ragged_bias(seed):
+    # packed bias offsets over random lengths (zero lengths included), both
+    # entry points, both dtypes and head dims
+    d = draw(7000 + seed)
+    r = d["rng"]
+    msl = -(-d["maxlen"] // BS) * BS
+    lens = r.integers(0, d["maxlen"] + 1, size=d["B"])
+    log("random ragged %d: %s" % (seed, {k: v for k, v in d.items() if k != "rng"}))
+    dc = to_device(workloads.decode_case(7100 + seed, num_seqs=d["B"], num_heads=d["H"],
+                                         head_dim=d["D"], lens=lens.tolist(), max_seq_len=msl,
+                                         dtype=d["dtype"], bias="normal",
+                                         sliding_window=d["window"]))
+    packed, starts = pack(dc.attn_bias.cpu(), lens)
+    out = pa.paged_attn_decode_ragged_bias(dc.q, dc.k_cache, dc.v_cache, dc.block_tables,
+                                           dc.context_lens, packed.to("cuda"),
+                                           starts.to("cuda"), d["window"], dc.scale,
+                                           max_seq_len=msl, partition_tokens=d["partition"])
+    h = to_host(dc)
+    ref = oracle.decode_ragged(h.q, h.k_cache, h.v_cache, h.block_tables, h.context_lens,
+                               packed, starts, d["window"], h.scale, msl)
+    assert_close(out, ref, d["dtype"], "random ragged decode %d" % seed)
+    q_lens = [int(r.integers(0, L + 1)) for L in lens]
+    pc = to_device(workloads.prefill_case(7200 + seed, num_seqs=d["B"], num_heads=d["H"],
+                                          head_dim=d["D"], lens=lens.tolist(), max_seq_len=msl,
+                                          dtype=d["dtype"], bias="normal",
+                                          sliding_window=d["window"], causal=d["causal"],
+                                          q_lens=q_lens))
+    packed, starts = pack(pc.attn_bias.cpu(), lens, q_lens)
+    out = pa.paged_attn_prefill_ragged_bias(pc.q, pc.k_cache, pc.v_cache, pc.block_tables,
+                                            pc.context_lens, pc.query_start_loc,
+                                            packed.to("cuda"), starts.to("cuda"), d["window"],
+                                            d["causal"], pc.scale, max_seq_len=msl)
+    h = to_host(pc)
+    ref = oracle.prefill_ragged(h.q, h.k_cache, h.v_cache, h.block_tables, h.context_lens,
+                                h.query_start_loc, packed, starts, d["window"],
+                                int(d["causal"]), h.scale, msl)
+    assert_close(out, ref, d["dtype"], "random ragged prefill %d" % seed)
