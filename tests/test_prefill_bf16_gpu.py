@@ -94,3 +94,36 @@ def test_modernbert_shaped_bf16_layer_sampled(layer):
     seqs = sorted(set([int(np.argmax(L)), int(np.argmin(L)), 5, 17]))
     sub = sample_prefill(case, seqs)
     assert_close(out[sub.rows.to(DEV)], oracle_prefill(sub), BF, "bf16 layer %d" % layer)
+
+
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("bias", [None, "normal", "relpos"])
+@pytest.mark.parametrize("partial", [False, True])
+def test_prefill_bf16_bidirectional_128_query_tiles(D, bias, partial):
+    # bidirectional launches without a window run in workgroups of 128 queries
+    # (four waves of 32, 32x32x16 MFMAs): lengths on both sides of 32 and 128
+    # and their multiples, a last wave with one query, and query sets that
+    # start part-way into the sequence (the last n_q positions)
+    lens = [1, 31, 32, 33, 97, 127, 128, 129, 160, 255, 257, 300]
+    q_lens = [L for L in lens] if not partial else [1, 30, 1, 32, 96, 1, 127, 128, 33, 200,
+                                                    129, 171]
+    msl = 304
+    scale = -0.09 if partial else None   # a negative scale on the partial sets
+    log("bf16 128-query tiles D=%d bias=%s partial=%s" % (D, bias, partial))
+    case = to_device(workloads.prefill_case(1500 + D + 3 * partial, num_seqs=len(lens),
+                                            num_heads=2, head_dim=D, lens=lens, max_seq_len=msl,
+                                            dtype=BF, bias="normal" if bias == "normal" else None,
+                                            q_lens=q_lens, scale=scale))
+    if bias != "relpos":
+        assert_close(gpu_prefill(case), oracle_prefill(case), BF,
+                     "bf16 128-query tiles D=%d bias=%s partial=%s" % (D, bias, partial))
+        return
+    nb, md = 16, 64
+    table = torch.from_numpy(np.random.default_rng(D).standard_normal((2, nb)).astype(np.float32))
+    out = pa.paged_attn_prefill_relpos(case.q, case.k_cache, case.v_cache, case.block_tables,
+                                       case.context_lens, case.query_start_loc, table.to(DEV),
+                                       nb, md, 1, -1, False, case.scale, max_seq_len=msl)
+    h = to_host(case)
+    ref = oracle.prefill_relpos(h.q, h.k_cache, h.v_cache, h.block_tables, h.context_lens,
+                                h.query_start_loc, table, nb, md, 1, -1, 0, h.scale, msl)
+    assert_close(out, ref, BF, "bf16 128-query tiles relpos D=%d partial=%s" % (D, partial))
