@@ -58,9 +58,10 @@ def source_sha(name):
     return hashlib.sha256(open(p, "rb").read()).hexdigest()[:16]
 
 
-def read_traffic(workload, kernel_src):
-    """HBM bytes per launch from the committed rocprofv3 counter summary, if it
-    was taken on the current kernel source; otherwise None."""
+def read_traffic(workload, kernel_src, key="hbm_bytes_per_launch"):
+    """HBM bytes (per launch, or the given key) from the committed rocprofv3
+    counter summary, if it was taken on the current kernel source; otherwise
+    None."""
     path = os.path.join(PROFILES, "%s_traffic.txt" % workload)
     if not os.path.exists(path):
         return None
@@ -72,7 +73,7 @@ def read_traffic(workload, kernel_src):
     if kv.get("kernel_source_sha") != source_sha(kernel_src):
         return None
     try:
-        return float(kv["hbm_bytes_per_launch"])
+        return float(kv[key])
     except (KeyError, ValueError):
         return None
 
@@ -340,7 +341,11 @@ def bench_prefill(args, dtype=torch.float32):
                    "windows": [workloads.modernbert_window(l) for l in range(12)]},
         "roofline": {"bound": "mfma", "achieved": tflops, "peak": peak,
                      "unit": "TFLOP/s", "frac": tflops / peak,
-                     "traffic": None, "kernel": "pa_prefill_%s (12 launches per step)" % tag},
+                     # HBM bytes of one step (the 12 launches), from the counters
+                     "traffic": read_traffic("modernbert_prefill_" + tag,
+                                             "pa_prefill.hip" if tag == "f32"
+                                             else "pa_prefill_bf16.hip", "hbm_bytes_per_step"),
+                     "kernel": "pa_prefill_%s (12 launches per step)" % tag},
         "algorithmic_flops_per_step": flops,
     }
     return line
