@@ -186,6 +186,22 @@ pa_prefill_f32(PrefillArgs a) {
   const int kstart = wg_lo & ~(kBlockSize - 1);
   const int ntiles = wg_hi > kstart ? (wg_hi - kstart + kKTile - 1) / kKTile : 0;
   const int nblk_seq = (L + kBlockSize - 1) / kBlockSize;
+  // Windowed launches visit the workgroup's key tiles in a rotated order:
+  // first the 64-key segment of the band whose index (key / 64) is a
+  // multiple of 3, then the following ones, wrapping round. Each segment is
+  // read by about three neighbouring query tiles, and this way all of them
+  // read it in the same third of their loop, while it is still in L2.
+  int rot = 0;
+  if constexpr (WINDOW) {
+    const int seg0 = kstart / 64;
+    const int first = (seg0 + (3 - seg0 % 3) % 3) * 64;
+    if (first > kstart && first < kstart + ntiles * kKTile) rot = (first - kstart) / kKTile;
+  }
+  auto tile_base = [&](int tk) {
+    int p = tk + rot;
+    if (p >= ntiles) p -= ntiles;
+    return kstart + p * kKTile;
+  };
 
   // block-table entries of one tile (uniform across the workgroup)
   constexpr int kTB = (kKTile + kBlockSize - 1) / kBlockSize;
@@ -193,7 +209,7 @@ pa_prefill_f32(PrefillArgs a) {
   auto load_table = [&](int tk) {
 #pragma unroll
     for (int i = 0; i < kTB; ++i) {
-      const int blk = (kstart + tk * kKTile) / kBlockSize + i;
+      const int blk = tile_base(tk) / kBlockSize + i;
       tb[i] = blk < nblk_seq ? table[blk] : 0;
     }
   };
@@ -227,7 +243,7 @@ pa_prefill_f32(PrefillArgs a) {
       *reinterpret_cast<float4_t*>(&kv_lds[buf][0][r * kRow + col]) = kst[i];
       *reinterpret_cast<float4_t*>(&kv_lds[buf][1][r * kRow + col]) = vst[i];
     }
-    const int base = kstart + tk * kKTile;
+    const int base = tile_base(tk);
     if (base + kKTile > L) {   // uniform: only a sequence's last tile
       // the zero is made here, not hoisted into a register held across the loop
       float z;
@@ -286,7 +302,7 @@ pa_prefill_f32(PrefillArgs a) {
   // LDS address is a per-lane base plus an immediate
   auto tile_step = [&](int tk, auto buf_c) {
     constexpr int buf = decltype(buf_c)::value;
-    const int base = kstart + tk * kKTile;
+    const int base = tile_base(tk);
     if (wave_active && base < wv_hi && base + kKTile > wv_lo) {
       const float* k_lds = kv_lds[buf][0];
       const float* v_lds = kv_lds[buf][1];

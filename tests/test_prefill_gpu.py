@@ -56,6 +56,23 @@ def test_prefill_partial_queries(causal):
     assert_close(gpu_prefill(case), oracle_prefill(case), torch.float32, "partial q")
 
 
+@pytest.mark.parametrize("window", [2, 40, 64, 100, 190])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("partial", [False, True])
+def test_prefill_window_segment_order(window, causal, partial):
+    """Windowed fp32 launches visit a workgroup's key tiles starting from a
+    64-key segment chosen by its index, wrapping round: bands of one to
+    several segments, cut off at either end of a sequence, and bands that do
+    not start on a segment boundary (partial query sets) must all give the
+    oracle's result."""
+    lens = [3, 64, 65, 127, 200, 333]
+    q_lens = [2, 50, 65, 100, 7, 301] if partial else None
+    case = to_device(small(640 + window, lens, H=2, window=window, causal=causal,
+                           q_lens=q_lens, msl=336))
+    assert_close(gpu_prefill(case), oracle_prefill(case), torch.float32,
+                 "segment order W=%d causal=%s partial=%s" % (window, causal, partial))
+
+
 def test_prefill_window_one_returns_own_value():
     case = to_device(small(630, [1, 20, 77], window=1))
     out = gpu_prefill(case).cpu()
