@@ -66,7 +66,7 @@ def call_decode(lib, a):
     (dict(window=0), 2), (dict(window=-2), 2),
     (dict(D=96), 3), (dict(D=32), 3), (dict(bs=32), 3), (dict(Hkv=2), 3), (dict(dtype=2), 3),
     (dict(maxb=7), 2), (dict(B=-1), 2), (dict(H=0), 2), (dict(scale=float("inf")), 2),
-    (dict(scale=float("nan")), 2),
+    (dict(scale=float("nan")), 2), (dict(B=65536), 2), (dict(H=65536, Hkv=65536), 2),
     (dict(q=FAKE + 4), 4), (dict(out=FAKE + 8), 4), (dict(bias=FAKE + 2), 4),
     (dict(part=24), 2), (dict(part=-16), 2), (dict(part=8192), 2),
 ])
@@ -132,6 +132,8 @@ def prefill_call(lib, **kw):
 @pytest.mark.parametrize("kw,status", [
     (dict(qsl=None), 1), (dict(causal=2), 2), (dict(tq=-1), 2), (dict(window=0), 2),
     (dict(D=80), 3), (dict(dtype=2), 3), (dict(qsl=FAKE + 2), 4), (dict(k=None), 1),
+    (dict(B=65536), 2), (dict(H=65536, Hkv=65536), 2), (dict(maxb=7), 2),
+    (dict(scale=float("nan")), 2),
 ])
 def test_prefill_rejects_on_host(kw, status):
     lib = pa.lib()
