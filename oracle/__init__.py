@@ -55,6 +55,10 @@ def _load():
         lib.oracle_prefill_f64.restype = ctypes.c_int
         lib.oracle_prefill_f64.argtypes = [P, P, P, P, P, P, P, P, I32, I32, F64,
                                            I32, I32, I32, I32, I32, I32, I32]
+        lib.oracle_decode_chunked_f64.restype = ctypes.c_int
+        lib.oracle_decode_chunked_f64.argtypes = lib.oracle_decode_f64.argtypes
+        lib.oracle_prefill_chunked_f64.restype = ctypes.c_int
+        lib.oracle_prefill_chunked_f64.argtypes = lib.oracle_prefill_f64.argtypes
         lib.oracle_t5_bucket_array.restype = None
         lib.oracle_t5_bucket_array.argtypes = [P, ctypes.c_int64, I32, I32, I32, P]
         lib.oracle_decode_relpos_f64.restype = ctypes.c_int
@@ -176,6 +180,51 @@ def prefill(q, k_cache, v_cache, block_tables, context_lens, query_start_loc, at
         bt.shape[1] if bt.ndim == 2 else 0, int(max_seq_len), dt)
     if rc != 0:
         raise ValueError("oracle_prefill_f64 rejected its arguments")
+    return out
+
+
+def decode_chunked(q, k_cache, v_cache, block_tables, context_lens, attn_bias, chunk_size,
+                   scale, max_seq_len):
+    """Float64 decode with chunked local attention (no window): the query at
+    position L-1 sees keys chunk_size * floor((L-1) / chunk_size) .. L-1.
+    Arguments and result as in decode()."""
+    dt = _kv_dtype(q)
+    qh, kh, vh = _host(q), _host(k_cache), _host(v_cache)
+    bt = _host(block_tables, np.int32)
+    cl = _host(context_lens, np.int32)
+    ab = _host(attn_bias, np.float32)
+    B, H, D = qh.shape
+    out = np.zeros((B, H, D), dtype=np.float64)
+    rc = _load().oracle_decode_chunked_f64(
+        _ptr(out), _ptr(qh), _ptr(kh), _ptr(vh), _ptr(bt), _ptr(cl), _ptr(ab),
+        int(chunk_size), float(scale), B, H, D, kh.shape[2],
+        bt.shape[1] if bt.ndim == 2 else 0, int(max_seq_len), dt)
+    if rc != 0:
+        raise ValueError("oracle_decode_chunked_f64 rejected its arguments")
+    return out
+
+
+def prefill_chunked(q, k_cache, v_cache, block_tables, context_lens, query_start_loc,
+                    attn_bias, chunk_size, causal, scale, max_seq_len):
+    """Float64 prefill with chunked local attention (no window): a query at
+    position p sees the keys j with floor(j / chunk_size) = floor(p /
+    chunk_size), and j <= p when causal. Arguments and result as in
+    prefill()."""
+    dt = _kv_dtype(q)
+    qh, kh, vh = _host(q), _host(k_cache), _host(v_cache)
+    bt = _host(block_tables, np.int32)
+    cl = _host(context_lens, np.int32)
+    qsl = _host(query_start_loc, np.int32)
+    ab = _host(attn_bias, np.float32)
+    TQ, H, D = qh.shape
+    B = cl.shape[0]
+    out = np.zeros((TQ, H, D), dtype=np.float64)
+    rc = _load().oracle_prefill_chunked_f64(
+        _ptr(out), _ptr(qh), _ptr(kh), _ptr(vh), _ptr(bt), _ptr(cl), _ptr(qsl), _ptr(ab),
+        int(chunk_size), int(causal), float(scale), B, H, D, kh.shape[2],
+        bt.shape[1] if bt.ndim == 2 else 0, int(max_seq_len), dt)
+    if rc != 0:
+        raise ValueError("oracle_prefill_chunked_f64 rejected its arguments")
     return out
 
 

@@ -42,14 +42,18 @@ static int64_t kv_offset(const int32_t* table, int32_t j, int32_t h, int32_t num
 
 /* Whether key j is visible to a query at logical position p: the key must be
  * one of the L cached tokens; with a window W >= 1 it must satisfy
- * |p - j| < W; a causal query also needs j <= p. */
-static int visible(int32_t p, int32_t j, int32_t L, int32_t window, int32_t causal) {
+ * |p - j| < W; with chunked local attention of chunk size C >= 1 it must lie
+ * in the query's chunk, floor(j / C) = floor(p / C); a causal query also
+ * needs j <= p. */
+static int visible(int32_t p, int32_t j, int32_t L, int32_t window, int32_t causal,
+                   int32_t chunk) {
   if (j < 0 || j >= L) return 0;
   if (causal && j > p) return 0;
   if (window > 0) {
     int32_t d = p > j ? p - j : j - p;
     if (d >= window) return 0;
   }
+  if (chunk > 0 && j / chunk != p / chunk) return 0;
   return 1;
 }
 
@@ -59,14 +63,14 @@ static int visible(int32_t p, int32_t j, int32_t L, int32_t window, int32_t caus
  * `s` is scratch for L scores. */
 static void attend_row(double* out_row, const void* q, int64_t q_off, const void* k_cache,
                        const void* v_cache, const int32_t* table, const float* bias_row,
-                       int32_t p, int32_t L, int32_t window, int32_t causal, double scale,
-                       int32_t h, int32_t num_heads, int32_t head_dim, int32_t block_size,
-                       int32_t dtype, double* s) {
+                       int32_t p, int32_t L, int32_t window, int32_t causal, int32_t chunk,
+                       double scale, int32_t h, int32_t num_heads, int32_t head_dim,
+                       int32_t block_size, int32_t dtype, double* s) {
   for (int32_t d = 0; d < head_dim; ++d) out_row[d] = 0.0;
   double m = -INFINITY;
   for (int32_t j = 0; j < L; ++j) {
     s[j] = -INFINITY;
-    if (!visible(p, j, L, window, causal)) continue;
+    if (!visible(p, j, L, window, causal, chunk)) continue;
     int64_t ko = kv_offset(table, j, h, num_heads, block_size, head_dim);
     double dot = 0.0;
     for (int32_t d = 0; d < head_dim; ++d)
@@ -98,12 +102,13 @@ static int bad_scalars(int32_t num_seqs, int32_t num_heads, int32_t head_dim,
   return 0;
 }
 
-int oracle_decode_f64(double* out, const void* q, const void* k_cache, const void* v_cache,
-                      const int32_t* block_tables, const int32_t* context_lens,
-                      const float* attn_bias, int32_t sliding_window, double scale,
-                      int32_t num_seqs, int32_t num_heads, int32_t head_dim,
-                      int32_t block_size, int32_t max_blocks_per_seq, int32_t max_seq_len,
-                      int32_t dtype) {
+static int decode_rows(double* out, const void* q, const void* k_cache, const void* v_cache,
+                       const int32_t* block_tables, const int32_t* context_lens,
+                       const float* attn_bias, int32_t sliding_window, int32_t chunk,
+                       double scale, int32_t num_seqs, int32_t num_heads, int32_t head_dim,
+                       int32_t block_size, int32_t max_blocks_per_seq, int32_t max_seq_len,
+                       int32_t dtype) {
+  if (chunk < 0) return -1;
   if (bad_scalars(num_seqs, num_heads, head_dim, block_size, max_blocks_per_seq, max_seq_len,
                   sliding_window, dtype))
     return -1;
@@ -122,20 +127,52 @@ int oracle_decode_f64(double* out, const void* q, const void* k_cache, const voi
       /* the decode query is the newest token, at position L - 1 */
       attend_row(out + bh * head_dim, q, bh * head_dim, k_cache, v_cache,
                  block_tables + (int64_t)b * max_blocks_per_seq, bias_row, L - 1, L,
-                 sliding_window, 0, scale, h, num_heads, head_dim, block_size, dtype, s);
+                 sliding_window, 0, chunk, scale, h, num_heads, head_dim, block_size, dtype, s);
     }
     free(s);
   }
   return 0;
 }
 
-int oracle_prefill_f64(double* out, const void* q, const void* k_cache, const void* v_cache,
-                       const int32_t* block_tables, const int32_t* context_lens,
-                       const int32_t* query_start_loc, const float* attn_bias,
-                       int32_t sliding_window, int32_t causal, double scale,
-                       int32_t num_seqs, int32_t num_heads, int32_t head_dim,
-                       int32_t block_size, int32_t max_blocks_per_seq, int32_t max_seq_len,
-                       int32_t dtype) {
+int oracle_decode_f64(double* out, const void* q, const void* k_cache, const void* v_cache,
+                      const int32_t* block_tables, const int32_t* context_lens,
+                      const float* attn_bias, int32_t sliding_window, double scale,
+                      int32_t num_seqs, int32_t num_heads, int32_t head_dim,
+                      int32_t block_size, int32_t max_blocks_per_seq, int32_t max_seq_len,
+                      int32_t dtype) {
+  return decode_rows(out, q, k_cache, v_cache, block_tables, context_lens, attn_bias,
+                     sliding_window, 0, scale, num_seqs, num_heads, head_dim, block_size,
+                     max_blocks_per_seq, max_seq_len, dtype);
+}
+
+/* Chunked local attention ("[V1] Add sliding window support to Flex
+ * Attention backend", review thread on attention groups: Llama 4 alternates
+ * full-attention layers with chunked-local-attention layers). The page names
+ * the layer type only; the reading taken here is the plain one: positions are
+ * cut into consecutive chunks of chunk_size tokens, and a query sees exactly
+ * the keys of its own chunk (a causal query only those up to itself). Parity
+ * unpinned for that reading. chunk_size >= 1; a decode query (position L - 1)
+ * sees keys chunk_size * floor((L - 1) / chunk_size) .. L - 1. */
+int oracle_decode_chunked_f64(double* out, const void* q, const void* k_cache,
+                              const void* v_cache, const int32_t* block_tables,
+                              const int32_t* context_lens, const float* attn_bias,
+                              int32_t chunk_size, double scale, int32_t num_seqs,
+                              int32_t num_heads, int32_t head_dim, int32_t block_size,
+                              int32_t max_blocks_per_seq, int32_t max_seq_len, int32_t dtype) {
+  if (chunk_size < 1) return -1;
+  return decode_rows(out, q, k_cache, v_cache, block_tables, context_lens, attn_bias, -1,
+                     chunk_size, scale, num_seqs, num_heads, head_dim, block_size,
+                     max_blocks_per_seq, max_seq_len, dtype);
+}
+
+static int prefill_rows(double* out, const void* q, const void* k_cache, const void* v_cache,
+                        const int32_t* block_tables, const int32_t* context_lens,
+                        const int32_t* query_start_loc, const float* attn_bias,
+                        int32_t sliding_window, int32_t causal, int32_t chunk, double scale,
+                        int32_t num_seqs, int32_t num_heads, int32_t head_dim,
+                        int32_t block_size, int32_t max_blocks_per_seq, int32_t max_seq_len,
+                        int32_t dtype) {
+  if (chunk < 0) return -1;
   if (bad_scalars(num_seqs, num_heads, head_dim, block_size, max_blocks_per_seq, max_seq_len,
                   sliding_window, dtype))
     return -1;
@@ -164,12 +201,39 @@ int oracle_prefill_f64(double* out, const void* q, const void* k_cache, const vo
                 : NULL;
         attend_row(out + row, q, row, k_cache, v_cache,
                    block_tables + (int64_t)b * max_blocks_per_seq, bias_row, p, L,
-                   sliding_window, causal, scale, h, num_heads, head_dim, block_size, dtype, s);
+                   sliding_window, causal, chunk, scale, h, num_heads, head_dim, block_size,
+                   dtype, s);
       }
     }
     free(s);
   }
   return 0;
+}
+
+int oracle_prefill_f64(double* out, const void* q, const void* k_cache, const void* v_cache,
+                       const int32_t* block_tables, const int32_t* context_lens,
+                       const int32_t* query_start_loc, const float* attn_bias,
+                       int32_t sliding_window, int32_t causal, double scale,
+                       int32_t num_seqs, int32_t num_heads, int32_t head_dim,
+                       int32_t block_size, int32_t max_blocks_per_seq, int32_t max_seq_len,
+                       int32_t dtype) {
+  return prefill_rows(out, q, k_cache, v_cache, block_tables, context_lens, query_start_loc,
+                      attn_bias, sliding_window, causal, 0, scale, num_seqs, num_heads,
+                      head_dim, block_size, max_blocks_per_seq, max_seq_len, dtype);
+}
+
+int oracle_prefill_chunked_f64(double* out, const void* q, const void* k_cache,
+                               const void* v_cache, const int32_t* block_tables,
+                               const int32_t* context_lens, const int32_t* query_start_loc,
+                               const float* attn_bias, int32_t chunk_size, int32_t causal,
+                               double scale, int32_t num_seqs, int32_t num_heads,
+                               int32_t head_dim, int32_t block_size,
+                               int32_t max_blocks_per_seq, int32_t max_seq_len,
+                               int32_t dtype) {
+  if (chunk_size < 1) return -1;
+  return prefill_rows(out, q, k_cache, v_cache, block_tables, context_lens, query_start_loc,
+                      attn_bias, -1, causal, chunk_size, scale, num_seqs, num_heads, head_dim,
+                      block_size, max_blocks_per_seq, max_seq_len, dtype);
 }
 
 /* ------------------------------------------------------------------------
@@ -252,7 +316,7 @@ int oracle_decode_relpos_f64(double* out, const void* q, const void* k_cache, co
                                           max_distance)];
       attend_row(out + bh * head_dim, q, bh * head_dim, k_cache, v_cache,
                  block_tables + (int64_t)b * max_blocks_per_seq, a, L - 1, L, sliding_window, 0,
-                 scale, h, num_heads, head_dim, block_size, dtype, s);
+                 0, scale, h, num_heads, head_dim, block_size, dtype, s);
     }
     free(s);
     free(a);
@@ -300,7 +364,7 @@ int oracle_prefill_relpos_f64(double* out, const void* q, const void* k_cache,
         int64_t row = ((int64_t)(q0 + t) * num_heads + h) * head_dim;
         attend_row(out + row, q, row, k_cache, v_cache,
                    block_tables + (int64_t)b * max_blocks_per_seq, a, p, L, sliding_window,
-                   causal, scale, h, num_heads, head_dim, block_size, dtype, s);
+                   causal, 0, scale, h, num_heads, head_dim, block_size, dtype, s);
       }
     }
     free(s);
@@ -338,7 +402,7 @@ int oracle_decode_ragged_f64(double* out, const void* q, const void* k_cache, co
       const float* bias_row = bias + bias_start[b] + (int64_t)h * L;
       attend_row(out + bh * head_dim, q, bh * head_dim, k_cache, v_cache,
                  block_tables + (int64_t)b * max_blocks_per_seq, bias_row, L - 1, L,
-                 sliding_window, 0, scale, h, num_heads, head_dim, block_size, dtype, s);
+                 sliding_window, 0, 0, scale, h, num_heads, head_dim, block_size, dtype, s);
     }
     free(s);
   }
@@ -377,7 +441,8 @@ int oracle_prefill_ragged_f64(double* out, const void* q, const void* k_cache, c
         const float* bias_row = bias + bias_start[b] + ((int64_t)h * nq + t) * L;
         attend_row(out + row, q, row, k_cache, v_cache,
                    block_tables + (int64_t)b * max_blocks_per_seq, bias_row, p, L,
-                   sliding_window, causal, scale, h, num_heads, head_dim, block_size, dtype, s);
+                   sliding_window, causal, 0, scale, h, num_heads, head_dim, block_size, dtype,
+                   s);
       }
     }
     free(s);

@@ -72,6 +72,25 @@ int oracle_prefill_f64(double* out, const void* q, const void* k_cache, const vo
                        int32_t block_size, int32_t max_blocks_per_seq, int32_t max_seq_len,
                        int32_t dtype);
 
+/* Chunked local attention: as above with no window, but a query at position
+ * p sees only keys j with floor(j / chunk_size) = floor(p / chunk_size) (and,
+ * for a causal query, j <= p). chunk_size >= 1. Parity unpinned for this
+ * reading: the page that names the layer type gives no formula. */
+int oracle_decode_chunked_f64(double* out, const void* q, const void* k_cache,
+                              const void* v_cache, const int32_t* block_tables,
+                              const int32_t* context_lens, const float* attn_bias,
+                              int32_t chunk_size, double scale, int32_t num_seqs,
+                              int32_t num_heads, int32_t head_dim, int32_t block_size,
+                              int32_t max_blocks_per_seq, int32_t max_seq_len, int32_t dtype);
+int oracle_prefill_chunked_f64(double* out, const void* q, const void* k_cache,
+                               const void* v_cache, const int32_t* block_tables,
+                               const int32_t* context_lens, const int32_t* query_start_loc,
+                               const float* attn_bias, int32_t chunk_size, int32_t causal,
+                               double scale, int32_t num_seqs, int32_t num_heads,
+                               int32_t head_dim, int32_t block_size,
+                               int32_t max_blocks_per_seq, int32_t max_seq_len,
+                               int32_t dtype);
+
 /* T5 relative-position bucket of relative_position = key - query position
  * (see oracle.c for the definition); bidirectional 0 (decoder) or 1
  * (encoder). The array form fills out[i] for relative_position[i]. */

@@ -554,3 +554,149 @@ def test_thread_count_does_not_change_results():
         oracle.set_num_threads(n)
     assert oracle.num_threads() == n
     np.testing.assert_array_equal(one, ref)
+
+
+# ----------------------------------------------------------------------------
+# chunked local attention ("[V1] Add sliding window support to Flex Attention
+# backend", attention-groups thread: Llama 4's chunked-local layers). Reading:
+# a query sees the keys of its own chunk of chunk_size positions (causal: up to
+# itself). The pins tie the oracle to that reading, not the reading to a page.
+# ----------------------------------------------------------------------------
+def chunk_mask(pos, L, chunk, causal):
+    """Additive mask [len(pos), L]: a block-diagonal matrix of all-ones chunks
+    (torch.block_diag), optionally intersected with the lower triangle."""
+    sizes = [min(chunk, L - s) for s in range(0, L, chunk)]
+    ok = torch.block_diag(*[torch.ones(n, n) for n in sizes]).bool()
+    if causal:
+        ok &= torch.tril(torch.ones(L, L, dtype=torch.bool))
+    ok = ok[torch.as_tensor(pos, dtype=torch.long)]
+    m = torch.zeros(ok.shape, dtype=torch.float64)
+    m[~ok] = float("-inf")
+    return m
+
+
+def sdpa_rows(case, b, pos, mask, bias_rows):
+    H = case.q.shape[1]
+    L = int(case.lens[b])
+    K = unpage(case.k_cache, case.block_tables[b], L)
+    V = unpage(case.v_cache, case.block_tables[b], L)
+    m = mask[None].expand(H, len(pos), L).clone()
+    if bias_rows is not None:
+        m = m + case.scale * bias_rows
+    return K, V, m
+
+
+def sdpa_decode_chunked(case, chunk):
+    B, H, D = case.q.shape
+    out = torch.zeros(B, H, D, dtype=torch.float64)
+    for b in range(B):
+        L = int(case.lens[b])
+        if L == 0:
+            continue
+        bias = None if case.attn_bias is None else case.attn_bias[b, :, :L].double()[:, None, :]
+        K, V, m = sdpa_rows(case, b, [L - 1], chunk_mask([L - 1], L, chunk, False), bias)
+        out[b] = F.scaled_dot_product_attention(case.q[b].double()[:, None, :], K, V,
+                                                attn_mask=m, scale=case.scale)[:, 0, :]
+    return out.numpy()
+
+
+def sdpa_prefill_chunked(case, chunk):
+    TQ, H, D = case.q.shape
+    out = torch.zeros(TQ, H, D, dtype=torch.float64)
+    qsl = case.query_start_loc
+    for b in range(case.num_seqs):
+        L = int(case.lens[b])
+        q0, q1 = int(qsl[b]), int(qsl[b + 1])
+        if q1 == q0:
+            continue
+        pos = list(range(L - (q1 - q0), L))
+        bias = None if case.attn_bias is None else case.attn_bias[b][:, pos, :L].double()
+        K, V, m = sdpa_rows(case, b, pos, chunk_mask(pos, L, chunk, case.causal), bias)
+        qb = case.q[q0:q1].double().permute(1, 0, 2)
+        out[q0:q1] = F.scaled_dot_product_attention(qb, K, V, attn_mask=m,
+                                                    scale=case.scale).permute(1, 0, 2)
+    return out.numpy()
+
+
+def run_decode_chunked(case, chunk, bias="case"):
+    return oracle.decode_chunked(case.q, case.k_cache, case.v_cache, case.block_tables,
+                                 case.context_lens, case.attn_bias if bias == "case" else bias,
+                                 chunk, case.scale, case.max_seq_len)
+
+
+def run_prefill_chunked(case, chunk, bias="case"):
+    return oracle.prefill_chunked(case.q, case.k_cache, case.v_cache, case.block_tables,
+                                  case.context_lens, case.query_start_loc,
+                                  case.attn_bias if bias == "case" else bias, chunk,
+                                  int(case.causal), case.scale, case.max_seq_len)
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+@pytest.mark.parametrize("bias", ["normal", None])
+@pytest.mark.parametrize("chunk", [1, 5, 16, 17, 64])
+def test_decode_chunked_equals_sdpa(dtype, bias, chunk):
+    case = small_decode(2100 + chunk, dtype=dtype, bias=bias, B=6)
+    np.testing.assert_allclose(run_decode_chunked(case, chunk), sdpa_decode_chunked(case, chunk),
+                               rtol=0, atol=1e-12)
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("chunk", [1, 3, 8, 16, 33])
+@pytest.mark.parametrize("partial", [False, True])
+def test_prefill_chunked_equals_sdpa(dtype, causal, chunk, partial):
+    case = small_prefill(2200 + chunk, dtype=dtype, causal=causal,
+                         lens=[5, 21, 40] if partial else (1, 40),
+                         q_lens=[1, 7, 20] if partial else None)
+    np.testing.assert_allclose(run_prefill_chunked(case, chunk),
+                               sdpa_prefill_chunked(case, chunk), rtol=0, atol=1e-12)
+
+
+def test_chunk_covering_the_sequence_equals_full_attention_bit_exact():
+    d = small_decode(2300)
+    assert np.array_equal(run_decode_chunked(d, 1000), run_decode(d, window=-1))
+    for causal in (False, True):
+        p = small_prefill(2301, causal=causal)
+        assert np.array_equal(run_prefill_chunked(p, 1000), run_prefill(p, window=-1))
+
+
+def test_chunk_one_returns_own_value():
+    """A chunk of one position holds only the query's own key: out = v_p
+    exactly, whatever the bias and scale."""
+    d = small_decode(2310, lens=(1, 40))
+    out = run_decode_chunked(d, 1)
+    for b in range(d.q.shape[0]):
+        L = int(d.lens[b])
+        v = unpage(d.v_cache, d.block_tables[b], L)[:, L - 1, :]
+        assert np.array_equal(out[b], v.numpy())
+    p = small_prefill(2311)
+    outp = run_prefill_chunked(p, 1)
+    for b in range(p.num_seqs):
+        L = int(p.lens[b])
+        q0 = int(p.query_start_loc[b])
+        v = unpage(p.v_cache, p.block_tables[b], L)
+        for t in range(L):
+            assert np.array_equal(outp[q0 + t], v[:, t, :].numpy())
+
+
+@pytest.mark.parametrize("chunk", [3, 16, 21])
+def test_decode_chunked_equals_window_over_the_chunks_tail_bit_exact(chunk):
+    """The decode query sits at L-1, so its chunk's visible keys are the last
+    ((L-1) mod C) + 1 tokens: the same key set, in the same order, as a window
+    of that size."""
+    case = small_decode(2320 + chunk, B=6)
+    out = run_decode_chunked(case, chunk)
+    for b in range(6):
+        L = int(case.lens[b])
+        w = (L - 1) % chunk + 1
+        assert np.array_equal(out[b], run_decode(case, window=w)[b])
+
+
+def test_oracle_rejects_non_positive_chunks():
+    d = small_decode(2330)
+    p = small_prefill(2331)
+    for c in (0, -1):
+        with pytest.raises(ValueError):
+            run_decode_chunked(d, c)
+        with pytest.raises(ValueError):
+            run_prefill_chunked(p, c)
