@@ -252,6 +252,48 @@ pa_status_t paged_attn_prefill_ragged_bias(void* out, const void* q, const void*
                                            int64_t total_q, pa_dtype_t dtype, void* stream);
 
 /*
+ * Chunked local attention ("[V1] Add sliding window support to Flex Attention
+ * backend", the attention-groups thread: Llama 4 alternates full-attention
+ * layers with chunked-local-attention layers, a mask family beside the
+ * sliding window). The page names the layer type only; these entry points
+ * take its plain reading: positions are cut into consecutive chunks of
+ * chunk_size tokens (chunk c holds positions c*chunk_size ..
+ * c*chunk_size + chunk_size - 1), and a query at position p sees exactly the
+ * keys of its own chunk, floor(j / chunk_size) == floor(p / chunk_size); a
+ * causal prefill query also needs j <= p. The decode query (position L-1)
+ * therefore sees keys chunk_size * floor((L-1) / chunk_size) .. L-1; blocks
+ * before that chunk are never read.
+ *
+ * Arguments are those of paged_attn_decode / paged_attn_prefill with
+ * chunk_size (>= 1, else PA_ERR_INVALID_ARG) in place of sliding_window; there
+ * is no window. The optional attn_bias is the padded materialised bias of the
+ * base entry points. The decode workspace is sized by
+ * pa_decode_workspace_bytes with sliding_window = chunk_size (a chunk spans
+ * at most as many tokens as a window of that size). With PA_VALIDATE=1 the
+ * block-table entries from the first query's chunk onwards are checked.
+ */
+pa_status_t paged_attn_decode_chunked(void* out, const void* q, const void* k_cache,
+                                      const void* v_cache, const int32_t* block_tables,
+                                      const int32_t* context_lens, const float* attn_bias,
+                                      int32_t chunk_size, float scale, int32_t num_seqs,
+                                      int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
+                                      int32_t block_size, int32_t max_blocks_per_seq,
+                                      int32_t max_seq_len, int64_t num_blocks, pa_dtype_t dtype,
+                                      int32_t partition_tokens, void* workspace,
+                                      size_t workspace_bytes, void* stream);
+
+pa_status_t paged_attn_prefill_chunked(void* out, const void* q, const void* k_cache,
+                                       const void* v_cache, const int32_t* block_tables,
+                                       const int32_t* context_lens,
+                                       const int32_t* query_start_loc, const float* attn_bias,
+                                       int32_t chunk_size, int32_t causal, float scale,
+                                       int32_t num_seqs, int32_t num_heads,
+                                       int32_t num_kv_heads, int32_t head_dim,
+                                       int32_t block_size, int32_t max_blocks_per_seq,
+                                       int32_t max_seq_len, int64_t num_blocks, int64_t total_q,
+                                       pa_dtype_t dtype, void* stream);
+
+/*
  * KV-cache write, the step that precedes decode: token t's keys and values
  * (all heads) are stored at physical slot slot_mapping[t] = block * 16 +
  * offset of the paged caches (layout above; the block tables themselves are

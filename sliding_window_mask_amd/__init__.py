@@ -137,6 +137,10 @@ class PagedAttnLib:
         lib.paged_attn_prefill.restype = ctypes.c_int
         lib.paged_attn_prefill.argtypes = [P, P, P, P, P, P, P, P, I32, I32, F32, I32, I32,
                                            I32, I32, I32, I32, I32, I64, I64, ctypes.c_int, P]
+        lib.paged_attn_decode_chunked.restype = ctypes.c_int
+        lib.paged_attn_decode_chunked.argtypes = lib.paged_attn_decode.argtypes
+        lib.paged_attn_prefill_chunked.restype = ctypes.c_int
+        lib.paged_attn_prefill_chunked.argtypes = lib.paged_attn_prefill.argtypes
         lib.paged_attn_decode_relpos.restype = ctypes.c_int
         lib.paged_attn_decode_relpos.argtypes = [P, P, P, P, P, P, P, I32, I32, I32, I32, F32,
                                                  I32, I32, I32, I32, I32, I32, I32, I64,
@@ -215,6 +219,24 @@ class PagedAttnLib:
         k_cache, v_cache [num_blocks,H,16,D]; block_tables int32 [B,max_blocks];
         context_lens int32 [B]; attn_bias fp32 [B,H,max_seq_len] or None.
         Cross-attention: pass the encoder table and lengths, sliding_window -1."""
+        return self._decode(self._lib.paged_attn_decode, q, k_cache, v_cache, block_tables,
+                            context_lens, attn_bias, sliding_window, scale, max_seq_len, out,
+                            workspace, partition_tokens, stream)
+
+    def paged_attn_decode_chunked(self, q, k_cache, v_cache, block_tables, context_lens,
+                                  attn_bias, chunk_size, scale, *, max_seq_len, out=None,
+                                  workspace=None, partition_tokens=0, stream=None):
+        """Decode with chunked local attention: the query (position L-1) sees
+        the keys of its chunk of chunk_size positions. Otherwise as
+        paged_attn_decode (no window)."""
+        return self._decode(self._lib.paged_attn_decode_chunked, q, k_cache, v_cache,
+                            block_tables, context_lens, attn_bias, chunk_size, scale,
+                            max_seq_len, out, workspace, partition_tokens, stream)
+
+    def _decode(self, fn, q, k_cache, v_cache, block_tables, context_lens, attn_bias, band,
+                scale, max_seq_len, out, workspace, partition_tokens, stream):
+        # band: the sliding window, or the chunk size of the chunked entry point
+        # (which bounds the workspace like a window of that size)
         _tensor(q, "q", None, _FLOAT_DTYPES, ndim=3)
         B, H, D = q.shape
         if out is None:
@@ -223,13 +245,13 @@ class PagedAttnLib:
         if attn_bias is not None:
             _tensor(attn_bias, "attn_bias", dev, (torch.float32,), shape=(B, H, max_seq_len))
         if workspace is None:
-            workspace = self.workspace_for(q, max_seq_len, sliding_window, partition_tokens)
+            workspace = self.workspace_for(q, max_seq_len, band, partition_tokens)
         else:
             _tensor(workspace, "workspace", dev, ndim=1)
         ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-        self._check(self._lib.paged_attn_decode(
+        self._check(fn(
             _ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables),
-            _ptr(context_lens), _ptr(attn_bias), int(sliding_window), float(scale), B, H,
+            _ptr(context_lens), _ptr(attn_bias), int(band), float(scale), B, H,
             k_cache.shape[1], D, k_cache.shape[2], block_tables.shape[1], int(max_seq_len),
             k_cache.shape[0], _dtype_code(q), int(partition_tokens), _ptr(workspace), ws_bytes,
             _stream(stream)))
@@ -242,6 +264,22 @@ class PagedAttnLib:
 
         query_start_loc int32 [B+1]; attn_bias fp32 [B,H,max_seq_len,max_seq_len]
         or None; causal False for encoder-only bidirectional attention."""
+        return self._prefill(self._lib.paged_attn_prefill, q, k_cache, v_cache, block_tables,
+                             context_lens, query_start_loc, attn_bias, sliding_window, causal,
+                             scale, max_seq_len, out, stream)
+
+    def paged_attn_prefill_chunked(self, q, k_cache, v_cache, block_tables, context_lens,
+                                   query_start_loc, attn_bias, chunk_size, causal, scale, *,
+                                   max_seq_len, out=None, stream=None):
+        """Prefill with chunked local attention: a query at position p sees the
+        keys of its chunk (floor(j / chunk_size) == floor(p / chunk_size)), and
+        with causal only those up to p. Otherwise as paged_attn_prefill."""
+        return self._prefill(self._lib.paged_attn_prefill_chunked, q, k_cache, v_cache,
+                             block_tables, context_lens, query_start_loc, attn_bias,
+                             chunk_size, causal, scale, max_seq_len, out, stream)
+
+    def _prefill(self, fn, q, k_cache, v_cache, block_tables, context_lens, query_start_loc,
+                 attn_bias, band, causal, scale, max_seq_len, out, stream):
         _tensor(q, "q", None, _FLOAT_DTYPES, ndim=3)
         TQ, H, D = q.shape
         if out is None:
@@ -252,9 +290,9 @@ class PagedAttnLib:
         if attn_bias is not None:
             _tensor(attn_bias, "attn_bias", dev, (torch.float32,),
                     shape=(B, H, max_seq_len, max_seq_len))
-        self._check(self._lib.paged_attn_prefill(
+        self._check(fn(
             _ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables),
-            _ptr(context_lens), _ptr(query_start_loc), _ptr(attn_bias), int(sliding_window),
+            _ptr(context_lens), _ptr(query_start_loc), _ptr(attn_bias), int(band),
             int(bool(causal)), float(scale), context_lens.shape[0], H, k_cache.shape[1], D,
             k_cache.shape[2], block_tables.shape[1], int(max_seq_len), k_cache.shape[0], TQ,
             _dtype_code(q), _stream(stream)))
@@ -391,6 +429,14 @@ def paged_attn_decode(*args, **kwargs):
 
 def paged_attn_prefill(*args, **kwargs):
     return lib().paged_attn_prefill(*args, **kwargs)
+
+
+def paged_attn_decode_chunked(*args, **kwargs):
+    return lib().paged_attn_decode_chunked(*args, **kwargs)
+
+
+def paged_attn_prefill_chunked(*args, **kwargs):
+    return lib().paged_attn_prefill_chunked(*args, **kwargs)
 
 
 def paged_attn_decode_relpos(*args, **kwargs):

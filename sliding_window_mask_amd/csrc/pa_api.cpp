@@ -185,15 +185,62 @@ pa_status_t make_relpos(const float* table, int32_t num_buckets, int32_t max_dis
   return PA_OK;
 }
 
+// Host check of the metadata a call would read (pa_check_metadata, and the
+// PA_VALIDATE path with chunked local attention as well): lengths, query
+// offsets, and the block-table entries of every block a query can see.
+pa_status_t check_metadata_impl(const int32_t* block_tables, const int32_t* context_lens,
+                                const int32_t* query_start_loc, int32_t sliding_window,
+                                int32_t chunk, int32_t causal, int32_t num_seqs,
+                                int32_t max_blocks_per_seq, int32_t max_seq_len,
+                                int64_t num_blocks, int64_t total_q) {
+  (void)causal;
+  if (num_seqs < 0) return fail(PA_ERR_INVALID_ARG, "num_seqs < 0");
+  if (num_seqs > 0 && (!context_lens || (max_blocks_per_seq > 0 && !block_tables)))
+    return fail(PA_ERR_NULL_POINTER, "metadata pointer is NULL");
+  if (query_start_loc) {
+    if (query_start_loc[0] != 0)
+      return fail(PA_ERR_INVALID_ARG, "query_start_loc[0] = %d, expected 0", query_start_loc[0]);
+    if (query_start_loc[num_seqs] != total_q)
+      return fail(PA_ERR_INVALID_ARG, "query_start_loc[%d] = %d, expected total_q = %lld",
+                  num_seqs, query_start_loc[num_seqs], (long long)total_q);
+  }
+  for (int32_t b = 0; b < num_seqs; ++b) {
+    const int32_t L = context_lens[b];
+    if (L < 0 || L > max_seq_len)
+      return fail(PA_ERR_INVALID_ARG, "context_lens[%d] = %d outside [0, %d]", b, L, max_seq_len);
+    int32_t first_pos = L - 1;   // decode: the one query
+    if (query_start_loc) {
+      const int32_t nq = query_start_loc[b + 1] - query_start_loc[b];
+      if (nq < 0 || nq > L)
+        return fail(PA_ERR_INVALID_ARG, "sequence %d has %d queries for %d keys", b, nq, L);
+      if (nq == 0) continue;
+      first_pos = L - nq;
+    }
+    if (L == 0) continue;
+    int32_t lo = 0;
+    if (sliding_window > 0 && first_pos - sliding_window + 1 > 0)
+      lo = first_pos - sliding_window + 1;
+    if (chunk > 0) lo = first_pos / chunk * chunk;   // the first query's chunk
+    for (int32_t n = lo / pa::kBlockSize; n < (L + pa::kBlockSize - 1) / pa::kBlockSize; ++n) {
+      const int32_t id = block_tables[(int64_t)b * max_blocks_per_seq + n];
+      if (id < 0 || id >= num_blocks)
+        return fail(PA_ERR_INVALID_ARG, "block_tables[%d][%d] = %d outside [0, %lld)", b, n, id,
+                    (long long)num_blocks);
+    }
+  }
+  return ok();
+}
+
+
 bool validate_env() {
   const char* e = std::getenv("PA_VALIDATE");
   return e && e[0] && std::strcmp(e, "0") != 0;
 }
 
 pa_status_t validate_device(const int32_t* bt, const int32_t* cl, const int32_t* qsl,
-                            int32_t window, int32_t causal, int32_t num_seqs, int32_t max_blocks,
-                            int32_t max_seq_len, int64_t num_blocks, int64_t total_q,
-                            hipStream_t stream) {
+                            int32_t window, int32_t chunk, int32_t causal, int32_t num_seqs,
+                            int32_t max_blocks, int32_t max_seq_len, int64_t num_blocks,
+                            int64_t total_q, hipStream_t stream) {
   std::vector<int32_t> hbt((size_t)num_seqs * max_blocks), hcl(num_seqs), hqsl;
   hipError_t e = hipMemcpyAsync(hcl.data(), cl, sizeof(int32_t) * num_seqs,
                                 hipMemcpyDeviceToHost, stream);
@@ -208,8 +255,8 @@ pa_status_t validate_device(const int32_t* bt, const int32_t* cl, const int32_t*
   if (e == hipSuccess) e = hipStreamSynchronize(stream);
   if (e != hipSuccess)
     return fail(PA_ERR_HIP, "PA_VALIDATE copy failed: %s", hipGetErrorString(e));
-  return pa_check_metadata(hbt.data(), hcl.data(), qsl ? hqsl.data() : nullptr, window, causal,
-                           num_seqs, max_blocks, max_seq_len, num_blocks, total_q);
+  return check_metadata_impl(hbt.data(), hcl.data(), qsl ? hqsl.data() : nullptr, window, chunk,
+                             causal, num_seqs, max_blocks, max_seq_len, num_blocks, total_q);
 }
 
 }  // namespace
@@ -245,41 +292,9 @@ pa_status_t pa_check_metadata(const int32_t* block_tables, const int32_t* contex
                               const int32_t* query_start_loc, int32_t sliding_window,
                               int32_t causal, int32_t num_seqs, int32_t max_blocks_per_seq,
                               int32_t max_seq_len, int64_t num_blocks, int64_t total_q) {
-  (void)causal;
-  if (num_seqs < 0) return fail(PA_ERR_INVALID_ARG, "num_seqs < 0");
-  if (num_seqs > 0 && (!context_lens || (max_blocks_per_seq > 0 && !block_tables)))
-    return fail(PA_ERR_NULL_POINTER, "metadata pointer is NULL");
-  if (query_start_loc) {
-    if (query_start_loc[0] != 0)
-      return fail(PA_ERR_INVALID_ARG, "query_start_loc[0] = %d, expected 0", query_start_loc[0]);
-    if (query_start_loc[num_seqs] != total_q)
-      return fail(PA_ERR_INVALID_ARG, "query_start_loc[%d] = %d, expected total_q = %lld",
-                  num_seqs, query_start_loc[num_seqs], (long long)total_q);
-  }
-  for (int32_t b = 0; b < num_seqs; ++b) {
-    const int32_t L = context_lens[b];
-    if (L < 0 || L > max_seq_len)
-      return fail(PA_ERR_INVALID_ARG, "context_lens[%d] = %d outside [0, %d]", b, L, max_seq_len);
-    int32_t first_pos = L - 1;   // decode: the one query
-    if (query_start_loc) {
-      const int32_t nq = query_start_loc[b + 1] - query_start_loc[b];
-      if (nq < 0 || nq > L)
-        return fail(PA_ERR_INVALID_ARG, "sequence %d has %d queries for %d keys", b, nq, L);
-      if (nq == 0) continue;
-      first_pos = L - nq;
-    }
-    if (L == 0) continue;
-    int32_t lo = 0;
-    if (sliding_window > 0 && first_pos - sliding_window + 1 > 0)
-      lo = first_pos - sliding_window + 1;
-    for (int32_t n = lo / pa::kBlockSize; n < (L + pa::kBlockSize - 1) / pa::kBlockSize; ++n) {
-      const int32_t id = block_tables[(int64_t)b * max_blocks_per_seq + n];
-      if (id < 0 || id >= num_blocks)
-        return fail(PA_ERR_INVALID_ARG, "block_tables[%d][%d] = %d outside [0, %lld)", b, n, id,
-                    (long long)num_blocks);
-    }
-  }
-  return ok();
+  return check_metadata_impl(block_tables, context_lens, query_start_loc, sliding_window, 0,
+                             causal, num_seqs, max_blocks_per_seq, max_seq_len, num_blocks,
+                             total_q);
 }
 
 }  // extern "C"
@@ -294,7 +309,7 @@ pa_status_t decode_impl(void* out, const void* q, const void* k_cache, const voi
                         int32_t head_dim, int32_t block_size, int32_t max_blocks_per_seq,
                         int32_t max_seq_len, int64_t num_blocks, pa_dtype_t dtype,
                         int32_t partition_tokens, void* workspace, size_t workspace_bytes,
-                        void* stream) {
+                        void* stream, int32_t chunk = 0) {
   pa_status_t st = check_common(out, q, k_cache, v_cache, block_tables, context_lens, attn_bias,
                                 sliding_window, scale, num_seqs, num_heads, num_kv_heads,
                                 head_dim, block_size, max_blocks_per_seq, max_seq_len,
@@ -309,8 +324,9 @@ pa_status_t decode_impl(void* out, const void* q, const void* k_cache, const voi
     return fail(PA_ERR_INVALID_ARG, "partition_tokens %d: use 0 or a multiple of 16 in "
                 "[16, %d]", partition_tokens, pa::kMaxPartition);
   if (num_seqs == 0) return ok();
+  // a chunk bounds the visible span like a window of the chunk's size
   const DecodePlan plan = plan_decode(num_seqs, num_heads, head_dim, max_seq_len,
-                                      sliding_window, partition_tokens);
+                                      chunk > 0 ? chunk : sliding_window, partition_tokens);
   if (plan.num_partitions > 65535)
     return fail(PA_ERR_INVALID_ARG, "too many partitions (%d)", plan.num_partitions);
   if (plan.ws_bytes > 0) {
@@ -322,7 +338,7 @@ pa_status_t decode_impl(void* out, const void* q, const void* k_cache, const voi
   }
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (validate_env()) {
-    st = validate_device(block_tables, context_lens, nullptr, sliding_window, 0, num_seqs,
+    st = validate_device(block_tables, context_lens, nullptr, sliding_window, chunk, 0, num_seqs,
                          max_blocks_per_seq, max_seq_len, num_blocks, 0, s);
     if (st != PA_OK) return st;
   }
@@ -336,6 +352,7 @@ pa_status_t decode_impl(void* out, const void* q, const void* k_cache, const voi
   a.attn_bias = attn_bias;
   a.bias_start = bias_start;
   a.window = sliding_window;
+  a.chunk = chunk;
   a.scale_log2 = (float)((double)scale * 1.4426950408889634074);
   a.num_seqs = num_seqs;
   a.num_heads = num_heads;
@@ -365,7 +382,7 @@ pa_status_t prefill_impl(void* out, const void* q, const void* k_cache, const vo
                          float scale, int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
                          int32_t head_dim, int32_t block_size, int32_t max_blocks_per_seq,
                          int32_t max_seq_len, int64_t num_blocks, int64_t total_q,
-                         pa_dtype_t dtype, void* stream) {
+                         pa_dtype_t dtype, void* stream, int32_t chunk = 0) {
   if (num_seqs < 0 || num_seqs > 65535)
     return fail(PA_ERR_INVALID_ARG, "num_seqs %d out of range [0, 65535]", num_seqs);
   if (total_q < 0 || total_q > INT32_MAX)
@@ -384,8 +401,9 @@ pa_status_t prefill_impl(void* out, const void* q, const void* k_cache, const vo
     return fail(PA_ERR_MISALIGNED, "query_start_loc must be 4-byte aligned");
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (validate_env()) {
-    st = validate_device(block_tables, context_lens, query_start_loc, sliding_window, causal,
-                         num_seqs, max_blocks_per_seq, max_seq_len, num_blocks, total_q, s);
+    st = validate_device(block_tables, context_lens, query_start_loc, sliding_window, chunk,
+                         causal, num_seqs, max_blocks_per_seq, max_seq_len, num_blocks, total_q,
+                         s);
     if (st != PA_OK) return st;
   }
   if (total_q == 0 || max_seq_len == 0) return ok();
@@ -400,6 +418,7 @@ pa_status_t prefill_impl(void* out, const void* q, const void* k_cache, const vo
   a.attn_bias = attn_bias;
   a.bias_start = bias_start;
   a.window = sliding_window;
+  a.chunk = chunk;
   a.causal = causal;
   a.scale_log2 = (float)((double)scale * 1.4426950408889634074);
   a.num_seqs = num_seqs;
@@ -530,6 +549,39 @@ pa_status_t paged_attn_prefill_ragged_bias(void* out, const void* q, const void*
                       attn_bias, bias_start, nullptr, sliding_window, causal, scale, num_seqs,
                       num_heads, num_kv_heads, head_dim, block_size, max_blocks_per_seq,
                       max_seq_len, num_blocks, total_q, dtype, stream);
+}
+
+pa_status_t paged_attn_decode_chunked(void* out, const void* q, const void* k_cache,
+                                      const void* v_cache, const int32_t* block_tables,
+                                      const int32_t* context_lens, const float* attn_bias,
+                                      int32_t chunk_size, float scale, int32_t num_seqs,
+                                      int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
+                                      int32_t block_size, int32_t max_blocks_per_seq,
+                                      int32_t max_seq_len, int64_t num_blocks, pa_dtype_t dtype,
+                                      int32_t partition_tokens, void* workspace,
+                                      size_t workspace_bytes, void* stream) {
+  if (chunk_size < 1) return fail(PA_ERR_INVALID_ARG, "chunk_size %d: must be >= 1", chunk_size);
+  return decode_impl(out, q, k_cache, v_cache, block_tables, context_lens, attn_bias, nullptr,
+                     nullptr, -1, scale, num_seqs, num_heads, num_kv_heads, head_dim, block_size,
+                     max_blocks_per_seq, max_seq_len, num_blocks, dtype, partition_tokens,
+                     workspace, workspace_bytes, stream, chunk_size);
+}
+
+pa_status_t paged_attn_prefill_chunked(void* out, const void* q, const void* k_cache,
+                                       const void* v_cache, const int32_t* block_tables,
+                                       const int32_t* context_lens,
+                                       const int32_t* query_start_loc, const float* attn_bias,
+                                       int32_t chunk_size, int32_t causal, float scale,
+                                       int32_t num_seqs, int32_t num_heads,
+                                       int32_t num_kv_heads, int32_t head_dim,
+                                       int32_t block_size, int32_t max_blocks_per_seq,
+                                       int32_t max_seq_len, int64_t num_blocks, int64_t total_q,
+                                       pa_dtype_t dtype, void* stream) {
+  if (chunk_size < 1) return fail(PA_ERR_INVALID_ARG, "chunk_size %d: must be >= 1", chunk_size);
+  return prefill_impl(out, q, k_cache, v_cache, block_tables, context_lens, query_start_loc,
+                      attn_bias, nullptr, nullptr, -1, causal, scale, num_seqs, num_heads,
+                      num_kv_heads, head_dim, block_size, max_blocks_per_seq, max_seq_len,
+                      num_blocks, total_q, dtype, stream, chunk_size);
 }
 
 int32_t pa_window_first_live_block(int32_t context_len, int32_t sliding_window) {

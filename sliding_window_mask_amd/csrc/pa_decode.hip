@@ -53,6 +53,14 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
   return (uint16_t)(u >> 16);
 }
 
+// First key the decode query (position L - 1) may see: the first of the W
+// newest tokens with a window, the start of the query's chunk with chunked
+// local attention, else 0.
+__device__ __forceinline__ int decode_first_key(const DecodeArgs& a, int L) {
+  if (a.chunk > 0) return L > 0 ? (L - 1) / a.chunk * a.chunk : 0;
+  return (a.window > 0 && L > a.window) ? L - a.window : 0;
+}
+
 template <int CTRL>
 __device__ __forceinline__ float dpp(float v) {
   return __builtin_amdgcn_update_dpp(0.0f, v, CTRL, 0xf, 0xf, false);
@@ -192,7 +200,7 @@ pa_decode_partition(DecodeArgs a) {
   const int P = a.partition;
 
   const int L = a.context_lens[b];
-  const int lo = (a.window > 0 && L > a.window) ? L - a.window : 0;
+  const int lo = decode_first_key(a, L);
   const int start = lo & ~(kBlockSize - 1);
   const int t0 = start + part * P;                     // first token of partition
   if (L <= 0 || t0 >= L) {
@@ -410,7 +418,7 @@ __global__ void __launch_bounds__(D) pa_decode_merge(DecodeArgs a) {
   const int b = (int)(row / a.num_heads);
   const int tid = threadIdx.x;
   const int L = a.context_lens[b];
-  const int lo = (a.window > 0 && L > a.window) ? L - a.window : 0;
+  const int lo = decode_first_key(a, L);
   const int start = lo & ~(kBlockSize - 1);
   const int np = L > 0 ? (L - start + a.partition - 1) / a.partition : 0;
   const int64_t base = row * a.num_partitions;

@@ -44,6 +44,7 @@ struct DecodeArgs {
   const int64_t* bias_start;  // null: bias padded [B,H,max_seq_len]; else sequence b's
                               // rows [H][L_b] start at attn_bias + bias_start[b]
   int32_t window;             // -1 or >= 1
+  int32_t chunk;              // chunked local attention: chunk size >= 1, or 0 (window is -1)
   float scale_log2;           // scale * log2(e): scores are kept in base 2
   int32_t num_seqs, num_heads, head_dim, max_blocks, max_seq_len;
   int32_t dtype;              // 0 fp32, 1 bf16
@@ -67,6 +68,7 @@ struct PrefillArgs {
   const int64_t* bias_start;  // null: bias padded [B,H,MS,MS]; else sequence b's rows
                               // [H][n_q][L_b] start at attn_bias + bias_start[b]
   int32_t window;             // -1 or >= 1
+  int32_t chunk;              // chunked local attention: chunk size >= 1, or 0 (window is -1)
   int32_t causal;             // 0 or 1
   float scale_log2;
   int32_t num_seqs, num_heads, head_dim, max_blocks, max_seq_len;
@@ -77,14 +79,52 @@ struct PrefillArgs {
 
 // Visible key interval [lo, hi) for query positions [p0, p1] of a sequence
 // of length L (caller guarantees p0 <= p1 < L): all keys, keys up to the
-// last query for a causal prompt, and with a window W only |p - j| < W.
-__device__ __forceinline__ void prefill_key_range(int p0, int p1, int L, int window, int causal,
-                                                  int& lo, int& hi) {
+// last query for a causal prompt, with a window W only |p - j| < W, and with
+// chunked local attention of chunk size C only the keys of each query's
+// chunk, floor(j / C) = floor(p / C).
+__device__ __forceinline__ void prefill_key_range(int p0, int p1, int L, int window, int chunk,
+                                                  int causal, int& lo, int& hi) {
   lo = 0;
   hi = causal ? p1 + 1 : L;
   if (window > 0) {
     lo = max(0, p0 - window + 1);
     if (!causal) hi = min(L, p1 + window);
+  } else if (chunk > 0) {
+    lo = p0 / chunk * chunk;
+    if (!causal) hi = min(L, p1 / chunk * chunk + chunk);
+  }
+}
+
+// Masks of the windowed prefill path, for a query at position p of a
+// sequence of length L (key j, d = p - j): key j is visible iff
+// dlo < d < dhi. Window W: dhi = W and d > -W; chunk C: the key lies in p's
+// chunk [p - p % C, p - p % C + C), i.e. p % C - C < d < p % C + 1. Both
+// also need j < L (d > p - L), and causal queries j <= p (d > -1).
+__device__ __forceinline__ void prefill_row_bounds(int p, int L, int window, int chunk,
+                                                   bool causal, int& dlo, int& dhi) {
+  int lo = p - L;
+  if (causal) lo = max(lo, -1);
+  if (window > 0) {
+    lo = max(lo, -window);
+    dhi = window;
+  } else {
+    const int r = p % chunk;
+    lo = max(lo, r - chunk);
+    dhi = r + 1;
+  }
+  dlo = lo;
+}
+
+// Keys [wlo, whi) that every position in [p0, p1] may see under its window or
+// chunk (the sequence end and a causal limit are checked separately).
+__device__ __forceinline__ void prefill_common_keys(int p0, int p1, int window, int chunk,
+                                                    int& wlo, int& whi) {
+  if (window > 0) {
+    wlo = p1 - window + 1;
+    whi = p0 + window;
+  } else {
+    wlo = p1 / chunk * chunk;
+    whi = p0 / chunk * chunk + chunk;
   }
 }
 
@@ -107,7 +147,7 @@ constexpr int kRankMaxSeqs = 63;   // batches ranked by length inside the kernel
 // sequences by the distinct keys (L << 6) | (63 - j) (vector compares
 // against keys broadcast from LDS, four per read; needs max_seq_len < 2^25)
 // and hands its sequence's values to the other waves through LDS (one
-// barrier). Windowed launches (bounded work per workgroup) and larger
+// barrier). Windowed and chunked launches (bounded work per workgroup) and larger
 // batches keep index order.
 __device__ __forceinline__ bool prefill_work_of(int n, const PrefillArgs& a, int& b, int& h,
                                                 int& tile, int& L, int& q0, int& nq) {
@@ -119,7 +159,7 @@ __device__ __forceinline__ bool prefill_work_of(int n, const PrefillArgs& a, int
   if (pr >= B * H) return false;
   const int r = pr / H;   // rank of the sequence in dispatch order
   h = pr % H;
-  if (B <= kRankMaxSeqs && a.window <= 0 && a.max_seq_len < (1 << 25)) {
+  if (B <= kRankMaxSeqs && a.window <= 0 && a.chunk <= 0 && a.max_seq_len < (1 << 25)) {
     __shared__ int picked[4];
     __shared__ __attribute__((aligned(16))) unsigned keys[64];
     if (threadIdx.x < 64) {

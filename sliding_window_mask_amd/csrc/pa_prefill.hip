@@ -88,9 +88,12 @@ __device__ __forceinline__ float vmax(float x, float y) {
 
 // BIAS: 0 none, 1 materialised attn_bias[b, h, p, j], 2 T5 relative-position
 // bias from a bucket table (a.rel).
-template <int D, int NG, int BIAS, bool CAUSAL, bool WINDOW>
+// BAND: 0 no band, 1 sliding window, 2 chunked local attention (separate
+// variants so that the window's mask stays a compare against a uniform W).
+template <int D, int NG, int BIAS, bool CAUSAL, int BAND>
 __global__ void __launch_bounds__(kThreads)
 pa_prefill_f32(PrefillArgs a) {
+  constexpr bool WINDOW = BAND != 0;   // banded: window or chunks
   constexpr int kKTile = key_tile<D>();
   constexpr int kChunks = kKTile / 16;               // 16-key chunks per tile
   constexpr int kRow = D + kPad;                     // LDS row stride (floats)
@@ -120,19 +123,22 @@ pa_prefill_f32(PrefillArgs a) {
   // workgroup and wave query ranges (positions), clamped to valid rows
   const int wg_last = min(t_first + kQT, nq) - 1;
   int wg_lo, wg_hi;
-  prefill_key_range(pos0 + t_first, pos0 + wg_last, L, a.window, CAUSAL, wg_lo, wg_hi);
+  prefill_key_range(pos0 + t_first, pos0 + wg_last, L, a.window, a.chunk, CAUSAL, wg_lo,
+                    wg_hi);
   const int w_first = t_first + wave * kWaveRows;
   const bool wave_active = w_first < nq;
   int wv_lo = 0, wv_hi = 0;
   if (wave_active)
-    prefill_key_range(pos0 + w_first, pos0 + min(w_first + kWaveRows, nq) - 1, L, a.window, CAUSAL,
-              wv_lo, wv_hi);
+    prefill_key_range(pos0 + w_first, pos0 + min(w_first + kWaveRows, nq) - 1, L, a.window,
+                      a.chunk, CAUSAL, wv_lo, wv_hi);
 
   // per query group: first/last existing position, this lane's row. Masking
   // of partly visible chunks: with d = p - j for key j = c0 + 4g + r,
   // d = dq - c0 - r, and the key is visible iff dlo < d (j < L, causal
-  // j <= p, window p - j > -W) and, with a window, d < W.
-  int gp0[NG], gp1[NG], t[NG], p[NG], dq[NG], dlo[NG];
+  // j <= p, window p - j > -W, chunk start) and, with a window or chunks,
+  // d < dhi (window W, or the end of p's chunk). Keys [wlo, whi) are inside
+  // the window or chunk of every row of the group.
+  int gp0[NG], gp1[NG], t[NG], p[NG], dq[NG], dlo[NG], dhi[NG], wlo[NG], whi[NG];
   bool row_ok[NG];
 #pragma unroll
   for (int q = 0; q < NG; ++q) {
@@ -144,10 +150,16 @@ pa_prefill_f32(PrefillArgs a) {
     row_ok[q] = t[q] < nq;
     p[q] = pos0 + t[q];
     dq[q] = p[q] - 4 * g;
-    int lo = p[q] - L;
-    if constexpr (CAUSAL) lo = max(lo, -1);
-    if constexpr (WINDOW) lo = max(lo, -a.window);
-    dlo[q] = lo;
+    if constexpr (BAND == 1) {
+      dlo[q] = max(CAUSAL ? max(p[q] - L, -1) : p[q] - L, -a.window);
+      dhi[q] = wlo[q] = whi[q] = 0;
+    } else if constexpr (BAND == 2) {
+      prefill_row_bounds(p[q], L, a.window, a.chunk, CAUSAL, dlo[q], dhi[q]);
+      prefill_common_keys(gp0[q], gp1[q], a.window, a.chunk, wlo[q], whi[q]);
+    } else {
+      dlo[q] = CAUSAL ? max(p[q] - L, -1) : p[q] - L;
+      dhi[q] = wlo[q] = whi[q] = 0;
+    }
   }
 
   // Q operands: D/4 contiguous floats per lane, pre-multiplied by
@@ -380,15 +392,17 @@ pa_prefill_f32(PrefillArgs a) {
           // or past L, and their outputs are never stored.
           bool whole = c0 + 16 <= L;
           if constexpr (CAUSAL) whole = whole && c0 + 15 <= gp0[q];
-          if constexpr (WINDOW)
+          if constexpr (BAND == 1)
             whole = whole && gp1[q] - c0 < a.window && c0 + 15 - gp0[q] < a.window;
+          if constexpr (BAND == 2) whole = whole && c0 >= wlo[q] && c0 + 16 <= whi[q];
           if (!whole) {
             const int d0 = dq[q] - c0;
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
               const int d = d0 - r;
               bool vis = d > dlo[q];
-              if constexpr (WINDOW) vis = vis && d < a.window;
+              if constexpr (BAND == 1) vis = vis && d < a.window;
+              if constexpr (BAND == 2) vis = vis && d < dhi[q];
               s[q][ch][r] = vis ? s[q][ch][r] : -INFINITY;
             }
           }
@@ -485,23 +499,24 @@ pa_prefill_f32(PrefillArgs a) {
   }
 }
 
+template <int D, int NG, int BIAS, int BAND>
+void launch_band(const PrefillArgs& a, dim3 grid, hipStream_t stream) {
+  if (a.causal)
+    hipLaunchKernelGGL((pa_prefill_f32<D, NG, BIAS, true, BAND>), grid, dim3(kThreads), 0,
+                       stream, a);
+  else
+    hipLaunchKernelGGL((pa_prefill_f32<D, NG, BIAS, false, BAND>), grid, dim3(kThreads), 0,
+                       stream, a);
+}
+
 template <int D, int NG, int BIAS>
 void launch_mask(const PrefillArgs& a, dim3 grid, hipStream_t stream) {
-  if (a.causal) {
-    if (a.window > 0)
-      hipLaunchKernelGGL((pa_prefill_f32<D, NG, BIAS, true, true>), grid, dim3(kThreads), 0,
-                         stream, a);
-    else
-      hipLaunchKernelGGL((pa_prefill_f32<D, NG, BIAS, true, false>), grid, dim3(kThreads),
-                         0, stream, a);
-  } else {
-    if (a.window > 0)
-      hipLaunchKernelGGL((pa_prefill_f32<D, NG, BIAS, false, true>), grid, dim3(kThreads),
-                         0, stream, a);
-    else
-      hipLaunchKernelGGL((pa_prefill_f32<D, NG, BIAS, false, false>), grid, dim3(kThreads),
-                         0, stream, a);
-  }
+  if (a.window > 0)
+    launch_band<D, NG, BIAS, 1>(a, grid, stream);
+  else if (a.chunk > 0)
+    launch_band<D, NG, BIAS, 2>(a, grid, stream);
+  else
+    launch_band<D, NG, BIAS, 0>(a, grid, stream);
 }
 
 template <int D, int NG>

@@ -119,13 +119,14 @@ pa_prefill_bf16(PrefillArgs a) {
 
   const int wg_last = min(t_first + kQT, nq) - 1;
   int wg_lo, wg_hi;
-  prefill_key_range(pos0 + t_first, pos0 + wg_last, L, a.window, CAUSAL, wg_lo, wg_hi);
+  prefill_key_range(pos0 + t_first, pos0 + wg_last, L, a.window, a.chunk, CAUSAL, wg_lo,
+                    wg_hi);
   const int w_first = t_first + wave * 16 * kSub;
   const bool wave_active = w_first < nq;
   int wv_lo = 0, wv_hi = 0;
   if (wave_active)
     prefill_key_range(pos0 + w_first, pos0 + min(w_first + 16 * kSub, nq) - 1, L, a.window,
-                      CAUSAL, wv_lo, wv_hi);
+                      a.chunk, CAUSAL, wv_lo, wv_hi);
 
   // exponent multiplier (> 0) and the sign the unscaled scores carry
   const float cs = a.scale_log2 == 0.0f ? 1.0f : fabsf(a.scale_log2);
@@ -135,8 +136,11 @@ pa_prefill_bf16(PrefillArgs a) {
   // sub-tile's first / last existing position (uniform). Masking of partly
   // visible chunks: with d = p - j for key j = c0 + 4g + r, d = dq - c0 - r,
   // and the key is visible iff dlo < d (j < L, causal j <= p, window
-  // p - j > -W) and, with a window, d < W.
-  int t_row[kSub], p_row[kSub], sp0[kSub], sp1[kSub], dq[kSub], dlo[kSub];
+  // p - j > -W, chunk start) and, with a window or chunks, d < dhi (window
+  // W, or the end of p's chunk). Keys [wlo, whi) are inside the window or
+  // chunk of every row of the sub-tile.
+  int t_row[kSub], p_row[kSub], sp0[kSub], sp1[kSub], dq[kSub], dlo[kSub], dhi[kSub];
+  int wlo[kSub], whi[kSub];
   bool row_ok[kSub];
 #pragma unroll
   for (int sb = 0; sb < kSub; ++sb) {
@@ -147,10 +151,13 @@ pa_prefill_bf16(PrefillArgs a) {
     sp0[sb] = pos0 + f;
     sp1[sb] = pos0 + min(f + 15, nq - 1);
     dq[sb] = p_row[sb] - 4 * g;
-    int lo = p_row[sb] - L;
-    if constexpr (CAUSAL) lo = max(lo, -1);
-    if constexpr (WINDOW) lo = max(lo, -a.window);
-    dlo[sb] = lo;
+    if constexpr (WINDOW) {
+      prefill_row_bounds(p_row[sb], L, a.window, a.chunk, CAUSAL, dlo[sb], dhi[sb]);
+      prefill_common_keys(sp0[sb], sp1[sb], a.window, a.chunk, wlo[sb], whi[sb]);
+    } else {
+      dlo[sb] = CAUSAL ? max(p_row[sb] - L, -1) : p_row[sb] - L;
+      dhi[sb] = wlo[sb] = whi[sb] = 0;
+    }
   }
 
   // Q operands: kSteps x 8 bf16 per sub-tile (rows past n_q, and every row
@@ -372,15 +379,14 @@ pa_prefill_bf16(PrefillArgs a) {
           // at or past L, and their outputs are never stored
           bool whole = c0 + 16 <= L;
           if constexpr (CAUSAL) whole = whole && c0 + 15 <= sp0[sb];
-          if constexpr (WINDOW)
-            whole = whole && sp1[sb] - c0 < a.window && c0 + 15 - sp0[sb] < a.window;
+          if constexpr (WINDOW) whole = whole && c0 >= wlo[sb] && c0 + 16 <= whi[sb];
           if (!whole) {
             const int d0 = dq[sb] - c0;
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
               const int d = d0 - r;
               bool vis = d > dlo[sb];
-              if constexpr (WINDOW) vis = vis && d < a.window;
+              if constexpr (WINDOW) vis = vis && d < dhi[sb];
               s[sb][ch][r] = vis ? s[sb][ch][r] : -INFINITY;
             }
           }
@@ -767,17 +773,19 @@ pa_prefill_bf16_32(PrefillArgs a) {
   }
 }
 
-// Bidirectional launches without a window take the 32-query-per-wave kernel;
-// causal and windowed ones the 16-query-per-wave kernel.
+// Bidirectional launches without a window or chunks take the
+// 32-query-per-wave kernel; causal, windowed and chunked ones the
+// 16-query-per-wave kernel.
 template <int D, int BIAS>
 void launch_bias(const PrefillArgs& a, dim3 grid, hipStream_t stream) {
   const dim3 block(Cfg<D>::kThreads);
+  const bool banded = a.window > 0 || a.chunk > 0;
   if (a.causal) {
-    if (a.window > 0)
+    if (banded)
       hipLaunchKernelGGL((pa_prefill_bf16<D, BIAS, true, true>), grid, block, 0, stream, a);
     else
       hipLaunchKernelGGL((pa_prefill_bf16<D, BIAS, true, false>), grid, block, 0, stream, a);
-  } else if (a.window > 0) {
+  } else if (banded) {
     hipLaunchKernelGGL((pa_prefill_bf16<D, BIAS, false, true>), grid, block, 0, stream, a);
   } else {
     hipLaunchKernelGGL((pa_prefill_bf16_32<D, BIAS>), grid, dim3(kThreads32), 0, stream, a);
@@ -786,7 +794,8 @@ void launch_bias(const PrefillArgs& a, dim3 grid, hipStream_t stream) {
 
 template <int D>
 hipError_t launch_d(PrefillArgs a, hipStream_t stream) {
-  const int qt = !a.causal && a.window <= 0 ? kQT32 : kQT;   // queries per workgroup
+  // queries per workgroup
+  const int qt = !a.causal && a.window <= 0 && a.chunk <= 0 ? kQT32 : kQT;
   a.num_qtiles = (a.max_seq_len + qt - 1) / qt;
   const int64_t pairs = (int64_t)a.num_seqs * a.num_heads;
   const int64_t nwg = (pairs + kXcds - 1) / kXcds * kXcds * a.num_qtiles;

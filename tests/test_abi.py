@@ -26,7 +26,8 @@ def test_header_declares_entry_points():
     names = declared_functions()
     for n in ("paged_attn_decode", "paged_attn_prefill", "pa_decode_workspace_bytes",
               "pa_last_error", "pa_abi_version", "pa_check_metadata",
-              "pa_decode_default_partition"):
+              "pa_decode_default_partition", "paged_attn_decode_chunked",
+              "paged_attn_prefill_chunked"):
         assert n in names
 
 
@@ -75,6 +76,39 @@ def test_decode_rejects_on_host(kw, status):
     st = call_decode(lib, decode_args(**kw))
     assert st == status, (st, lib.pa_last_error())
     assert lib.pa_last_error()
+
+
+@pytest.mark.parametrize("chunk", [0, -1, -16])
+def test_chunked_entry_points_reject_non_positive_chunks(chunk):
+    lib = pa.lib()
+    a = decode_args(window=chunk)          # the chunk size takes the window's place
+    st = lib._lib.paged_attn_decode_chunked(
+        a["out"], a["q"], a["k"], a["v"], a["bt"], a["cl"], a["bias"], a["window"], a["scale"],
+        a["B"], a["H"], a["Hkv"], a["D"], a["bs"], a["maxb"], a["msl"], a["nb"], a["dtype"],
+        a["part"], a["ws"], a["wsb"], a["stream"])
+    assert st == 2 and "chunk_size" in lib.pa_last_error()
+    st = lib._lib.paged_attn_prefill_chunked(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None,
+                                             chunk, 0, 0.125, 2, 4, 4, 64, 16, 8, 128, 64, 10,
+                                             0, None)
+    assert st == 2 and "chunk_size" in lib.pa_last_error()
+
+
+def test_chunked_entry_points_check_like_the_base_ones():
+    lib = pa.lib()
+    a = decode_args(window=32, q=None)
+    st = lib._lib.paged_attn_decode_chunked(
+        a["out"], a["q"], a["k"], a["v"], a["bt"], a["cl"], a["bias"], a["window"], a["scale"],
+        a["B"], a["H"], a["Hkv"], a["D"], a["bs"], a["maxb"], a["msl"], a["nb"], a["dtype"],
+        a["part"], a["ws"], a["wsb"], a["stream"])
+    assert st == 1                                       # NULL q
+    st = lib._lib.paged_attn_prefill_chunked(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None,
+                                             32, 2, 0.125, 2, 4, 4, 64, 16, 8, 128, 64, 10,
+                                             0, None)
+    assert st == 2                                       # causal must be 0 or 1
+    # an empty batch launches nothing and needs no pointers
+    assert lib._lib.paged_attn_decode_chunked(None, None, None, None, None, None, None, 32,
+                                              0.125, 0, 4, 4, 64, 16, 8, 128, 64, 0, 0, None,
+                                              0, None) == 0
 
 
 def test_decode_workspace_required():
