@@ -17,12 +17,13 @@ Prints ONE JSON line. Options:
   --steps K       timed steps (default 20)
   --warmup W      untimed warm-up steps (default 5)
   --workload X    large_biased_decode_bf16 (default) | modernbert_prefill_f32 |
-                  modernbert_prefill_bf16 |
+                  modernbert_prefill_bf16 | modernbert_chunked_prefill_f32 |
+                  modernbert_chunked_prefill_bf16 (one layer, 128-token chunks) |
                   t5_small_self_decode_bf16 | t5_large_cross_decode_bf16 (cold-cache
                   median of single calls) | kv_write_modernbert_f32 | copy_probe (a plain device copy of
                   known size, for calibrating the rocprofv3 byte counters)
   --no-cpu-baseline   skip the oracle timing
-  --no-variants       skip the window / null-bias / no-bias-build variants
+  --no-variants       skip the window / chunk / null-bias / no-bias-build variants
 """
 from __future__ import annotations
 
@@ -121,13 +122,18 @@ def per_call_ms(fn, n):
 # ----------------------------------------------------------------------------
 # decode
 # ----------------------------------------------------------------------------
-def decode_bytes(lens, H, D, esize, window, with_bias):
+def decode_bytes(lens, H, D, esize, window, with_bias, chunk=0):
     """Algorithmic HBM bytes of one decode call: for every (sequence, head)
     the visible tokens' K and V rows (2*D*e bytes) and bias entries (4 bytes),
-    plus the q read and out write (2*D*e). Block-table and length reads
-    (< 0.1%) are not counted."""
+    plus the q read and out write (2*D*e). Visible: all L tokens, the W newest
+    with a window, or with chunked local attention the query's chunk up to it,
+    ((L-1) mod C) + 1 tokens. Block-table and length reads (< 0.1%) are not
+    counted."""
     L = lens.astype(np.int64)
-    n_vis = np.minimum(L, window) if window > 0 else L
+    if chunk > 0:
+        n_vis = np.where(L > 0, (L - 1) % chunk + 1, 0)
+    else:
+        n_vis = np.minimum(L, window) if window > 0 else L
     per_tok = 2 * D * esize + (4 if with_bias else 0)
     return int(H * np.sum(n_vis * per_tok + 2 * D * esize))
 
@@ -243,6 +249,15 @@ def bench_decode(args):
         bw = decode_bytes(case.lens, H, D, 2, 1024, True)
         var["window_1024"] = {"ms_per_step": msw, "tokens_per_s": B / (msw * 1e-3),
                               "GBps": bw / (msw * 1e-3) / 1e9}
+        # chunked local attention, 1024-token chunks (the query sees its chunk's
+        # first ((L-1) mod 1024) + 1 tokens)
+        msc = time_steps(lambda: lib.paged_attn_decode_chunked(
+            case.q, case.k_cache, case.v_cache, case.block_tables, case.context_lens,
+            case.attn_bias, 1024, case.scale, max_seq_len=case.max_seq_len, out=out),
+            args.steps, args.warmup)
+        bc = decode_bytes(case.lens, H, D, 2, -1, True, chunk=1024)
+        var["chunk_1024"] = {"ms_per_step": msc, "tokens_per_s": B / (msc * 1e-3),
+                             "GBps": bc / (msc * 1e-3) / 1e9}
         msn = time_steps(lambda: step(bias=None), args.steps, args.warmup)
         bn = decode_bytes(case.lens, H, D, 2, -1, False)
         var["null_bias"] = {"ms_per_step": msn, "tokens_per_s": B / (msn * 1e-3),
@@ -291,8 +306,14 @@ def bench_decode(args):
 # ----------------------------------------------------------------------------
 # prefill (12-layer ModernBERT-shaped encoder)
 # ----------------------------------------------------------------------------
-def prefill_flops(lens, H, D, window):
+def prefill_flops(lens, H, D, window, chunk=0):
+    """Algorithmic flops of a bidirectional prefill layer: 4*D per visible
+    (query, key) pair, every pair of a sequence, |i - j| < W with a window, or
+    pairs inside one chunk of C positions with chunked local attention."""
     L = lens.astype(np.int64)
+    if chunk > 0:
+        full, rem = L // chunk, L % chunk
+        return int(4 * D * H * np.sum(full * chunk * chunk + rem * rem))
     if window > 0:
         W = np.minimum(window, L)
         pairs = L * (2 * W - 1) - W * (W - 1)
@@ -349,6 +370,38 @@ def bench_prefill(args, dtype=torch.float32):
         "algorithmic_flops_per_step": flops,
     }
     return line
+
+
+def bench_chunked_prefill(args, dtype=torch.float32):
+    """One ModernBERT-shaped layer (32 sequences of U[64,1024], 12 heads,
+    head_dim 64) with bidirectional chunked local attention in 128-token
+    chunks, through paged_attn_prefill_chunked."""
+    c = workloads.prefill_case(4, num_seqs=32, num_heads=12, head_dim=64, lens=(64, 1024),
+                               max_seq_len=1024, dtype=dtype, device="cuda", layer_seed=[4, 1])
+    torch.cuda.synchronize()
+    out = torch.empty_like(c.q)
+    lib = pa.lib()
+    ms = time_steps(lambda: lib.paged_attn_prefill_chunked(
+        c.q, c.k_cache, c.v_cache, c.block_tables, c.context_lens, c.query_start_loc, None,
+        128, False, c.scale, max_seq_len=c.max_seq_len, out=out), args.steps, args.warmup)
+    flops = prefill_flops(c.lens, 12, 64, -1, chunk=128)
+    tflops = flops / (ms * 1e-3) / 1e12
+    peak = FP32_MFMA_PEAK_TFLOPS if dtype == torch.float32 else BF16_MFMA_PEAK_TFLOPS
+    tag = "f32" if dtype == torch.float32 else "bf16"
+    return {
+        "metric": "chunked-local prefill tokens/s (one layer) and MFMA TFLOP/s",
+        "value": int(c.lens.sum()) / (ms * 1e-3), "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": tag,
+        "data": "synthetic",
+        "config": {"workload": "modernbert_chunked_prefill_" + tag, "layers": 1,
+                   "num_seqs": 32, "num_heads": 12, "head_dim": 64,
+                   "context_lens": "uniform [64, 1024]", "chunk_size": 128},
+        "roofline": {"bound": "mfma", "achieved": tflops, "peak": peak, "unit": "TFLOP/s",
+                     "frac": tflops / peak, "traffic": None,
+                     "kernel": "pa_prefill_%s (banded variant, one launch)" % tag},
+        "algorithmic_flops_per_step": flops,
+    }
 
 
 def bench_copy(args):
@@ -480,6 +533,10 @@ def main():
         line = bench_prefill(args)
     elif args.workload == "modernbert_prefill_bf16":
         line = bench_prefill(args, torch.bfloat16)
+    elif args.workload == "modernbert_chunked_prefill_f32":
+        line = bench_chunked_prefill(args)
+    elif args.workload == "modernbert_chunked_prefill_bf16":
+        line = bench_chunked_prefill(args, torch.bfloat16)
     elif args.workload in ("t5_small_self_decode_bf16", "t5_large_cross_decode_bf16"):
         line = bench_small_decode(args, args.workload)
     elif args.workload == "kv_write_modernbert_f32":

@@ -21,7 +21,7 @@ sys.path.insert(0, ROOT)
 import bench  # noqa: E402
 
 
-def brute_decode_bytes(lens, H, D, esize, window, with_bias):
+def brute_decode_bytes(lens, H, D, esize, window, with_bias, chunk=0):
     total = 0
     for L in lens:
         for _ in range(H):
@@ -30,16 +30,20 @@ def brute_decode_bytes(lens, H, D, esize, window, with_bias):
             for j in range(L):
                 if window > 0 and not (0 <= i - j < window):
                     continue
+                if chunk > 0 and j // chunk != i // chunk:
+                    continue
                 total += 2 * D * esize + (4 if with_bias else 0)
     return total
 
 
-def brute_prefill_flops(lens, H, D, window):
+def brute_prefill_flops(lens, H, D, window, chunk=0):
     pairs = 0
     for L in lens:
         for i in range(L):
             for j in range(L):
                 if window > 0 and abs(i - j) >= window:
+                    continue
+                if chunk > 0 and i // chunk != j // chunk:
                     continue
                 pairs += 1
     return 4 * D * H * pairs                # q.k and p.v: 2 flops per MAC each
@@ -54,11 +58,25 @@ def test_decode_bytes_match_brute_force(window, with_bias, esize):
     assert got == brute_decode_bytes(lens.tolist(), 3, 64, esize, window, with_bias)
 
 
+@pytest.mark.parametrize("chunk", [1, 5, 16, 40])
+def test_chunked_decode_bytes_match_brute_force(chunk):
+    lens = np.array([1, 2, 15, 16, 17, 33, 40, 81], dtype=np.int32)
+    got = bench.decode_bytes(lens, 3, 64, 2, -1, True, chunk=chunk)
+    assert got == brute_decode_bytes(lens.tolist(), 3, 64, 2, -1, True, chunk=chunk)
+
+
 @pytest.mark.parametrize("window", [-1, 1, 2, 7, 30, 64])
 def test_prefill_flops_match_brute_force(window):
     lens = np.array([1, 3, 16, 29, 64, 70], dtype=np.int32)
     got = bench.prefill_flops(lens, 2, 64, window)
     assert got == brute_prefill_flops(lens.tolist(), 2, 64, window)
+
+
+@pytest.mark.parametrize("chunk", [1, 7, 16, 64, 128])
+def test_chunked_prefill_flops_match_brute_force(chunk):
+    lens = np.array([1, 3, 16, 29, 64, 70, 130], dtype=np.int32)
+    got = bench.prefill_flops(lens, 2, 64, -1, chunk=chunk)
+    assert got == brute_prefill_flops(lens.tolist(), 2, 64, -1, chunk=chunk)
 
 
 def test_read_traffic_requires_the_measured_source(tmp_path, monkeypatch):
