@@ -185,3 +185,44 @@ def test_random_ragged_bias(seed):
                                 h.query_start_loc, packed, starts, d["window"],
                                 int(d["causal"]), h.scale, msl)
     assert_close(out, ref, d["dtype"], "random ragged prefill %d" % seed)
+
+
+@pytest.mark.parametrize("seed", range(16))
+def test_random_chunked(seed):
+    """Chunked local attention, decode and prefill, on drawn shapes: chunk
+    sizes from 1 to beyond the longest sequence, zero-length sequences and
+    partial query sets included."""
+    d = draw(6000 + seed)
+    chunk = int(d["rng"].choice([1, 3, 16, 31, 64, 129, 1000]))
+    msl = -(-d["maxlen"] // BS) * BS
+    lens = d["rng"].integers(0, d["maxlen"] + 1, size=d["B"])
+    log("random chunked %d: C=%d %s" % (seed, chunk, {k: v for k, v in d.items() if k != "rng"}))
+    dc = to_device(workloads.decode_case(6100 + seed, num_seqs=d["B"], num_heads=d["H"],
+                                         head_dim=d["D"], lens=lens.tolist(), max_seq_len=msl,
+                                         dtype=d["dtype"], bias=d["bias"]))
+    out = pa.lib().paged_attn_decode_chunked(dc.q, dc.k_cache, dc.v_cache, dc.block_tables,
+                                             dc.context_lens, dc.attn_bias, chunk, dc.scale,
+                                             max_seq_len=dc.max_seq_len,
+                                             partition_tokens=d["partition"])
+    torch.cuda.synchronize()
+    h = to_host(dc)
+    ref = oracle.decode_chunked(h.q, h.k_cache, h.v_cache, h.block_tables, h.context_lens,
+                                h.attn_bias, chunk, h.scale, h.max_seq_len)
+    assert_close(out, ref, d["dtype"], "random chunked decode %d" % seed)
+    q_lens = [int(d["rng"].integers(0, L + 1)) if d["rng"].integers(0, 2) else int(L)
+              for L in lens]
+    pc = to_device(workloads.prefill_case(6200 + seed, num_seqs=d["B"], num_heads=d["H"],
+                                          head_dim=d["D"], lens=lens.tolist(), max_seq_len=msl,
+                                          dtype=d["dtype"],
+                                          bias=None if d["bias"] == "zero" else d["bias"],
+                                          causal=d["causal"], q_lens=q_lens))
+    outp = pa.lib().paged_attn_prefill_chunked(pc.q, pc.k_cache, pc.v_cache, pc.block_tables,
+                                               pc.context_lens, pc.query_start_loc,
+                                               pc.attn_bias, chunk, pc.causal, pc.scale,
+                                               max_seq_len=pc.max_seq_len)
+    torch.cuda.synchronize()
+    hp = to_host(pc)
+    refp = oracle.prefill_chunked(hp.q, hp.k_cache, hp.v_cache, hp.block_tables,
+                                  hp.context_lens, hp.query_start_loc, hp.attn_bias, chunk,
+                                  int(hp.causal), hp.scale, hp.max_seq_len)
+    assert_close(outp, refp, d["dtype"], "random chunked prefill %d" % seed)
