@@ -100,6 +100,7 @@ __device__ __forceinline__ void prefill_key_range(int p0, int p1, int L, int win
 // dlo < d < dhi. Window W: dhi = W and d > -W; chunk C: the key lies in p's
 // chunk [p - p % C, p - p % C + C), i.e. p % C - C < d < p % C + 1. Both
 // also need j < L (d > p - L), and causal queries j <= p (d > -1).
+// Banded launches only: window >= 1, or window <= 0 and chunk >= 1; p >= 0.
 __device__ __forceinline__ void prefill_row_bounds(int p, int L, int window, int chunk,
                                                    bool causal, int& dlo, int& dhi) {
   int lo = p - L;
@@ -117,6 +118,7 @@ __device__ __forceinline__ void prefill_row_bounds(int p, int L, int window, int
 
 // Keys [wlo, whi) that every position in [p0, p1] may see under its window or
 // chunk (the sequence end and a causal limit are checked separately).
+// Banded launches only, as prefill_row_bounds.
 __device__ __forceinline__ void prefill_common_keys(int p0, int p1, int window, int chunk,
                                                     int& wlo, int& whi) {
   if (window > 0) {
