@@ -24,7 +24,9 @@ import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "oracle.c")
-_LIB = os.path.join(_HERE, "liboracle.so")
+# PA_ORACLE_LIB points the tests at another build of oracle.c (the mutation
+# test loads copies with planted mistakes this way)
+_LIB = os.environ.get("PA_ORACLE_LIB") or os.path.join(_HERE, "liboracle.so")
 _lib = None
 
 DTYPE_F32 = 0
