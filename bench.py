@@ -477,7 +477,8 @@ def bench_small_decode(args, name):
                            B, H, D, case.max_seq_len, -1),
                        "attn_bias": None if case.attn_bias is None else "fp32 (T5 buckets)"},
             "roofline": {"bound": "hbm", "achieved": gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                         "frac": gbps / HBM_PEAK_GBPS, "traffic": None,
+                         "frac": gbps / HBM_PEAK_GBPS,
+                         "traffic": read_traffic(name, "pa_decode.hip"),
                          "kernel": "paged_attn_decode call"},
             "algorithmic_bytes_per_step": nbytes, "variants": extra}
 
@@ -506,7 +507,8 @@ def bench_kv_write(args):
             "config": {"workload": "kv_write_modernbert_f32", "tokens": T, "num_heads": H,
                        "head_dim": D},
             "roofline": {"bound": "hbm", "achieved": gbps, "peak": HBM_PEAK_GBPS,
-                         "unit": "GB/s", "frac": gbps / HBM_PEAK_GBPS, "traffic": None,
+                         "unit": "GB/s", "frac": gbps / HBM_PEAK_GBPS,
+                         "traffic": read_traffic("kv_write_modernbert_f32", "pa_cache.hip"),
                          "kernel": "pa_kv_write"},
             "algorithmic_bytes_per_step": nbytes}
 

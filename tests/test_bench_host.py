@@ -98,7 +98,10 @@ def test_committed_traffic_summaries_parse():
     """The committed counter summaries hold the keys the bench lines read."""
     for wl, key in (("decode_large_biased_bf16", "hbm_bytes_per_launch"),
                     ("modernbert_prefill_f32", "hbm_bytes_per_step"),
-                    ("modernbert_prefill_bf16", "hbm_bytes_per_step")):
+                    ("modernbert_prefill_bf16", "hbm_bytes_per_step"),
+                    ("t5_small_self_decode_bf16", "hbm_bytes_per_launch"),
+                    ("t5_large_cross_decode_bf16", "hbm_bytes_per_launch"),
+                    ("kv_write_modernbert_f32", "hbm_bytes_per_launch")):
         kv = {}
         for ln in open(os.path.join(ROOT, "profiles", "%s_traffic.txt" % wl)):
             if "=" in ln and not ln.startswith("#"):
