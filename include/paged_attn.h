@@ -33,8 +33,11 @@
  *   context_lens      int32 [num_seqs], 0 <= L <= max_seq_len
  *   attn_bias         fp32, decode [num_seqs, num_heads, max_seq_len],
  *                     prefill [num_seqs, num_heads, max_seq_len, max_seq_len],
- *                     indexed by logical positions; entries of keys that are
- *                     not visible are never read. NULL = no bias.
+ *                     indexed by logical positions (prefill: [query position]
+ *                     [key position]); an entry is read only when its query is
+ *                     one of the call's queries and its key is visible to that
+ *                     query, so every other entry may hold anything (NaN
+ *                     included). NULL = no bias.
  *
  * Conventions of every entry point:
  *   - returns a pa_status_t; never aborts or throws; pa_last_error() gives a
@@ -43,7 +46,13 @@
  *     host BEFORE any HIP call; the contents of device arrays (lengths, table
  *     entries) are not validated unless the environment variable
  *     PA_VALIDATE=1 is set, in which case they are copied to the host
- *     (synchronously) and range-checked first;
+ *     (synchronously) and range-checked first. Without it the kernels still
+ *     refuse to go out of range on bad lengths: a decode sequence whose L is
+ *     outside [0, max_seq_len] gets a zero output, and a prefill sequence
+ *     with L > max_seq_len, n_q outside [0, L] or query rows outside
+ *     [0, total_q) is skipped (its rows are left unwritten). Block-table
+ *     entries are used as given: an entry outside [0, num_blocks) that backs
+ *     a visible token can fault the device;
  *   - work is enqueued asynchronously on `stream` (a hipStream_t; NULL = the
  *     default stream); device faults surface at the caller's next sync;
  *   - the library allocates nothing and keeps no state between calls that

@@ -191,11 +191,24 @@ class PagedAttnLib:
 
     def pa_check_metadata(self, block_tables, context_lens, query_start_loc, sliding_window,
                           causal, max_seq_len, num_blocks, total_q=0) -> None:
-        """Range-check host (CPU) int32 tensors; raises PagedAttnError."""
+        """Range-check host (CPU) int32 tensors; raises PagedAttnError.
+
+        block_tables [B, max_blocks], context_lens [B], query_start_loc [B+1]
+        or None: the shapes are checked here, since the C check reads exactly
+        that many entries of each array."""
         for t in (block_tables, context_lens, query_start_loc):
-            if t is not None and (t.device.type != "cpu" or t.dtype != torch.int32
-                                  or not t.is_contiguous()):
+            if t is not None and (not isinstance(t, torch.Tensor) or t.device.type != "cpu"
+                                  or t.dtype != torch.int32 or not t.is_contiguous()):
                 raise TypeError("pa_check_metadata takes contiguous CPU int32 tensors")
+        if context_lens is None or context_lens.dim() != 1:
+            raise ValueError("context_lens must be a 1-D tensor [num_seqs]")
+        B = context_lens.shape[0]
+        if block_tables is None or block_tables.dim() != 2 or block_tables.shape[0] != B:
+            raise ValueError("block_tables must have shape (%d, max_blocks_per_seq), got %s"
+                             % (B, None if block_tables is None else tuple(block_tables.shape)))
+        if query_start_loc is not None and tuple(query_start_loc.shape) != (B + 1,):
+            raise ValueError("query_start_loc must have shape (%d,), got %s"
+                             % (B + 1, tuple(query_start_loc.shape)))
         self._check(self._lib.pa_check_metadata(
             _ptr(block_tables), _ptr(context_lens), _ptr(query_start_loc),
             int(sliding_window), int(causal), context_lens.shape[0], block_tables.shape[1],

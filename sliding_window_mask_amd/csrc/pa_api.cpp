@@ -195,6 +195,12 @@ pa_status_t check_metadata_impl(const int32_t* block_tables, const int32_t* cont
                                 int64_t num_blocks, int64_t total_q) {
   (void)causal;
   if (num_seqs < 0) return fail(PA_ERR_INVALID_ARG, "num_seqs < 0");
+  // the table rows must cover max_seq_len: every entry read below then lies
+  // inside the num_seqs x max_blocks_per_seq array
+  if (max_seq_len < 0 || max_blocks_per_seq < 0 ||
+      (int64_t)max_blocks_per_seq * pa::kBlockSize < max_seq_len)
+    return fail(PA_ERR_INVALID_ARG, "max_blocks_per_seq %d does not cover max_seq_len %d",
+                max_blocks_per_seq, max_seq_len);
   if (num_seqs > 0 && (!context_lens || (max_blocks_per_seq > 0 && !block_tables)))
     return fail(PA_ERR_NULL_POINTER, "metadata pointer is NULL");
   if (query_start_loc) {
@@ -427,6 +433,7 @@ pa_status_t prefill_impl(void* out, const void* q, const void* k_cache, const vo
   a.max_blocks = max_blocks_per_seq;
   a.max_seq_len = max_seq_len;
   a.dtype = (int32_t)dtype;
+  a.total_q = (int32_t)total_q;
   if (rel) a.rel = *rel;
   hipError_t e = dtype == PA_DTYPE_F32 ? pa::launch_prefill_f32(a, s) : pa::launch_prefill_bf16(a, s);
   if (e != hipSuccess) return fail(PA_ERR_HIP, "prefill launch failed: %s", hipGetErrorString(e));

@@ -199,11 +199,13 @@ pa_decode_partition(DecodeArgs a) {
   const int H = a.num_heads;
   const int P = a.partition;
 
+  // a length outside [0, max_seq_len] (unchecked unless PA_VALIDATE is set)
+  // is treated as an empty sequence rather than read past the table row
   const int L = a.context_lens[b];
   const int lo = decode_first_key(a, L);
   const int start = lo & ~(kBlockSize - 1);
   const int t0 = start + part * P;                     // first token of partition
-  if (L <= 0 || t0 >= L) {
+  if (L <= 0 || L > a.max_seq_len || t0 >= L) {
     if (SINGLE && part == 0 && tid < D)                 // empty sequence: zeros
       store_out<DT>(a.out, ((int64_t)b * H + h) * D + tid, 0.0f);
     return;
@@ -420,7 +422,7 @@ __global__ void __launch_bounds__(D) pa_decode_merge(DecodeArgs a) {
   const int L = a.context_lens[b];
   const int lo = decode_first_key(a, L);
   const int start = lo & ~(kBlockSize - 1);
-  const int np = L > 0 ? (L - start + a.partition - 1) / a.partition : 0;
+  const int np = L > 0 && L <= a.max_seq_len ? (L - start + a.partition - 1) / a.partition : 0;
   const int64_t base = row * a.num_partitions;
   float M = -INFINITY;
   for (int p = 0; p < np; ++p) M = fmaxf(M, a.ws_m[base + p]);

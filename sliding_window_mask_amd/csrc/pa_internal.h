@@ -73,6 +73,7 @@ struct PrefillArgs {
   float scale_log2;
   int32_t num_seqs, num_heads, head_dim, max_blocks, max_seq_len;
   int32_t dtype;
+  int32_t total_q;            // rows of q and out
   int32_t num_qtiles;         // query tiles per sequence in the grid (set by the launcher)
   RelPos rel;                 // used when rel.table is set (attn_bias is then null)
 };
@@ -151,6 +152,10 @@ constexpr int kRankMaxSeqs = 63;   // batches ranked by length inside the kernel
 // and hands its sequence's values to the other waves through LDS (one
 // barrier). Windowed and chunked launches (bounded work per workgroup) and larger
 // batches keep index order.
+// Metadata outside the documented ranges (0 <= n_q <= L <= max_seq_len, the
+// sequence's query rows inside [0, total_q)) also returns false: such a
+// workgroup writes nothing rather than read or write out of bounds (the
+// host checks these ranges only under PA_VALIDATE).
 __device__ __forceinline__ bool prefill_work_of(int n, const PrefillArgs& a, int& b, int& h,
                                                 int& tile, int& L, int& q0, int& nq) {
   const int H = a.num_heads;
@@ -199,7 +204,8 @@ __device__ __forceinline__ bool prefill_work_of(int n, const PrefillArgs& a, int
     q0 = a.query_start_loc[b];
     nq = a.query_start_loc[b + 1] - q0;
   }
-  return true;
+  return b >= 0 && b < B && L <= a.max_seq_len && nq >= 0 && nq <= L && q0 >= 0 &&
+         q0 <= a.total_q - nq;
 }
 
 // Bucket of a non-negative distance within one direction (see RelPos).

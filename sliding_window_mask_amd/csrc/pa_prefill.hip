@@ -138,14 +138,19 @@ pa_prefill_f32(PrefillArgs a) {
   // j <= p, window p - j > -W, chunk start) and, with a window or chunks,
   // d < dhi (window W, or the end of p's chunk). Keys [wlo, whi) are inside
   // the window or chunk of every row of the group.
-  int gp0[NG], gp1[NG], t[NG], p[NG], dq[NG], dlo[NG], dhi[NG], wlo[NG], whi[NG];
+  // Rows past n_q see no key at all (their dlo is the largest int), and where
+  // a chunk is seen whole by the group they read the bias row of the group's
+  // first existing query (fr): the bias entries of keys a row cannot see are
+  // never read. A group with no existing row (possible only with NG > 1)
+  // takes the workgroup's last query as its only row.
+  int gp0[NG], gp1[NG], fr[NG], t[NG], p[NG], dq[NG], dlo[NG], dhi[NG], wlo[NG], whi[NG];
   bool row_ok[NG];
 #pragma unroll
   for (int q = 0; q < NG; ++q) {
     const int first = w_first + 16 * q;
-    const int last = min(first + 16, nq) - 1;
-    gp0[q] = pos0 + first;
-    gp1[q] = pos0 + last;
+    fr[q] = min(first, nq - 1);
+    gp0[q] = pos0 + fr[q];
+    gp1[q] = pos0 + max(min(first + 16, nq) - 1, fr[q]);
     t[q] = first + c;
     row_ok[q] = t[q] < nq;
     p[q] = pos0 + t[q];
@@ -160,6 +165,7 @@ pa_prefill_f32(PrefillArgs a) {
       dlo[q] = CAUSAL ? max(p[q] - L, -1) : p[q] - L;
       dhi[q] = wlo[q] = whi[q] = 0;
     }
+    if (!row_ok[q]) dlo[q] = 0x7fffffff;
   }
 
   // Q operands: D/4 contiguous floats per lane, pre-multiplied by
@@ -285,9 +291,8 @@ pa_prefill_f32(PrefillArgs a) {
     m_ref[q] = -INFINITY;
     neg_m[q] = 0.0f;
     l_run[q] = 0.0f;
-    // rows past n_q point at the tile's first row and are masked, so every
-    // bias read is in bounds
-    const int tb_row = row_ok[q] ? t[q] : t_first;   // query index within the sequence
+    // rows past n_q read the group's first existing row (see above)
+    const int tb_row = row_ok[q] ? t[q] : fr[q];     // query index within the sequence
     if (BIAS != 1)
       bias_row[q] = nullptr;
     else if (a.bias_start)                           // ragged rows [H][n_q][L]
@@ -375,27 +380,26 @@ pa_prefill_f32(PrefillArgs a) {
             s[q][ch] = float4_t{-INFINITY, -INFINITY, -INFINITY, -INFINITY};
             continue;
           }
-          // bias (added as a * scale * log2(e): the same sum as (q.k + a) * scale)
-          if constexpr (BIAS == 1) {
-#pragma unroll
-            for (int r = 0; r < 4; ++r)
-              s[q][ch][r] = s[q][ch][r] + bias_row[q][min(j0 + r, L - 1)] * cs;
-          }
           if constexpr (BIAS == 2) {
 #pragma unroll
             for (int r = 0; r < 4; ++r)
               s[q][ch][r] = s[q][ch][r] + rel_lds[min(max(j0 + r - p[q], -rel_md), rel_md) + rel_md];
           }
           // per-element mask only where some existing row of the group does
-          // not see the whole chunk (sequence end, window edges, diagonal).
-          // Rows past n_q are not masked: their q is zero, they see no key at
-          // or past L, and their outputs are never stored.
+          // not see the whole chunk (sequence end, window edges, diagonal);
+          // a materialised bias (added as a * scale * log2(e): the same sum as
+          // (q.k + a) * scale) is read only for visible keys
           bool whole = c0 + 16 <= L;
           if constexpr (CAUSAL) whole = whole && c0 + 15 <= gp0[q];
           if constexpr (BAND == 1)
             whole = whole && gp1[q] - c0 < a.window && c0 + 15 - gp0[q] < a.window;
           if constexpr (BAND == 2) whole = whole && c0 >= wlo[q] && c0 + 16 <= whi[q];
-          if (!whole) {
+          if (whole) {
+            if constexpr (BIAS == 1) {
+#pragma unroll
+              for (int r = 0; r < 4; ++r) s[q][ch][r] = s[q][ch][r] + bias_row[q][j0 + r] * cs;
+            }
+          } else {
             const int d0 = dq[q] - c0;
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
@@ -403,7 +407,13 @@ pa_prefill_f32(PrefillArgs a) {
               bool vis = d > dlo[q];
               if constexpr (BAND == 1) vis = vis && d < a.window;
               if constexpr (BAND == 2) vis = vis && d < dhi[q];
-              s[q][ch][r] = vis ? s[q][ch][r] : -INFINITY;
+              if constexpr (BIAS == 1) {
+                float x = -INFINITY;
+                if (vis) x = s[q][ch][r] + bias_row[q][j0 + r] * cs;
+                s[q][ch][r] = x;
+              } else {
+                s[q][ch][r] = vis ? s[q][ch][r] : -INFINITY;
+              }
             }
           }
         }

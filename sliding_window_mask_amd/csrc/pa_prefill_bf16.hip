@@ -139,17 +139,23 @@ pa_prefill_bf16(PrefillArgs a) {
   // p - j > -W, chunk start) and, with a window or chunks, d < dhi (window
   // W, or the end of p's chunk). Keys [wlo, whi) are inside the window or
   // chunk of every row of the sub-tile.
-  int t_row[kSub], p_row[kSub], sp0[kSub], sp1[kSub], dq[kSub], dlo[kSub], dhi[kSub];
+  // Rows past n_q see no key at all (their dlo is the largest int), and where
+  // a chunk is seen whole by the sub-tile they read the bias row of its first
+  // existing query (fr): the bias entries of keys a row cannot see are never
+  // read. A sub-tile with no existing row (possible only with kSub > 1) takes
+  // the workgroup's last query as its only row.
+  int t_row[kSub], p_row[kSub], sp0[kSub], sp1[kSub], fr[kSub], dq[kSub], dlo[kSub], dhi[kSub];
   int wlo[kSub], whi[kSub];
   bool row_ok[kSub];
 #pragma unroll
   for (int sb = 0; sb < kSub; ++sb) {
     const int f = w_first + 16 * sb;
+    fr[sb] = min(f, nq - 1);
     t_row[sb] = f + c;
     row_ok[sb] = t_row[sb] < nq;
     p_row[sb] = pos0 + t_row[sb];
-    sp0[sb] = pos0 + f;
-    sp1[sb] = pos0 + min(f + 15, nq - 1);
+    sp0[sb] = pos0 + fr[sb];
+    sp1[sb] = pos0 + max(min(f + 15, nq - 1), fr[sb]);
     dq[sb] = p_row[sb] - 4 * g;
     if constexpr (WINDOW) {
       prefill_row_bounds(p_row[sb], L, a.window, a.chunk, CAUSAL, dlo[sb], dhi[sb]);
@@ -158,6 +164,7 @@ pa_prefill_bf16(PrefillArgs a) {
       dlo[sb] = CAUSAL ? max(p_row[sb] - L, -1) : p_row[sb] - L;
       dhi[sb] = wlo[sb] = whi[sb] = 0;
     }
+    if (!row_ok[sb]) dlo[sb] = 0x7fffffff;
   }
 
   // Q operands: kSteps x 8 bf16 per sub-tile (rows past n_q, and every row
@@ -269,7 +276,7 @@ pa_prefill_bf16(PrefillArgs a) {
     neg_m[sb] = 0.0f;
     bias_row[sb] = nullptr;
     if (BIAS == 1) {
-      const int tb_row = row_ok[sb] ? t_row[sb] : t_first;
+      const int tb_row = row_ok[sb] ? t_row[sb] : fr[sb];
       bias_row[sb] = a.bias_start
                          ? a.attn_bias + a.bias_start[b] + ((int64_t)h * nq + tb_row) * L
                          : a.attn_bias + (((int64_t)b * H + h) * a.max_seq_len + pos0 + tb_row) *
@@ -365,29 +372,37 @@ pa_prefill_bf16(PrefillArgs a) {
             s[sb][ch] = float4_t{-INFINITY, -INFINITY, -INFINITY, -INFINITY};
             continue;
           }
-          if constexpr (BIAS == 1) {
-#pragma unroll
-            for (int r = 0; r < 4; ++r)
-              s[sb][ch][r] = fmaf(bias_row[sb][min(j0 + r, L - 1)], bmul, s[sb][ch][r]);
-          }
           if constexpr (BIAS == 2) {
 #pragma unroll
             for (int r = 0; r < 4; ++r)
               s[sb][ch][r] += rel_lds[min(max(j0 + r - p_row[sb], -rel_md), rel_md) + rel_md];
           }
-          // rows past n_q are not masked: their q is zero, they see no key
-          // at or past L, and their outputs are never stored
+          // per-element mask only where some existing row of the sub-tile
+          // does not see the whole chunk; a materialised bias is read only
+          // for visible keys
           bool whole = c0 + 16 <= L;
           if constexpr (CAUSAL) whole = whole && c0 + 15 <= sp0[sb];
           if constexpr (WINDOW) whole = whole && c0 >= wlo[sb] && c0 + 16 <= whi[sb];
-          if (!whole) {
+          if (whole) {
+            if constexpr (BIAS == 1) {
+#pragma unroll
+              for (int r = 0; r < 4; ++r)
+                s[sb][ch][r] = fmaf(bias_row[sb][j0 + r], bmul, s[sb][ch][r]);
+            }
+          } else {
             const int d0 = dq[sb] - c0;
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
               const int d = d0 - r;
               bool vis = d > dlo[sb];
               if constexpr (WINDOW) vis = vis && d < dhi[sb];
-              s[sb][ch][r] = vis ? s[sb][ch][r] : -INFINITY;
+              if constexpr (BIAS == 1) {
+                float x = -INFINITY;
+                if (vis) x = fmaf(bias_row[sb][j0 + r], bmul, s[sb][ch][r]);
+                s[sb][ch][r] = x;
+              } else {
+                s[sb][ch][r] = vis ? s[sb][ch][r] : -INFINITY;
+              }
             }
           }
         }
@@ -679,7 +694,9 @@ pa_prefill_bf16_32(PrefillArgs a) {
             *reinterpret_cast<const uint4*>(&k_lds[buf][j * kKRow + 16 * st + 8 * hh]);
         s = mfma32_bf16(__builtin_bit_cast(bf16x8_t, kv), qv[st], s);
       }
-      // ---- bias (unscaled scores) and the tail mask ----
+      // ---- bias (unscaled scores) and the tail mask. Every row of these
+      // launches sees all L keys, so every bias entry read is a visible one
+      // (keys past L of the last tile re-read entry L - 1, then are masked) ----
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
         const int j0 = c0 + 8 * u + 4 * hh;

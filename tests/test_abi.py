@@ -215,6 +215,29 @@ def test_check_metadata_host():
                               48, 4, total_q=58)
 
 
+def test_check_metadata_rejects_mismatched_shapes():
+    """The C check reads num_seqs rows of the table and num_seqs + 1 query
+    offsets: the binding refuses arrays of other shapes before the call, and
+    the C check refuses a table too narrow for max_seq_len."""
+    lib = pa.lib()
+    bt = torch.tensor([[3, 1, 0], [2, 3, 9]], dtype=torch.int32)
+    cl = torch.tensor([40, 17], dtype=torch.int32)
+    with pytest.raises(ValueError):               # table has fewer rows than sequences
+        lib.pa_check_metadata(bt[:1].contiguous(), cl, None, -1, 0, 48, 4)
+    with pytest.raises(ValueError):               # 1-D table
+        lib.pa_check_metadata(bt.reshape(-1), cl, None, -1, 0, 48, 4)
+    with pytest.raises(ValueError):               # B offsets instead of B + 1
+        lib.pa_check_metadata(bt, cl, torch.tensor([0, 40], dtype=torch.int32), -1, 0, 48, 4,
+                              total_q=40)
+    with pytest.raises(ValueError):
+        lib.pa_check_metadata(bt, cl.reshape(2, 1), None, -1, 0, 48, 4)
+    with pytest.raises(TypeError):
+        lib.pa_check_metadata(bt, cl.to(torch.int64), None, -1, 0, 48, 4)
+    with pytest.raises(pa.PagedAttnError):        # 3 blocks cover 48 tokens, not 64
+        lib.pa_check_metadata(bt, torch.tensor([40, 17], dtype=torch.int32), None, -1, 0, 64,
+                              16)
+
+
 def test_binding_fails_loudly_without_library(tmp_path):
     with pytest.raises(RuntimeError):
         pa.PagedAttnLib(str(tmp_path / "missing.so"))
