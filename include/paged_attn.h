@@ -142,6 +142,35 @@ pa_status_t paged_attn_decode(void* out, const void* q, const void* k_cache,
                               size_t workspace_bytes, void* stream);
 
 /*
+ * paged_attn_decode for callers that cannot allocate device memory: code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc. Arguments and results are those of paged_attn_decode without
+ * the workspace. When the shape needs split-K partials, they go to a
+ * file-scope device array of PA_NOALLOC_SCRATCH_BYTES bytes that each GPU
+ * the library runs on holds until the process ends; a shape whose
+ * pa_decode_workspace_bytes(...) exceeds that size is rejected with
+ * PA_ERR_WORKSPACE before any launch. The entry point calls no hipMalloc,
+ * hipFree or other allocating routine (set PA_VALIDATE only where host
+ * copies and a stream synchronisation are acceptable). The array's address
+ * on a device is looked up on the first call there (the device of `stream`,
+ * or the current device for the null stream).
+ * Every call on one GPU shares that GPU's array: calls that overlap on one
+ * GPU (concurrent streams, other threads) race and may return wrong
+ * results; serialise them. Nothing in the array needs clearing between
+ * calls (each call writes every partial it reads).
+ * Errors: as paged_attn_decode, plus UNSUPPORTED for a device index >= 64.
+ */
+#define PA_NOALLOC_SCRATCH_BYTES (16u << 20)
+pa_status_t paged_attn_decode_noalloc(void* out, const void* q, const void* k_cache,
+                                      const void* v_cache, const int32_t* block_tables,
+                                      const int32_t* context_lens, const float* attn_bias,
+                                      int32_t sliding_window, float scale, int32_t num_seqs,
+                                      int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
+                                      int32_t block_size, int32_t max_blocks_per_seq,
+                                      int32_t max_seq_len, int64_t num_blocks, pa_dtype_t dtype,
+                                      int32_t partition_tokens, void* stream);
+
+/*
  * Prefill attention over packed queries, for bidirectional encoder-only
  * attention (causal = 0; n_q = L per sequence) or causal decoder prompts
  * (causal = 1). Uses MFMA for both contractions.

@@ -8,6 +8,7 @@ library is not built, or a call fails, an exception is raised.
 
 Functions mirror the C entry points:
   paged_attn_decode(...)         decoder self-attention / cross-attention decode
+  paged_attn_decode_noalloc(...) the same without a workspace or any device allocation
   paged_attn_prefill(...)        encoder-only (bidirectional) or causal prefill
   paged_attn_decode_relpos(...)  decode with the T5 relative-position bias in-kernel
   paged_attn_prefill_relpos(...) prefill with the T5 relative-position bias in-kernel
@@ -137,6 +138,9 @@ class PagedAttnLib:
         lib.paged_attn_prefill.restype = ctypes.c_int
         lib.paged_attn_prefill.argtypes = [P, P, P, P, P, P, P, P, I32, I32, F32, I32, I32,
                                            I32, I32, I32, I32, I32, I64, I64, ctypes.c_int, P]
+        lib.paged_attn_decode_noalloc.restype = ctypes.c_int
+        lib.paged_attn_decode_noalloc.argtypes = [P, P, P, P, P, P, P, I32, F32, I32, I32, I32,
+                                                  I32, I32, I32, I32, I64, ctypes.c_int, I32, P]
         lib.paged_attn_decode_chunked.restype = ctypes.c_int
         lib.paged_attn_decode_chunked.argtypes = lib.paged_attn_decode.argtypes
         lib.paged_attn_prefill_chunked.restype = ctypes.c_int
@@ -235,6 +239,25 @@ class PagedAttnLib:
         return self._decode(self._lib.paged_attn_decode, q, k_cache, v_cache, block_tables,
                             context_lens, attn_bias, sliding_window, scale, max_seq_len, out,
                             workspace, partition_tokens, stream)
+
+    def paged_attn_decode_noalloc(self, q, k_cache, v_cache, block_tables, context_lens,
+                                  attn_bias, sliding_window, scale, *, max_seq_len, out,
+                                  partition_tokens=0, stream=None):
+        """paged_attn_decode without a workspace and without any device
+        allocation: split-K partials go to the library's fixed per-GPU scratch
+        (PA_NOALLOC_SCRATCH_BYTES; larger needs are rejected). `out` must be
+        given. Calls that overlap on one GPU race."""
+        _tensor(q, "q", None, _FLOAT_DTYPES, ndim=3)
+        B, H, D = q.shape
+        dev = _check_attention_args(q, k_cache, v_cache, block_tables, context_lens, out)
+        if attn_bias is not None:
+            _tensor(attn_bias, "attn_bias", dev, (torch.float32,), shape=(B, H, max_seq_len))
+        self._check(self._lib.paged_attn_decode_noalloc(
+            _ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables),
+            _ptr(context_lens), _ptr(attn_bias), int(sliding_window), float(scale), B, H,
+            k_cache.shape[1], D, k_cache.shape[2], block_tables.shape[1], int(max_seq_len),
+            k_cache.shape[0], _dtype_code(q), int(partition_tokens), _stream(stream)))
+        return out
 
     def paged_attn_decode_chunked(self, q, k_cache, v_cache, block_tables, context_lens,
                                   attn_bias, chunk_size, scale, *, max_seq_len, out=None,
@@ -442,6 +465,10 @@ def paged_attn_decode(*args, **kwargs):
 
 def paged_attn_prefill(*args, **kwargs):
     return lib().paged_attn_prefill(*args, **kwargs)
+
+
+def paged_attn_decode_noalloc(*args, **kwargs):
+    return lib().paged_attn_decode_noalloc(*args, **kwargs)
 
 
 def paged_attn_decode_chunked(*args, **kwargs):

@@ -8,6 +8,7 @@
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
+#include <mutex>
 #include <vector>
 
 #include "pa_internal.h"
@@ -307,6 +308,46 @@ pa_status_t pa_check_metadata(const int32_t* block_tables, const int32_t* contex
 
 namespace {
 
+// Split-K scratch of paged_attn_decode_noalloc: the partition partials of one
+// call, in the layout of the decode workspace. Each GPU holds its own copy for
+// the life of the process; every call on a GPU reuses it (so calls that
+// overlap on one GPU race). Host code never uses the array's name as an
+// address: noalloc_scratch looks up each device's copy once.
+static __device__ __align__(256) unsigned char scratch[PA_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch[kMaxDevices];
+
+// Device address of `scratch` on the device `stream` runs on (the current
+// device for the null stream), looked up with that device current on its
+// first use and kept.
+pa_status_t noalloc_scratch(hipStream_t stream, void** ptr) {
+  int dev = 0;
+  hipError_t e = stream ? hipStreamGetDevice(stream, &dev) : hipGetDevice(&dev);
+  if (e != hipSuccess)
+    return fail(PA_ERR_HIP, "cannot find the stream's device: %s", hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices)
+    return fail(PA_ERR_UNSUPPORTED, "device %d: the no-allocation scratch serves devices "
+                "0..%d", dev, kMaxDevices - 1);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch[dev]) {
+    int cur = 0;
+    e = hipGetDevice(&cur);
+    const bool other = e == hipSuccess && cur != dev;
+    if (other) e = hipSetDevice(dev);
+    void* p = nullptr;
+    if (e == hipSuccess) e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    const hipError_t back = other ? hipSetDevice(cur) : hipSuccess;
+    if (e != hipSuccess || back != hipSuccess || !p)
+      return fail(PA_ERR_HIP, "no-allocation scratch lookup on device %d failed: %s", dev,
+                  hipGetErrorString(e != hipSuccess ? e : back));
+    g_scratch[dev] = p;
+  }
+  *ptr = g_scratch[dev];
+  return PA_OK;
+}
+
 pa_status_t decode_impl(void* out, const void* q, const void* k_cache, const void* v_cache,
                         const int32_t* block_tables, const int32_t* context_lens,
                         const float* attn_bias, const int64_t* bias_start,
@@ -315,7 +356,7 @@ pa_status_t decode_impl(void* out, const void* q, const void* k_cache, const voi
                         int32_t head_dim, int32_t block_size, int32_t max_blocks_per_seq,
                         int32_t max_seq_len, int64_t num_blocks, pa_dtype_t dtype,
                         int32_t partition_tokens, void* workspace, size_t workspace_bytes,
-                        void* stream, int32_t chunk = 0) {
+                        void* stream, int32_t chunk = 0, bool noalloc = false) {
   pa_status_t st = check_common(out, q, k_cache, v_cache, block_tables, context_lens, attn_bias,
                                 sliding_window, scale, num_seqs, num_heads, num_kv_heads,
                                 head_dim, block_size, max_blocks_per_seq, max_seq_len,
@@ -335,6 +376,16 @@ pa_status_t decode_impl(void* out, const void* q, const void* k_cache, const voi
                                       chunk > 0 ? chunk : sliding_window, partition_tokens);
   if (plan.num_partitions > 65535)
     return fail(PA_ERR_INVALID_ARG, "too many partitions (%d)", plan.num_partitions);
+  if (noalloc && plan.ws_bytes > 0) {
+    if (plan.ws_bytes > PA_NOALLOC_SCRATCH_BYTES)
+      return fail(PA_ERR_WORKSPACE, "this shape needs %zu bytes of split-K scratch; the "
+                  "no-allocation entry point holds %zu (use paged_attn_decode with a "
+                  "workspace, or longer partitions)", plan.ws_bytes,
+                  (size_t)PA_NOALLOC_SCRATCH_BYTES);
+    st = noalloc_scratch(static_cast<hipStream_t>(stream), &workspace);
+    if (st != PA_OK) return st;
+    workspace_bytes = PA_NOALLOC_SCRATCH_BYTES;
+  }
   if (plan.ws_bytes > 0) {
     if (!workspace || workspace_bytes < plan.ws_bytes)
       return fail(PA_ERR_WORKSPACE, "decode workspace of %zu bytes needed, %zu given (%p)",
@@ -457,6 +508,20 @@ pa_status_t paged_attn_decode(void* out, const void* q, const void* k_cache,
                      nullptr, sliding_window, scale, num_seqs, num_heads, num_kv_heads, head_dim,
                      block_size, max_blocks_per_seq, max_seq_len, num_blocks, dtype,
                      partition_tokens, workspace, workspace_bytes, stream);
+}
+
+pa_status_t paged_attn_decode_noalloc(void* out, const void* q, const void* k_cache,
+                                      const void* v_cache, const int32_t* block_tables,
+                                      const int32_t* context_lens, const float* attn_bias,
+                                      int32_t sliding_window, float scale, int32_t num_seqs,
+                                      int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
+                                      int32_t block_size, int32_t max_blocks_per_seq,
+                                      int32_t max_seq_len, int64_t num_blocks, pa_dtype_t dtype,
+                                      int32_t partition_tokens, void* stream) {
+  return decode_impl(out, q, k_cache, v_cache, block_tables, context_lens, attn_bias, nullptr,
+                     nullptr, sliding_window, scale, num_seqs, num_heads, num_kv_heads, head_dim,
+                     block_size, max_blocks_per_seq, max_seq_len, num_blocks, dtype,
+                     partition_tokens, nullptr, 0, stream, 0, true);
 }
 
 pa_status_t paged_attn_decode_relpos(void* out, const void* q, const void* k_cache,
