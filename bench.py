@@ -6,11 +6,18 @@ block permutation). One step = one paged_attn_decode call = one decode step of
 one attention layer for all 256 sequences; throughput is decode tokens/s
 (sequences served per second) and the achieved HBM bandwidth of the call.
 
+The default run also measures the other workloads of the path and reports each
+as an entry of "configs" in the same line: T5-small self-attention decode and
+T5-large cross-attention decode (cold caches, median single call), and the
+12-layer ModernBERT-shaped encoder prefill in fp32 and in bf16. Every entry
+carries its time per step, its roofline fraction and its own CPU baseline.
+
 Timing: W untimed warm-up steps, further untimed steps until 0.3 s of warm-up
 have passed (the GPU's clocks ramp over the first ~0.1 s of load), then exactly
 K steps between two HIP events on the stream the library launches on, with a
 device synchronisation on both sides. The CPU baseline times the float64
-oracle on the same workload (repeated to ~10 s of CPU work).
+oracle, as it stands, on a bounded sample of the same inputs, at all the
+threads it gets and at one thread, and names the host CPU.
 
 Prints ONE JSON line. Options:
   --gpus N        only 1 is supported (the path runs on one GPU)
@@ -20,34 +27,51 @@ Prints ONE JSON line. Options:
                   modernbert_prefill_bf16 | modernbert_chunked_prefill_f32 |
                   modernbert_chunked_prefill_bf16 (one layer, 128-token chunks) |
                   t5_small_self_decode_bf16 | t5_large_cross_decode_bf16 (cold-cache
-                  median of single calls) | kv_write_modernbert_f32 | copy_probe (a plain device copy of
-                  known size, for calibrating the rocprofv3 byte counters)
+                  median of single calls) | kv_write_modernbert_f32 | copy_probe (a plain
+                  device copy of known size, for calibrating the rocprofv3 byte counters)
   --no-cpu-baseline   skip the oracle timing
   --no-variants       skip the window / chunk / null-bias / no-bias-build variants
+  --no-configs        default workload only: skip the other workloads' entries
+  --profile-run       warm-up, settle and the K timed steps only, nothing after them
+                      (no variants, single-call timings or baselines): under
+                      rocprofv3 the last K steps' dispatches are the timed ones
+  --write-profiles X  write profiles/X_kernel_trace.md and profiles/X_traffic.txt
+                      from rocprofv3 output of --profile-run runs of workload X
+                      (see write_profiles for the arguments)
 """
 from __future__ import annotations
 
 import argparse
+import csv
+import glob
 import hashlib
 import json
 import math
 import os
+import statistics
 import sys
 import time
 
 import numpy as np
-import torch
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
-import sliding_window_mask_amd as pa  # noqa: E402
-import workloads  # noqa: E402
-
 METRIC = "decode tokens/s and achieved HBM GB/s (% of MI355X peak), biased paged attn"
 HBM_PEAK_GBPS = 8000.0
 FP32_MFMA_PEAK_TFLOPS = 157.3
+BF16_MFMA_PEAK_TFLOPS = 2500.0
 PROFILES = os.path.join(ROOT, "profiles")
+
+# kernel source each workload's dominant kernels are built from
+KERNEL_SOURCE = {
+    "large_biased_decode_bf16": "pa_decode.hip",
+    "t5_small_self_decode_bf16": "pa_decode.hip",
+    "t5_large_cross_decode_bf16": "pa_decode.hip",
+    "modernbert_prefill_f32": "pa_prefill.hip",
+    "modernbert_prefill_bf16": "pa_prefill_bf16.hip",
+    "kv_write_modernbert_f32": "pa_cache.hip",
+}
 
 
 def log(msg):
@@ -79,6 +103,25 @@ def read_traffic(workload, kernel_src, key="hbm_bytes_per_launch"):
         return None
 
 
+def cpu_model():
+    """Model name of the host CPU: lscpu's "Model name", else /proc/cpuinfo's."""
+    import subprocess
+    try:
+        out = subprocess.run(["lscpu"], capture_output=True, text=True, timeout=10).stdout
+        for ln in out.splitlines():
+            if ln.strip().lower().startswith("model name"):
+                return ln.split(":", 1)[1].strip()
+    except (OSError, subprocess.SubprocessError):
+        pass
+    try:
+        for ln in open("/proc/cpuinfo"):
+            if ln.lower().startswith("model name"):
+                return ln.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 SETTLE_S = 0.3     # untimed run time before the timed steps, for the clocks to ramp
 
 
@@ -87,6 +130,7 @@ def time_steps(fn, steps, warmup):
     of warmup have passed (an idle MI355X ramps its clocks over the first
     ~0.1 s of sustained work; short steps otherwise get timed at low clock),
     then exactly `steps` timed steps between two events."""
+    import torch
     t0 = time.perf_counter()
     for _ in range(warmup):
         fn()
@@ -107,6 +151,7 @@ def time_steps(fn, steps, warmup):
 def per_call_ms(fn, n):
     """Distribution of single-call times (each call between its own pair of
     events, after the timed region): median, p10, p90."""
+    import torch
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
           for _ in range(n)]
     for s, e in ev:
@@ -119,8 +164,26 @@ def per_call_ms(fn, n):
             "p90": float(np.percentile(t, 90))}
 
 
+def cold_call_times(fn, steps, warmup, flush):
+    """Single calls after an L2 + Infinity Cache flush (a 1 GiB write, outside
+    the timed interval), each between its own pair of events."""
+    import torch
+    for _ in range(warmup):
+        fn()
+    times = []
+    for _ in range(steps):
+        flush.zero_()
+        s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        s.record()
+        fn()
+        e.record()
+        torch.cuda.synchronize()
+        times.append(s.elapsed_time(e))
+    return times
+
+
 # ----------------------------------------------------------------------------
-# decode
+# algorithmic work
 # ----------------------------------------------------------------------------
 def decode_bytes(lens, H, D, esize, window, with_bias, chunk=0):
     """Algorithmic HBM bytes of one decode call: for every (sequence, head)
@@ -138,9 +201,83 @@ def decode_bytes(lens, H, D, esize, window, with_bias, chunk=0):
     return int(H * np.sum(n_vis * per_tok + 2 * D * esize))
 
 
-def compact_sample(case, seqs):
+def prefill_flops(lens, H, D, window, chunk=0):
+    """Algorithmic flops of a bidirectional prefill layer: 4*D per visible
+    (query, key) pair, every pair of a sequence, |i - j| < W with a window, or
+    pairs inside one chunk of C positions with chunked local attention."""
+    L = lens.astype(np.int64)
+    if chunk > 0:
+        full, rem = L // chunk, L % chunk
+        return int(4 * D * H * np.sum(full * chunk * chunk + rem * rem))
+    if window > 0:
+        W = np.minimum(window, L)
+        pairs = L * (2 * W - 1) - W * (W - 1)
+    else:
+        pairs = L * L
+    return int(4 * D * H * np.sum(pairs))
+
+
+def prefill_bytes(lens, H, D, esize):
+    """Algorithmic HBM bytes of an encoder prefill layer: q, K and V read once
+    and out written once over the valid tokens."""
+    return int(4 * int(np.sum(lens.astype(np.int64))) * H * D * esize)
+
+
+# ----------------------------------------------------------------------------
+# the oracle beside the GPU
+# ----------------------------------------------------------------------------
+def _sample_rates(prepare, n_total, target_s, single_s, describe):
+    """Time the oracle as it stands. `prepare(seqs)` makes host copies of the
+    inputs of the sequences `seqs` (not timed) and returns a function that
+    runs the oracle on them and returns (units of work, max |gpu - oracle|).
+    A one-sequence run estimates the cost, the sample is sized to ~target_s of
+    oracle time at the oracle's thread count (the whole workload, repeated on
+    the same inputs, when it takes less), then at one thread to ~single_s."""
+    import oracle
+    oracle.build(force=False)
+    rng = np.random.default_rng(12345)
+
+    def size_for(sec, per_seq):
+        return int(min(n_total, max(1, math.floor(sec / max(per_seq, 1e-9)))))
+
+    def go(n, min_s):
+        seqs = np.sort(rng.choice(n_total, size=n, replace=False))
+        run = prepare(seqs)
+        reps, units, err, dt = 0, 0, 0.0, 0.0
+        while True:
+            t0 = time.perf_counter()
+            u, e = run()
+            dt += time.perf_counter() - t0
+            units, err, reps = units + u, max(err, e), reps + 1
+            if dt >= min_s or reps >= 1000:
+                return n, reps, units, dt, err
+
+    _, _, _, dt, _ = go(1, 0.0)
+    n = size_for(target_s, dt)
+    n, reps, units, dt, err = go(n, target_s if n == n_total else 0.0)
+    threads = oracle.num_threads()
+    oracle.set_num_threads(1)
+    try:
+        _, _, _, dt1, _ = go(1, 0.0)
+        n1 = size_for(single_s, dt1)
+        n1, reps1, units1, dt1, _ = go(n1, single_s if n1 == n_total else 0.0)
+    finally:
+        oracle.set_num_threads(threads)
+    return {"value": units / dt, "cores": threads, "kind": "oracle",
+            "cpu_model": cpu_model(), "host_logical_cpus": os.cpu_count(),
+            "sample": "%s; %d of the %d sequences, %d pass(es), %.1f s of oracle time "
+                      "(host copies of the inputs made beforehand, not timed)"
+                      % (describe, n, n_total, reps, dt),
+            "single_thread": {"value": units1 / dt1, "cores": 1,
+                              "sample": "%d sequences, %d pass(es), %.1f s"
+                                        % (n1, reps1, dt1)},
+            "gpu_vs_oracle_max_abs_err_on_sample": err}
+
+
+def compact_decode_sample(case, seqs):
     """Host copies of the inputs of a subset of sequences, with a compact cache
     holding only the blocks they reference (for the oracle)."""
+    import torch
     idx = torch.as_tensor(seqs, dtype=torch.long, device=case.block_tables.device)
     bt = case.block_tables[idx].cpu()
     used = torch.unique(bt)
@@ -153,55 +290,87 @@ def compact_sample(case, seqs):
                 bias=None if case.attn_bias is None else case.attn_bias[idx].cpu())
 
 
-def cpu_baseline_decode(case, out_gpu):
-    """Time the float64 oracle (as it stands) on a bounded sample of the same
-    workload; also report the GPU-vs-oracle error on that sample."""
+def cpu_baseline_decode(case, out_gpu, target_s=10.0, single_s=5.0):
+    """The float64 oracle (as it stands) on a bounded sample of a decode
+    workload's sequences (all heads, whole contexts); the rate is decode
+    tokens/s (sequences per second), like the GPU line."""
+    import torch
     import oracle
-    oracle.build(force=False)
-    rng = np.random.default_rng(12345)
 
-    target_s = 15.0
+    def prepare(seqs):
+        s = compact_decode_sample(case, seqs)
+        g = out_gpu[torch.as_tensor(seqs, device=out_gpu.device)].float().cpu().double().numpy()
 
-    def run(n, min_s=0.0):
-        """Oracle on n sequences, repeated (same inputs) until min_s seconds."""
-        seqs = np.sort(rng.choice(case.num_seqs, size=n, replace=False))
-        s = compact_sample(case, seqs)
-        reps, t0 = 0, time.perf_counter()
-        while True:
+        def run():
             ref = oracle.decode(s["q"], s["k"], s["v"], s["bt"], s["cl"], s["bias"],
                                 case.sliding_window, case.scale, case.max_seq_len)
-            reps += 1
-            dt = time.perf_counter() - t0
-            if dt >= min_s or reps >= 100:
-                break
-        g = out_gpu[torch.as_tensor(seqs, device=out_gpu.device)].float().cpu().double().numpy()
-        return n, reps, dt, float(np.max(np.abs(g - ref)))
+            return len(seqs), float(np.max(np.abs(g - ref)))
+        return run
 
-    n, _, dt, _ = run(4)                                  # rate estimate
-    n = int(min(case.num_seqs, max(4, math.floor(target_s / max(dt / n, 1e-6)))))
-    # the whole workload can take well under the target: repeat it, so the
-    # rate comes from ~10 s of CPU work
-    n, reps, dt, err = run(n, min_s=10.0 if n == case.num_seqs else 0.0)
-    threads = oracle.num_threads()
-    # the same oracle on one thread, on a smaller sample (~5 s)
-    n1 = max(1, min(case.num_seqs, int(5.0 * n * reps / dt / max(threads, 1))))
-    oracle.set_num_threads(1)
-    try:
-        n1, reps1, dt1, _ = run(n1)
-    finally:
-        oracle.set_num_threads(threads)
-    return {"value": n * reps / dt, "unit": "tokens/s", "cores": threads,
-            "kind": "oracle",
-            "sample": "%d of the %d sequences (all 32 heads, their full contexts), "
-                      "float64 C loop over the block table, %d pass(es) in %.1f s"
-                      % (n, case.num_seqs, reps, dt),
-            "single_thread": {"value": n1 * reps1 / dt1, "unit": "tokens/s", "cores": 1,
-                              "sample": "%d sequences, %d pass(es) in %.1f s"
-                                        % (n1, reps1, dt1)},
-            "gpu_vs_oracle_max_abs_err_on_sample": err}
+    r = _sample_rates(prepare, case.num_seqs, target_s, single_s,
+                      "float64 C loop over the block table, all %d heads and whole contexts"
+                      % case.num_heads)
+    r["unit"] = r["single_thread"]["unit"] = "tokens/s"
+    return r
 
 
+def cpu_baseline_prefill(layers, outs, target_s=8.0, single_s=4.0):
+    """The float64 oracle on a bounded sample of the encoder batch: every
+    layer of the step for the sampled sequences (all heads, all queries); the
+    rate is tokens through the 12 layers per second, like the GPU line."""
+    import torch
+    import oracle
+    qsl = layers[0].query_start_loc.cpu()
+
+    def prepare(seqs):
+        rows = torch.cat([torch.arange(int(qsl[s]), int(qsl[s + 1])) for s in seqs])
+        nq = torch.tensor([int(qsl[s + 1] - qsl[s]) for s in seqs], dtype=torch.int32)
+        new_qsl = torch.zeros(len(seqs) + 1, dtype=torch.int32)
+        new_qsl[1:] = torch.cumsum(nq, 0)
+        idx = torch.as_tensor(seqs, dtype=torch.long)
+        host = []
+        for c, o in zip(layers, outs):
+            bt = c.block_tables.cpu()[idx]
+            used = torch.unique(bt)
+            remap = torch.full((c.num_blocks,), -1, dtype=torch.int32)
+            remap[used] = torch.arange(used.numel(), dtype=torch.int32)
+            dev_used = used.to(c.k_cache.device)
+            host.append((c, c.q[rows.to(c.q.device)].cpu(), c.k_cache[dev_used].cpu(),
+                         c.v_cache[dev_used].cpu(), remap[bt.long()], c.context_lens.cpu()[idx],
+                         o[rows.to(o.device)].float().cpu().double().numpy()))
+
+        def run():
+            err = 0.0
+            for c, q, k, v, bt, cl, g in host:
+                ref = oracle.prefill(q, k, v, bt, cl, new_qsl, None, c.sliding_window, 0,
+                                     c.scale, c.max_seq_len)
+                err = max(err, float(np.max(np.abs(g - ref))) if g.size else 0.0)
+            return int(nq.sum()), err
+        return run
+
+    r = _sample_rates(prepare, layers[0].num_seqs, target_s, single_s,
+                      "float64 C loop over the block table, all %d layers, heads and queries "
+                      "of each sampled sequence" % len(layers))
+    r["unit"] = r["single_thread"]["unit"] = "tokens/s (12 layers)"
+    return r
+
+
+def _line(metric, value, unit, ms, args, dtype, config, **extra):
+    d = {"metric": metric, "value": value, "unit": unit, "n_gpus": 1, "steps": args.steps,
+         "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True,
+         "scaling": "weak", "vs_baseline": None, "dtype": dtype, "data": "synthetic",
+         "config": config}
+    d.update(extra)
+    return d
+
+
+# ----------------------------------------------------------------------------
+# decode
+# ----------------------------------------------------------------------------
 def bench_decode(args):
+    import torch
+    import sliding_window_mask_amd as pa
+    import workloads
     t0 = time.time()
     case = workloads.large_biased_decode_bf16(device="cuda")
     torch.cuda.synchronize()
@@ -223,25 +392,22 @@ def bench_decode(args):
     gbps = nbytes / (ms * 1e-3) / 1e9
     tokens_per_s = B / (ms * 1e-3)
     log("decode: %.4f ms/step, %.0f tokens/s, %.1f GB/s" % (ms, tokens_per_s, gbps))
-    traffic = read_traffic("decode_large_biased_bf16", "pa_decode.hip")
-    line = {
-        "metric": METRIC, "value": tokens_per_s, "unit": "tokens/s", "n_gpus": 1,
-        "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms,
-        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
-        "data": "synthetic",
-        "config": {"workload": "large_biased_decode_bf16", "num_seqs": B, "num_heads": H,
-                   "head_dim": D, "block_size": 16, "context_lens": "uniform [1024, 4096]",
-                   "num_blocks": case.num_blocks, "max_seq_len": case.max_seq_len,
-                   "attn_bias": "fp32 [256, 32, 4096] N(0,1)", "sliding_window": -1,
-                   "partition_tokens": P, "parallelism": "single GPU"},
-        "achieved_GBps": gbps,
-        "algorithmic_bytes_per_step": nbytes,
-        "roofline": {"bound": "hbm", "achieved": gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": gbps / HBM_PEAK_GBPS,
-                     "traffic": traffic,
-                     "kernel": "paged_attn_decode call: pa_decode_partition" +
-                               ("" if ws is None else " + pa_decode_merge")},
-    }
+    traffic = read_traffic("large_biased_decode_bf16", "pa_decode.hip")
+    line = _line(
+        METRIC, tokens_per_s, "tokens/s", ms, args, "bf16",
+        {"workload": "large_biased_decode_bf16", "num_seqs": B, "num_heads": H,
+         "head_dim": D, "block_size": 16, "context_lens": "uniform [1024, 4096]",
+         "num_blocks": case.num_blocks, "max_seq_len": case.max_seq_len,
+         "attn_bias": "fp32 [256, 32, 4096] N(0,1)", "sliding_window": -1,
+         "partition_tokens": P, "parallelism": "single GPU"},
+        achieved_GBps=gbps, algorithmic_bytes_per_step=nbytes,
+        launches_per_step=1 if ws is None else 2,
+        roofline={"bound": "hbm", "achieved": gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                  "frac": gbps / HBM_PEAK_GBPS, "traffic": traffic,
+                  "kernel": "paged_attn_decode call: pa_decode_partition" +
+                            ("" if ws is None else " + pa_decode_merge")})
+    if args.profile_run:
+        return line
     line["per_call_ms"] = per_call_ms(step, max(args.steps, 20))
     if not args.no_variants:
         var = {}
@@ -303,122 +469,13 @@ def bench_decode(args):
     return line
 
 
-# ----------------------------------------------------------------------------
-# prefill (12-layer ModernBERT-shaped encoder)
-# ----------------------------------------------------------------------------
-def prefill_flops(lens, H, D, window, chunk=0):
-    """Algorithmic flops of a bidirectional prefill layer: 4*D per visible
-    (query, key) pair, every pair of a sequence, |i - j| < W with a window, or
-    pairs inside one chunk of C positions with chunked local attention."""
-    L = lens.astype(np.int64)
-    if chunk > 0:
-        full, rem = L // chunk, L % chunk
-        return int(4 * D * H * np.sum(full * chunk * chunk + rem * rem))
-    if window > 0:
-        W = np.minimum(window, L)
-        pairs = L * (2 * W - 1) - W * (W - 1)
-    else:
-        pairs = L * L
-    return int(4 * D * H * np.sum(pairs))
-
-
-BF16_MFMA_PEAK_TFLOPS = 2500.0
-
-
-def bench_prefill(args, dtype=torch.float32):
-    if dtype == torch.float32:
-        layers = [workloads.modernbert_prefill_f32(l, device="cuda")
-                  for l in range(workloads.MODERNBERT_LAYERS)]
-    else:
-        layers = [workloads.prefill_case(4, num_seqs=32, num_heads=12, head_dim=64,
-                                         lens=(64, 1024), max_seq_len=1024, dtype=dtype,
-                                         sliding_window=workloads.modernbert_window(l),
-                                         device="cuda", layer_seed=[4, l])
-                  for l in range(workloads.MODERNBERT_LAYERS)]
-    torch.cuda.synchronize()
-    outs = [torch.empty_like(c.q) for c in layers]
-    lib = pa.lib()
-
-    def step():
-        for c, o in zip(layers, outs):
-            lib.paged_attn_prefill(c.q, c.k_cache, c.v_cache, c.block_tables, c.context_lens,
-                                   c.query_start_loc, None, c.sliding_window, False, c.scale,
-                                   max_seq_len=c.max_seq_len, out=o)
-
-    ms = time_steps(step, args.steps, args.warmup)
-    c0 = layers[0]
-    flops = sum(prefill_flops(c.lens, 12, 64, c.sliding_window) for c in layers)
-    tflops = flops / (ms * 1e-3) / 1e12
-    tokens = int(c0.lens.sum())
-    peak = FP32_MFMA_PEAK_TFLOPS if dtype == torch.float32 else BF16_MFMA_PEAK_TFLOPS
-    tag = "f32" if dtype == torch.float32 else "bf16"
-    line = {
-        "metric": "encoder prefill tokens/s (12 layers) and MFMA TFLOP/s", "value":
-        tokens / (ms * 1e-3), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
-        "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak",
-        "vs_baseline": None, "dtype": tag, "data": "synthetic",
-        "config": {"workload": "modernbert_prefill_" + tag, "layers": 12, "num_seqs": 32,
-                   "num_heads": 12, "head_dim": 64, "context_lens": "uniform [64, 1024]",
-                   "windows": [workloads.modernbert_window(l) for l in range(12)]},
-        "roofline": {"bound": "mfma", "achieved": tflops, "peak": peak,
-                     "unit": "TFLOP/s", "frac": tflops / peak,
-                     # HBM bytes of one step (the 12 launches), from the counters
-                     "traffic": read_traffic("modernbert_prefill_" + tag,
-                                             "pa_prefill.hip" if tag == "f32"
-                                             else "pa_prefill_bf16.hip", "hbm_bytes_per_step"),
-                     "kernel": "pa_prefill_%s (12 launches per step)" % tag},
-        "algorithmic_flops_per_step": flops,
-    }
-    return line
-
-
-def bench_chunked_prefill(args, dtype=torch.float32):
-    """One ModernBERT-shaped layer (32 sequences of U[64,1024], 12 heads,
-    head_dim 64) with bidirectional chunked local attention in 128-token
-    chunks, through paged_attn_prefill_chunked."""
-    c = workloads.prefill_case(4, num_seqs=32, num_heads=12, head_dim=64, lens=(64, 1024),
-                               max_seq_len=1024, dtype=dtype, device="cuda", layer_seed=[4, 1])
-    torch.cuda.synchronize()
-    out = torch.empty_like(c.q)
-    lib = pa.lib()
-    ms = time_steps(lambda: lib.paged_attn_prefill_chunked(
-        c.q, c.k_cache, c.v_cache, c.block_tables, c.context_lens, c.query_start_loc, None,
-        128, False, c.scale, max_seq_len=c.max_seq_len, out=out), args.steps, args.warmup)
-    flops = prefill_flops(c.lens, 12, 64, -1, chunk=128)
-    tflops = flops / (ms * 1e-3) / 1e12
-    peak = FP32_MFMA_PEAK_TFLOPS if dtype == torch.float32 else BF16_MFMA_PEAK_TFLOPS
-    tag = "f32" if dtype == torch.float32 else "bf16"
-    return {
-        "metric": "chunked-local prefill tokens/s (one layer) and MFMA TFLOP/s",
-        "value": int(c.lens.sum()) / (ms * 1e-3), "unit": "tokens/s", "n_gpus": 1,
-        "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms,
-        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": tag,
-        "data": "synthetic",
-        "config": {"workload": "modernbert_chunked_prefill_" + tag, "layers": 1,
-                   "num_seqs": 32, "num_heads": 12, "head_dim": 64,
-                   "context_lens": "uniform [64, 1024]", "chunk_size": 128},
-        "roofline": {"bound": "mfma", "achieved": tflops, "peak": peak, "unit": "TFLOP/s",
-                     "frac": tflops / peak, "traffic": None,
-                     "kernel": "pa_prefill_%s (banded variant, one launch)" % tag},
-        "algorithmic_flops_per_step": flops,
-    }
-
-
-def bench_copy(args):
-    """A plain device-to-device copy of known size (256 MiB read + 256 MiB
-    written per launch), used to calibrate the rocprofv3 byte counters."""
-    n = 256 << 20
-    src = torch.empty(n, dtype=torch.uint8, device="cuda").random_(0, 255)
-    dst = torch.empty_like(src)
-    ms = time_steps(lambda: dst.copy_(src), args.steps, args.warmup)
-    return {"metric": "copy probe GB/s", "value": 2 * n / (ms * 1e-3) / 1e9, "unit": "GB/s",
-            "bytes_read_per_launch": n, "bytes_written_per_launch": n, "ms_per_step": ms,
-            "steps": args.steps, "warmup": args.warmup, "n_gpus": 1}
-
-
 def bench_small_decode(args, name):
     """T5-shaped decode workloads (small working sets: an L2 + Infinity Cache
-    flush precedes every timed call, and each call is timed on its own)."""
+    flush precedes every timed call, and each call is timed on its own; the
+    median is the step time)."""
+    import torch
+    import sliding_window_mask_amd as pa
+    import workloads
     if name == "t5_small_self_decode_bf16":
         case = workloads.t5_small_self_decode_bf16(device="cuda")
     else:
@@ -429,64 +486,215 @@ def bench_small_decode(args, name):
     ws = lib.workspace_for(case.q, case.max_seq_len, case.sliding_window)
     flush = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
 
-    def call():
+    def call(bias="case", o=out):
         lib.paged_attn_decode(case.q, case.k_cache, case.v_cache, case.block_tables,
-                              case.context_lens, case.attn_bias, case.sliding_window,
-                              case.scale, max_seq_len=case.max_seq_len, out=out, workspace=ws)
+                              case.context_lens, case.attn_bias if bias == "case" else bias,
+                              case.sliding_window, case.scale, max_seq_len=case.max_seq_len,
+                              out=o, workspace=ws)
 
-    for _ in range(args.warmup):
-        call()
-    times = []
-    for _ in range(args.steps):
-        flush.zero_()
-        s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        s.record()
-        call()
-        e.record()
-        torch.cuda.synchronize()
-        times.append(s.elapsed_time(e))
+    times = cold_call_times(call, args.steps, args.warmup, flush)
     ms = float(np.median(times))
-    nbytes = decode_bytes(case.lens, H, D, 2, -1, case.attn_bias is not None)
+    with_bias = case.attn_bias is not None
+    nbytes = decode_bytes(case.lens, H, D, 2, -1, with_bias)
+    gbps = nbytes / (ms * 1e-3) / 1e9
+    if name == "t5_small_self_decode_bf16":
+        cfg = {"workload": name, "config": "T5-small-shaped decoder self-attention decode",
+               "num_seqs": B, "num_heads": H, "head_dim": D, "context_lens": "uniform [32, 512]",
+               "attn_bias": "fp32 [64, 8, 512] materialised from a 32-bucket T5 table "
+                            "(max distance 128)"}
+    else:
+        cfg = {"workload": name, "config": "T5-large-shaped cross-attention decode",
+               "num_seqs": B, "num_heads": H, "head_dim": D,
+               "context_lens": "encoder lengths uniform [128, 512], separate cross table",
+               "attn_bias": "null (and a zero bias, bit-identical)"}
+    cfg["partition_tokens"] = lib.pa_decode_default_partition(B, H, D, case.max_seq_len, -1)
+    line = _line("decode tokens/s and achieved HBM GB/s (cold caches, median call)",
+                 B / (ms * 1e-3), "tokens/s", ms, args, "bf16", cfg,
+                 p10_ms=float(np.percentile(times, 10)),
+                 p90_ms=float(np.percentile(times, 90)),
+                 timing="cold caches (1 GiB flush before each call), median of %d single "
+                        "calls" % args.steps,
+                 algorithmic_bytes_per_step=nbytes, launches_per_step=1 if ws is None else 2,
+                 roofline={"bound": "hbm", "achieved": gbps, "peak": HBM_PEAK_GBPS,
+                           "unit": "GB/s", "frac": gbps / HBM_PEAK_GBPS,
+                           "traffic": read_traffic(name, "pa_decode.hip"),
+                           "kernel": "paged_attn_decode call"})
+    if args.profile_run:
+        return line
     extra = {}
     if case.t5_table is not None:
         # the same T5 bias computed in the kernel from the [8, 32] bucket table
-        rt = []
-        for _ in range(args.steps):
-            flush.zero_()
-            s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            s.record()
-            lib.paged_attn_decode_relpos(case.q, case.k_cache, case.v_cache, case.block_tables,
-                                         case.context_lens, case.t5_table, 32, 128, 0, -1,
-                                         case.scale, max_seq_len=case.max_seq_len, out=out,
-                                         workspace=ws)
-            e.record()
-            torch.cuda.synchronize()
-            rt.append(s.elapsed_time(e))
+        rt = cold_call_times(lambda: lib.paged_attn_decode_relpos(
+            case.q, case.k_cache, case.v_cache, case.block_tables, case.context_lens,
+            case.t5_table, 32, 128, 0, -1, case.scale, max_seq_len=case.max_seq_len, out=out,
+            workspace=ws), args.steps, args.warmup, flush)
         mr = float(np.median(rt))
         extra["t5_bias_in_kernel"] = {"ms_per_step": mr, "tokens_per_s": B / (mr * 1e-3),
                                       "GBps": decode_bytes(case.lens, H, D, 2, -1, False) /
                                       (mr * 1e-3) / 1e9}
-    gbps = nbytes / (ms * 1e-3) / 1e9
-    return {"metric": "decode tokens/s and achieved HBM GB/s (cold caches, median call)",
-            "value": B / (ms * 1e-3), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
-            "warmup": args.warmup, "ms_per_step": ms, "p10_ms": float(np.percentile(times, 10)),
-            "p90_ms": float(np.percentile(times, 90)), "higher_is_better": True,
-            "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
-            "config": {"workload": name, "num_seqs": B, "num_heads": H, "head_dim": D,
-                       "partition_tokens": lib.pa_decode_default_partition(
-                           B, H, D, case.max_seq_len, -1),
-                       "attn_bias": None if case.attn_bias is None else "fp32 (T5 buckets)"},
-            "roofline": {"bound": "hbm", "achieved": gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                         "frac": gbps / HBM_PEAK_GBPS,
-                         "traffic": read_traffic(name, "pa_decode.hip"),
-                         "kernel": "paged_attn_decode call"},
-            "algorithmic_bytes_per_step": nbytes, "variants": extra}
+    else:
+        # the zero-bias run of the cross-attention workload: identical output
+        zero = torch.zeros(B, H, case.max_seq_len, device="cuda")
+        out_zero = torch.empty_like(out)
+        zt = cold_call_times(lambda: call(bias=zero, o=out_zero), args.steps, args.warmup,
+                             flush)
+        call()
+        torch.cuda.synchronize()
+        mz = float(np.median(zt))
+        extra["zero_bias"] = {"ms_per_step": mz, "tokens_per_s": B / (mz * 1e-3),
+                              "GBps": decode_bytes(case.lens, H, D, 2, -1, True) /
+                              (mz * 1e-3) / 1e9,
+                              "bit_identical_to_null_bias": bool(torch.equal(
+                                  out.view(torch.int16), out_zero.view(torch.int16)))}
+    line["variants"] = extra
+    if not args.no_cpu_baseline:
+        call()
+        torch.cuda.synchronize()
+        line["cpu_baseline"] = cpu_baseline_decode(case, out, target_s=6.0, single_s=3.0)
+    return line
+
+
+# ----------------------------------------------------------------------------
+# prefill (12-layer ModernBERT-shaped encoder)
+# ----------------------------------------------------------------------------
+def modernbert_layers(dtype):
+    import workloads
+    return [workloads.prefill_case(4, num_seqs=32, num_heads=12, head_dim=64,
+                                   lens=(64, 1024), max_seq_len=1024, dtype=dtype,
+                                   sliding_window=workloads.modernbert_window(l),
+                                   device="cuda", layer_seed=[4, l])
+            for l in range(workloads.MODERNBERT_LAYERS)]
+
+
+def bench_prefill(args, dtype_name="f32"):
+    import torch
+    import sliding_window_mask_amd as pa
+    import workloads
+    dtype = torch.float32 if dtype_name == "f32" else torch.bfloat16
+    layers = modernbert_layers(dtype)
+    torch.cuda.synchronize()
+    outs = [torch.empty_like(c.q) for c in layers]
+    lib = pa.lib()
+
+    def run_layer(c, o, bias=None):
+        lib.paged_attn_prefill(c.q, c.k_cache, c.v_cache, c.block_tables, c.context_lens,
+                               c.query_start_loc, bias, c.sliding_window, False, c.scale,
+                               max_seq_len=c.max_seq_len, out=o)
+
+    def step():
+        for c, o in zip(layers, outs):
+            run_layer(c, o)
+
+    ms = time_steps(step, args.steps, args.warmup)
+    c0 = layers[0]
+    esize = 4 if dtype_name == "f32" else 2
+    flops = sum(prefill_flops(c.lens, 12, 64, c.sliding_window) for c in layers)
+    nbytes = sum(prefill_bytes(c.lens, 12, 64, esize) for c in layers)
+    tflops = flops / (ms * 1e-3) / 1e12
+    tokens = int(c0.lens.sum())
+    peak = FP32_MFMA_PEAK_TFLOPS if dtype_name == "f32" else BF16_MFMA_PEAK_TFLOPS
+    wl = "modernbert_prefill_" + dtype_name
+    line = _line(
+        "encoder prefill tokens/s (12 layers) and MFMA TFLOP/s", tokens / (ms * 1e-3),
+        "tokens/s", ms, args, dtype_name,
+        {"workload": wl,
+         "config": "ModernBERT-base-shaped encoder-only bidirectional prefill" +
+                   ("" if dtype_name == "f32" else " (bf16 variant)"),
+         "layers": 12, "num_seqs": 32, "num_heads": 12, "head_dim": 64,
+         "context_lens": "uniform [64, 1024]", "attn_bias": None,
+         "windows": [workloads.modernbert_window(l) for l in range(12)]},
+        algorithmic_flops_per_step=flops, algorithmic_bytes_per_step=nbytes,
+        launches_per_step=len(layers),
+        roofline={"bound": "mfma", "achieved": tflops, "peak": peak, "unit": "TFLOP/s",
+                  "frac": tflops / peak,
+                  # HBM bytes of one step (the 12 launches), from the counters
+                  "traffic": read_traffic(wl, KERNEL_SOURCE[wl], "hbm_bytes_per_step"),
+                  "kernel": "pa_prefill_%s (12 launches per step)" % dtype_name})
+    if args.profile_run:
+        return line
+    # per layer kind, and one full-attention layer with a materialised bias
+    full = [i for i, c in enumerate(layers) if c.sliding_window < 0]
+    win = [i for i, c in enumerate(layers) if c.sliding_window > 0]
+    var = {}
+    for kind, ids in (("full_attention_layer", full), ("window_64_layer", win)):
+        c, o = layers[ids[0]], outs[ids[0]]
+        msl = time_steps(lambda: run_layer(c, o), args.steps, args.warmup)
+        fl = prefill_flops(c.lens, 12, 64, c.sliding_window)
+        by = prefill_bytes(c.lens, 12, 64, esize)
+        var[kind] = {"ms_per_layer": msl, "TFLOPs": fl / (msl * 1e-3) / 1e12,
+                     "mfma_frac": fl / (msl * 1e-3) / 1e12 / peak,
+                     "GBps": by / (msl * 1e-3) / 1e9,
+                     "hbm_frac": by / (msl * 1e-3) / 1e9 / HBM_PEAK_GBPS}
+    c, o = layers[full[0]], outs[full[0]]
+    bias = torch.randn(c.num_seqs, 12, c.max_seq_len, c.max_seq_len, device="cuda")
+    msb = time_steps(lambda: run_layer(c, o, bias), args.steps, args.warmup)
+    fl = prefill_flops(c.lens, 12, 64, -1)
+    bias_bytes = 4 * 12 * int(np.sum(c.lens.astype(np.int64) ** 2))
+    var["full_attention_layer_with_bias"] = {
+        "ms_per_layer": msb, "TFLOPs": fl / (msb * 1e-3) / 1e12,
+        "attn_bias": "fp32 [32, 12, 1024, 1024] N(0,1), %d visible entries read"
+                     % (bias_bytes // 4),
+        "bias_GBps": bias_bytes / (msb * 1e-3) / 1e9,
+        "slowdown_vs_no_bias": msb / var["full_attention_layer"]["ms_per_layer"] - 1.0}
+    del bias
+    line["variants"] = var
+    if not args.no_cpu_baseline:
+        step()
+        torch.cuda.synchronize()
+        line["cpu_baseline"] = cpu_baseline_prefill(layers, outs)
+    return line
+
+
+def bench_chunked_prefill(args, dtype_name="f32"):
+    """One ModernBERT-shaped layer (32 sequences of U[64,1024], 12 heads,
+    head_dim 64) with bidirectional chunked local attention in 128-token
+    chunks, through paged_attn_prefill_chunked."""
+    import torch
+    import sliding_window_mask_amd as pa
+    import workloads
+    dtype = torch.float32 if dtype_name == "f32" else torch.bfloat16
+    c = workloads.prefill_case(4, num_seqs=32, num_heads=12, head_dim=64, lens=(64, 1024),
+                               max_seq_len=1024, dtype=dtype, device="cuda", layer_seed=[4, 1])
+    torch.cuda.synchronize()
+    out = torch.empty_like(c.q)
+    lib = pa.lib()
+    ms = time_steps(lambda: lib.paged_attn_prefill_chunked(
+        c.q, c.k_cache, c.v_cache, c.block_tables, c.context_lens, c.query_start_loc, None,
+        128, False, c.scale, max_seq_len=c.max_seq_len, out=out), args.steps, args.warmup)
+    flops = prefill_flops(c.lens, 12, 64, -1, chunk=128)
+    tflops = flops / (ms * 1e-3) / 1e12
+    peak = FP32_MFMA_PEAK_TFLOPS if dtype_name == "f32" else BF16_MFMA_PEAK_TFLOPS
+    return _line("chunked-local prefill tokens/s (one layer) and MFMA TFLOP/s",
+                 int(c.lens.sum()) / (ms * 1e-3), "tokens/s", ms, args, dtype_name,
+                 {"workload": "modernbert_chunked_prefill_" + dtype_name, "layers": 1,
+                  "num_seqs": 32, "num_heads": 12, "head_dim": 64,
+                  "context_lens": "uniform [64, 1024]", "chunk_size": 128},
+                 launches_per_step=1, algorithmic_flops_per_step=flops,
+                 roofline={"bound": "mfma", "achieved": tflops, "peak": peak,
+                           "unit": "TFLOP/s", "frac": tflops / peak, "traffic": None,
+                           "kernel": "pa_prefill_%s (banded variant, one launch)" % dtype_name})
+
+
+def bench_copy(args):
+    """A plain device-to-device copy of known size (256 MiB read + 256 MiB
+    written per launch), used to calibrate the rocprofv3 byte counters."""
+    import torch
+    n = 256 << 20
+    src = torch.empty(n, dtype=torch.uint8, device="cuda").random_(0, 255)
+    dst = torch.empty_like(src)
+    ms = time_steps(lambda: dst.copy_(src), args.steps, args.warmup)
+    return {"metric": "copy probe GB/s", "value": 2 * n / (ms * 1e-3) / 1e9, "unit": "GB/s",
+            "bytes_read_per_launch": n, "bytes_written_per_launch": n, "ms_per_step": ms,
+            "steps": args.steps, "warmup": args.warmup, "n_gpus": 1, "launches_per_step": 1}
 
 
 def bench_kv_write(args):
     """KV-cache write of a whole ModernBERT-shaped prompt batch (32 sequences,
     L ~ U[64,1024], 12 heads, D = 64, fp32) into a randomly permuted block
     pool: algorithmic bytes = k_new + v_new read + the same written."""
+    import torch
+    import sliding_window_mask_amd as pa
+    import workloads
     case = workloads.modernbert_prefill_f32(0, device="cuda")
     T, H, D = case.q.shape
     L = case.lens
@@ -500,17 +708,220 @@ def bench_kv_write(args):
                     args.steps, args.warmup)
     nbytes = 2 * 2 * T * H * D * 4
     gbps = nbytes / (ms * 1e-3) / 1e9
-    return {"metric": "KV-cache write GB/s", "value": gbps, "unit": "GB/s", "n_gpus": 1,
-            "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms,
-            "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
-            "data": "synthetic",
-            "config": {"workload": "kv_write_modernbert_f32", "tokens": T, "num_heads": H,
-                       "head_dim": D},
-            "roofline": {"bound": "hbm", "achieved": gbps, "peak": HBM_PEAK_GBPS,
-                         "unit": "GB/s", "frac": gbps / HBM_PEAK_GBPS,
-                         "traffic": read_traffic("kv_write_modernbert_f32", "pa_cache.hip"),
-                         "kernel": "pa_kv_write"},
-            "algorithmic_bytes_per_step": nbytes}
+    return _line("KV-cache write GB/s", gbps, "GB/s", ms, args, "f32",
+                 {"workload": "kv_write_modernbert_f32", "tokens": T, "num_heads": H,
+                  "head_dim": D},
+                 algorithmic_bytes_per_step=nbytes, launches_per_step=1,
+                 roofline={"bound": "hbm", "achieved": gbps, "peak": HBM_PEAK_GBPS,
+                           "unit": "GB/s", "frac": gbps / HBM_PEAK_GBPS,
+                           "traffic": read_traffic("kv_write_modernbert_f32", "pa_cache.hip"),
+                           "kernel": "pa_kv_write"})
+
+
+def bench_configs(args):
+    """Every other workload of the path, each as it is printed by its own
+    --workload run (roofline and CPU baseline included)."""
+    import torch
+    out = {}
+    for name, fn in (("t5_small_self_decode_bf16",
+                      lambda: bench_small_decode(args, "t5_small_self_decode_bf16")),
+                     ("t5_large_cross_decode_bf16",
+                      lambda: bench_small_decode(args, "t5_large_cross_decode_bf16")),
+                     ("modernbert_prefill_f32", lambda: bench_prefill(args, "f32")),
+                     ("modernbert_prefill_bf16", lambda: bench_prefill(args, "bf16"))):
+        t0 = time.time()
+        line = fn()
+        for k in ("n_gpus", "scaling", "data", "steps", "warmup"):
+            line.pop(k, None)
+        out[name] = line
+        torch.cuda.empty_cache()
+        log("%s: %.4f ms/step, roofline %.3f (%.1f s)"
+            % (name, line["ms_per_step"], line["roofline"]["frac"], time.time() - t0))
+    return out
+
+
+# ----------------------------------------------------------------------------
+# profile summaries (rocprofv3 output -> profiles/)
+# ----------------------------------------------------------------------------
+def _rows(path):
+    with open(path, newline="") as f:
+        return list(csv.DictReader(f))
+
+
+def _find(path, suffix):
+    """A rocprofv3 output file: `path` itself, or the one file under the
+    directory `path` whose name ends in `suffix`."""
+    if os.path.isfile(path):
+        return path
+    hits = sorted(glob.glob(os.path.join(path, "**", "*" + suffix), recursive=True))
+    if len(hits) != 1:
+        raise SystemExit("expected one *%s under %s, found %d" % (suffix, path, len(hits)))
+    return hits[0]
+
+
+def _ours(name):
+    return " pa::" in (" " + name) or name.startswith("pa::")
+
+
+def timed_dispatches(rows, n):
+    """The last n dispatches of the library's kernels, in dispatch order."""
+    mine = [r for r in rows if _ours(r["Kernel_Name"])]
+    mine.sort(key=lambda r: int(r["Dispatch_Id"]))
+    if len(mine) < n:
+        raise SystemExit("only %d dispatches of the library's kernels, %d expected"
+                         % (len(mine), n))
+    return mine[-n:]
+
+
+def trace_table(trace_csv, n):
+    """Per kernel name over the last n dispatches: count and mean / min / max
+    duration in microseconds (from the kernel trace's timestamps)."""
+    per = {}
+    for r in timed_dispatches(_rows(trace_csv), n):
+        d = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1000.0
+        per.setdefault(r["Kernel_Name"], []).append(d)
+    return per
+
+
+def counter_table(counter_csv, n):
+    """Per kernel name over the last n dispatches: the summed counter value of
+    each dispatch (rows of one dispatch are summed), as a list."""
+    rows = _rows(counter_csv)
+    by_disp = {}
+    for r in rows:
+        if not _ours(r["Kernel_Name"]):
+            continue
+        k = int(r["Dispatch_Id"])
+        by_disp.setdefault(k, [r["Kernel_Name"], 0.0])
+        by_disp[k][1] += float(r["Counter_Value"])
+    ids = sorted(by_disp)[-n:]
+    if len(ids) < n:
+        raise SystemExit("only %d counted dispatches, %d expected" % (len(ids), n))
+    per = {}
+    for k in ids:
+        per.setdefault(by_disp[k][0], []).append(by_disp[k][1])
+    return per
+
+
+def copy_counter(counter_csv):
+    """Median counter value (KiB) per dispatch of the calibration copy."""
+    vals = {}
+    for r in _rows(counter_csv):
+        if "copy" in r["Kernel_Name"].lower():
+            vals[r["Dispatch_Id"]] = vals.get(r["Dispatch_Id"], 0.0) + float(r["Counter_Value"])
+    if not vals:
+        raise SystemExit("no copy kernel in %s" % counter_csv)
+    return statistics.median(vals.values())
+
+
+def write_profiles(a):
+    """Write profiles/<workload>_kernel_trace.md (and, with the counter runs,
+    profiles/<workload>_traffic.txt) from rocprofv3 output of --profile-run
+    runs. --trace DIR: a `--kernel-trace --stats` run; --bench-line FILE: its
+    printed JSON line (steps and launches per step say which dispatches were
+    timed); --fetch/--write DIR: `--pmc FETCH_SIZE` / `--pmc WRITE_SIZE` runs
+    with --counter-line FILE their JSON line; --copy-fetch/--copy-write DIR:
+    the same passes over --workload copy_probe (the byte calibration)."""
+    wl = a.write_profiles
+    src = KERNEL_SOURCE[wl]
+    sha = source_sha(src)
+    line = json.loads(open(a.bench_line).read().strip().splitlines()[-1])
+    n = line["steps"] * line["launches_per_step"]
+    trace = _find(a.trace, "_kernel_trace.csv")
+    per = trace_table(trace, n)
+    step_us = sum(sum(v) for v in per.values()) / line["steps"]
+    cmd = a.command or "(command not recorded)"
+    md = ["# Kernel trace: %s (timed steps only)" % wl, "",
+          "Command (on the MI355X box, from the repository root):", "",
+          "    " + cmd, "",
+          "%s sha256[:16] = %s" % (src, sha), "",
+          "Averages over the last %d dispatches of the library's kernels: the %d timed "
+          "steps of `--profile-run` (%d launch(es) per step); warm-up and clock-settling "
+          "launches are excluded." % (n, line["steps"], line["launches_per_step"]), "",
+          "| kernel | calls | average (us) | min (us) | max (us) |", "|---|---|---|---|---|"]
+    for k, v in sorted(per.items(), key=lambda kv: -sum(kv[1])):
+        md.append("| `%s` | %d | %.1f | %.1f | %.1f |" % (k, len(v), sum(v) / len(v),
+                                                           min(v), max(v)))
+    md += ["", "Sum of kernel durations per step: %.1f us. The bench line of the same run "
+           "(HIP events around the %d timed steps): %.1f us per step, roofline frac %.4f."
+           % (step_us, line["steps"], line["ms_per_step"] * 1000, line["roofline"]["frac"])]
+    if "algorithmic_bytes_per_step" in line:
+        md.append("Algorithmic bytes per step: %d (%.1f GB/s over the summed kernel time)."
+                  % (line["algorithmic_bytes_per_step"],
+                     line["algorithmic_bytes_per_step"] / (step_us * 1e-6) / 1e9))
+    if "algorithmic_flops_per_step" in line:
+        md.append("Algorithmic flops per step: %d (%.1f TFLOP/s over the summed kernel time)."
+                  % (line["algorithmic_flops_per_step"],
+                     line["algorithmic_flops_per_step"] / (step_us * 1e-6) / 1e12))
+    open(os.path.join(PROFILES, "%s_kernel_trace.md" % wl), "w").write("\n".join(md) + "\n")
+    if not a.fetch:
+        return
+    cl = json.loads(open(a.counter_line).read().strip().splitlines()[-1])
+    nc = cl["steps"] * cl["launches_per_step"]
+    cf = copy_counter(_find(a.copy_fetch, "_counter_collection.csv"))
+    cw = copy_counter(_find(a.copy_write, "_counter_collection.csv"))
+    fs, ws = 262144.0 / cf, 262144.0 / cw
+    fpk = counter_table(_find(a.fetch, "_counter_collection.csv"), nc)
+    wpk = counter_table(_find(a.write, "_counter_collection.csv"), nc)
+    hb_step = (sum(sum(v) for v in fpk.values()) * fs +
+               sum(sum(v) for v in wpk.values()) * ws) * 1024 / cl["steps"]
+    alg = cl["algorithmic_bytes_per_step"]
+    txt = ["# HBM traffic: %s (counter passes over the timed steps of --profile-run)" % wl,
+           "#", "# Commands (each its own run, on the MI355X box, from the repository root):"]
+    txt += ["#   " + c for c in (a.counter_commands or [])]
+    txt += ["# Counter values are KiB per dispatch, scaled so that the same counter reads",
+            "# 262144 KiB for a plain 256 MiB device copy (read and written once).",
+            "# Bytes per step = summed scaled FETCH_SIZE + WRITE_SIZE of the last %d"
+            % nc, "# dispatches (%d steps of %d launch(es)), divided by %d."
+            % (cl["steps"], cl["launches_per_step"], cl["steps"]),
+            "kernel_source_sha = %s" % sha,
+            "copy_FETCH_SIZE_KiB = %.1f" % cf, "copy_WRITE_SIZE_KiB = %.1f" % cw,
+            "fetch_scale = %.5f" % fs, "write_scale = %.5f" % ws]
+    for k in sorted(fpk):
+        tag = k.split("(")[0].split("::")[-1].strip().replace(" ", "")
+        f_med = statistics.median(fpk[k])
+        w_med = statistics.median(wpk.get(k, [0.0]))
+        txt += ["# kernel %s" % k,
+                "%s_FETCH_SIZE_KiB_median = %.1f" % (tag, f_med),
+                "%s_WRITE_SIZE_KiB_median = %.1f" % (tag, w_med),
+                "%s_hbm_bytes_median = %.0f" % (tag, (f_med * fs + w_med * ws) * 1024)]
+    txt += ["hbm_bytes_per_step = %.0f" % hb_step,
+            "hbm_bytes_per_launch = %.0f" % (hb_step / cl["launches_per_step"]),
+            "algorithmic_bytes_per_step = %d" % alg,
+            "ratio_hbm_to_algorithmic = %.4f" % (hb_step / alg)]
+    open(os.path.join(PROFILES, "%s_traffic.txt" % wl), "w").write("\n".join(txt) + "\n")
+
+
+def write_counter_summary(a):
+    """profiles/<workload>_counters.md: the median per dispatch of every
+    counter of one `--pmc` run over the timed dispatches, per kernel."""
+    wl = a.counter_summary
+    line = json.loads(open(a.counter_line).read().strip().splitlines()[-1])
+    n = line["steps"] * line["launches_per_step"]
+    rows = _rows(_find(a.counters, "_counter_collection.csv"))
+    by = {}
+    for r in rows:
+        if _ours(r["Kernel_Name"]):
+            by.setdefault(int(r["Dispatch_Id"]), {"k": r["Kernel_Name"]})
+            d = by[int(r["Dispatch_Id"])]
+            d[r["Counter_Name"]] = d.get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+    ids = sorted(by)[-n:]
+    names = sorted({c for i in ids for c in by[i] if c != "k"})
+    kernels = sorted({by[i]["k"] for i in ids})
+    path = os.path.join(PROFILES, "%s_counters.md" % wl)
+    old = open(path).read() if os.path.exists(path) and a.append else ""
+    md = [old.rstrip() + "\n"] if old else ["# Counters: %s (timed steps of --profile-run)" % wl,
+                                            "", "%s sha256[:16] = %s" % (
+                                                KERNEL_SOURCE[wl],
+                                                source_sha(KERNEL_SOURCE[wl])), ""]
+    md += ["Command: `%s`" % (a.command or "(not recorded)"), "",
+           "| kernel | " + " | ".join(names) + " |", "|---|" + "---|" * len(names)]
+    for k in kernels:
+        vals = [statistics.median([by[i][c] for i in ids if by[i]["k"] == k and c in by[i]])
+                if any(by[i]["k"] == k and c in by[i] for i in ids) else float("nan")
+                for c in names]
+        md.append("| `%s` | " % k + " | ".join("%.4g" % v for v in vals) + " |")
+    open(path, "w").write("\n".join(md) + "\n")
 
 
 def main():
@@ -521,24 +932,46 @@ def main():
     ap.add_argument("--workload", default="large_biased_decode_bf16")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-variants", action="store_true")
+    ap.add_argument("--no-configs", action="store_true")
+    ap.add_argument("--profile-run", action="store_true")
+    ap.add_argument("--write-profiles", metavar="WORKLOAD")
+    ap.add_argument("--counter-summary", metavar="WORKLOAD")
+    ap.add_argument("--trace")
+    ap.add_argument("--bench-line")
+    ap.add_argument("--fetch")
+    ap.add_argument("--write")
+    ap.add_argument("--copy-fetch")
+    ap.add_argument("--copy-write")
+    ap.add_argument("--counters")
+    ap.add_argument("--counter-line")
+    ap.add_argument("--command")
+    ap.add_argument("--counter-commands", nargs="*")
+    ap.add_argument("--append", action="store_true")
     args = ap.parse_args()
+    if args.write_profiles:
+        write_profiles(args)
+        return
+    if args.counter_summary:
+        write_counter_summary(args)
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py runs on one GPU only: the paged-attention path is measured on a "
               "single MI355X (--gpus 1).", file=sys.stderr)
         sys.exit(2)
+    import torch
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(2)
+    if args.profile_run:
+        args.no_variants = args.no_cpu_baseline = args.no_configs = True
     if args.workload == "large_biased_decode_bf16":
         line = bench_decode(args)
-    elif args.workload == "modernbert_prefill_f32":
-        line = bench_prefill(args)
-    elif args.workload == "modernbert_prefill_bf16":
-        line = bench_prefill(args, torch.bfloat16)
-    elif args.workload == "modernbert_chunked_prefill_f32":
-        line = bench_chunked_prefill(args)
-    elif args.workload == "modernbert_chunked_prefill_bf16":
-        line = bench_chunked_prefill(args, torch.bfloat16)
+        if not args.no_configs:
+            line["configs"] = bench_configs(args)
+    elif args.workload in ("modernbert_prefill_f32", "modernbert_prefill_bf16"):
+        line = bench_prefill(args, args.workload.rsplit("_", 1)[1])
+    elif args.workload in ("modernbert_chunked_prefill_f32", "modernbert_chunked_prefill_bf16"):
+        line = bench_chunked_prefill(args, args.workload.rsplit("_", 1)[1])
     elif args.workload in ("t5_small_self_decode_bf16", "t5_large_cross_decode_bf16"):
         line = bench_small_decode(args, args.workload)
     elif args.workload == "kv_write_modernbert_f32":

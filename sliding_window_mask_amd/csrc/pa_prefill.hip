@@ -301,6 +301,24 @@ pa_prefill_f32(PrefillArgs a) {
       bias_row[q] = a.attn_bias +
                     (((int64_t)b * H + h) * a.max_seq_len + pos0 + tb_row) * a.max_seq_len;
   }
+  // A lane's 4 bias entries of a chunk (keys c0 + 4g .. + 3) are contiguous:
+  // where the group sees the chunk whole they are read as one 16-byte load,
+  // if every lane's row is 16-byte aligned (uniform per group)
+  bool bias_vec[NG];
+#pragma unroll
+  for (int q = 0; q < NG; ++q)
+    bias_vec[q] = BIAS == 1 &&
+                  __builtin_amdgcn_ballot_w64((reinterpret_cast<uintptr_t>(bias_row[q]) & 15) != 0) == 0;
+  // whether every key of the 16-key chunk at c0 is visible to every existing
+  // row of group q (uniform): no per-element mask is needed there
+  auto chunk_whole = [&](int q, int c0) {
+    bool whole = c0 + 16 <= L;
+    if constexpr (CAUSAL) whole = whole && c0 + 15 <= gp0[q];
+    if constexpr (BAND == 1)
+      whole = whole && gp1[q] - c0 < a.window && c0 + 15 - gp0[q] < a.window;
+    if constexpr (BAND == 2) whole = whole && c0 >= wlo[q] && c0 + 16 <= whi[q];
+    return whole;
+  };
 
   // ---- prologue: tile 0 into LDS buffer 0, tile 1 in flight, table of tile 2 ----
   if (ntiles > 0) {
@@ -334,6 +352,19 @@ pa_prefill_f32(PrefillArgs a) {
           const int c0 = base + ch * 16;
           live |= (c0 < wv_hi && c0 + 16 > wv_lo) ? 1 << ch : 0;
         }
+      }
+      // bias of the chunks seen whole, requested before the products
+      float4_t bpre[NG][kChunks];
+      if constexpr (BIAS == 1) {
+#pragma unroll
+        for (int q = 0; q < NG; ++q)
+#pragma unroll
+          for (int ch = 0; ch < kChunks; ++ch) {
+            const int c0 = base + ch * 16;
+            bpre[q][ch] = float4_t{0, 0, 0, 0};
+            if (bias_vec[q] && ((live >> ch) & 1) && chunk_whole(q, c0))
+              bpre[q][ch] = *reinterpret_cast<const float4_t*>(bias_row[q] + c0 + 4 * g);
+          }
       }
       // ---- S^T = K Q^T (base-2 scores); each K operand feeds every group ----
       float4_t s[NG][kChunks];
@@ -389,15 +420,16 @@ pa_prefill_f32(PrefillArgs a) {
           // not see the whole chunk (sequence end, window edges, diagonal);
           // a materialised bias (added as a * scale * log2(e): the same sum as
           // (q.k + a) * scale) is read only for visible keys
-          bool whole = c0 + 16 <= L;
-          if constexpr (CAUSAL) whole = whole && c0 + 15 <= gp0[q];
-          if constexpr (BAND == 1)
-            whole = whole && gp1[q] - c0 < a.window && c0 + 15 - gp0[q] < a.window;
-          if constexpr (BAND == 2) whole = whole && c0 >= wlo[q] && c0 + 16 <= whi[q];
-          if (whole) {
+          if (chunk_whole(q, c0)) {
             if constexpr (BIAS == 1) {
+              if (bias_vec[q]) {
 #pragma unroll
-              for (int r = 0; r < 4; ++r) s[q][ch][r] = s[q][ch][r] + bias_row[q][j0 + r] * cs;
+                for (int r = 0; r < 4; ++r) s[q][ch][r] = s[q][ch][r] + bpre[q][ch][r] * cs;
+              } else {
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                  s[q][ch][r] = s[q][ch][r] + bias_row[q][j0 + r] * cs;
+              }
             }
           } else {
             const int d0 = dq[q] - c0;

@@ -283,6 +283,22 @@ pa_prefill_bf16(PrefillArgs a) {
                                              a.max_seq_len;
     }
   }
+  // A lane's 4 bias entries of a chunk (keys c0 + 4g .. + 3) are contiguous:
+  // where the sub-tile sees the chunk whole they are read as one 16-byte
+  // load, if every lane's row is 16-byte aligned (uniform per sub-tile)
+  bool bias_vec[kSub];
+#pragma unroll
+  for (int sb = 0; sb < kSub; ++sb)
+    bias_vec[sb] = BIAS == 1 &&
+                   __builtin_amdgcn_ballot_w64((reinterpret_cast<uintptr_t>(bias_row[sb]) & 15) != 0) == 0;
+  // whether every key of the 16-key chunk at c0 is visible to every existing
+  // row of sub-tile sb (uniform): no per-element mask is needed there
+  auto chunk_whole = [&](int sb, int c0) {
+    bool whole = c0 + 16 <= L;
+    if constexpr (CAUSAL) whole = whole && c0 + 15 <= sp0[sb];
+    if constexpr (WINDOW) whole = whole && c0 >= wlo[sb] && c0 + 16 <= whi[sb];
+    return whole;
+  };
   bf16x8_t ones = __builtin_bit_cast(
       bf16x8_t, make_uint4(0x3f803f80u, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u));
 
@@ -315,6 +331,19 @@ pa_prefill_bf16(PrefillArgs a) {
           const int c0 = base + ch * 16;
           live |= (c0 < wv_hi && c0 + 16 > wv_lo) ? 1 << ch : 0;
         }
+      }
+      // bias of the chunks seen whole, requested before the products
+      float4_t bpre[kSub][2];
+      if constexpr (BIAS == 1) {
+#pragma unroll
+        for (int sb = 0; sb < kSub; ++sb)
+#pragma unroll
+          for (int ch = 0; ch < 2; ++ch) {
+            const int c0 = base + ch * 16;
+            bpre[sb][ch] = float4_t{0, 0, 0, 0};
+            if (bias_vec[sb] && ((live >> ch) & 1) && chunk_whole(sb, c0))
+              bpre[sb][ch] = *reinterpret_cast<const float4_t*>(bias_row[sb] + c0 + 4 * g);
+          }
       }
       // ---- S^T for the two 16-key chunks of every sub-tile ----
       float4_t s[kSub][2];
@@ -380,14 +409,17 @@ pa_prefill_bf16(PrefillArgs a) {
           // per-element mask only where some existing row of the sub-tile
           // does not see the whole chunk; a materialised bias is read only
           // for visible keys
-          bool whole = c0 + 16 <= L;
-          if constexpr (CAUSAL) whole = whole && c0 + 15 <= sp0[sb];
-          if constexpr (WINDOW) whole = whole && c0 >= wlo[sb] && c0 + 16 <= whi[sb];
-          if (whole) {
+          if (chunk_whole(sb, c0)) {
             if constexpr (BIAS == 1) {
+              if (bias_vec[sb]) {
 #pragma unroll
-              for (int r = 0; r < 4; ++r)
-                s[sb][ch][r] = fmaf(bias_row[sb][j0 + r], bmul, s[sb][ch][r]);
+                for (int r = 0; r < 4; ++r)
+                  s[sb][ch][r] = fmaf(bpre[sb][ch][r], bmul, s[sb][ch][r]);
+              } else {
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                  s[sb][ch][r] = fmaf(bias_row[sb][j0 + r], bmul, s[sb][ch][r]);
+              }
             }
           } else {
             const int d0 = dq[sb] - c0;
@@ -666,7 +698,23 @@ pa_prefill_bf16_32(PrefillArgs a) {
                    : a.attn_bias +
                          (((int64_t)b * H + h) * a.max_seq_len + pos0 + tb_row) * a.max_seq_len;
   }
+  // a lane's bias entries of a tile are 4 runs of 4 contiguous keys: 16-byte
+  // loads on tiles that lie wholly inside the sequence, if every lane's row
+  // is 16-byte aligned (uniform)
+  const bool bias_vec =
+      BIAS == 1 &&
+      __builtin_amdgcn_ballot_w64((reinterpret_cast<uintptr_t>(bias_row) & 15) != 0) == 0;
   const bf16x2_t one2 = __builtin_bit_cast(bf16x2_t, 0x3f803f80u);
+  // bias entries of the next tile lying wholly inside the sequence (16-byte
+  // loads), requested one tile ahead
+  float4_t bnext[4];
+#pragma unroll
+  for (int u = 0; u < 4; ++u) bnext[u] = float4_t{0, 0, 0, 0};
+  if (BIAS == 1 && bias_vec && wave_active && kKT <= L) {
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+      bnext[u] = *reinterpret_cast<const float4_t*>(bias_row + 8 * u + 4 * hh);
+  }
 
   if (ntiles > 0) {
     load_table(0);
@@ -684,6 +732,7 @@ pa_prefill_bf16_32(PrefillArgs a) {
     constexpr int buf = decltype(buf_c)::value;
     const int c0 = tk * kKT;
     if (wave_active) {
+      const bool bias_whole = bias_vec && c0 + kKT <= L;
       // ---- S^T for the tile's 32 keys ----
       float16_t s;
 #pragma unroll
@@ -697,14 +746,34 @@ pa_prefill_bf16_32(PrefillArgs a) {
       // ---- bias (unscaled scores) and the tail mask. Every row of these
       // launches sees all L keys, so every bias entry read is a visible one
       // (keys past L of the last tile re-read entry L - 1, then are masked) ----
+      if constexpr (BIAS == 1) {
+        if (bias_whole) {
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const int j0 = c0 + 8 * u + 4 * hh;
+          for (int u = 0; u < 4; ++u)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          if constexpr (BIAS == 1)
-            s[4 * u + r] = fmaf(bias_row[min(j0 + r, L - 1)], bmul, s[4 * u + r]);
-          if constexpr (BIAS == 2)
+            for (int r = 0; r < 4; ++r) s[4 * u + r] = fmaf(bnext[u][r], bmul, s[4 * u + r]);
+          // the next tile's entries, a whole tile of work ahead of their use
+          if (bias_vec && c0 + 2 * kKT <= L) {
+#pragma unroll
+            for (int u = 0; u < 4; ++u)
+              bnext[u] =
+                  *reinterpret_cast<const float4_t*>(bias_row + c0 + kKT + 8 * u + 4 * hh);
+          }
+        } else {
+#pragma unroll
+          for (int u = 0; u < 4; ++u)
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+              s[4 * u + r] =
+                  fmaf(bias_row[min(c0 + 8 * u + 4 * hh + r, L - 1)], bmul, s[4 * u + r]);
+        }
+      }
+      if constexpr (BIAS == 2) {
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const int j0 = c0 + 8 * u + 4 * hh;
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
             s[4 * u + r] += rel_lds[min(max(j0 + r - p_row, -rel_md), rel_md) + rel_md];
         }
       }

@@ -117,3 +117,85 @@ def test_more_than_one_gpu_is_refused():
                        capture_output=True, text=True, timeout=300)
     assert r.returncode == 2
     assert "one GPU" in r.stderr
+
+
+def test_prefill_bytes_count_each_token_once():
+    lens = np.array([1, 16, 17, 300], dtype=np.int32)
+    # q, K, V read and out written once per token, head and dim
+    assert bench.prefill_bytes(lens, 12, 64, 4) == 4 * 334 * 12 * 64 * 4
+    assert bench.prefill_bytes(lens, 12, 64, 2) == 4 * 334 * 12 * 64 * 2
+
+
+TRACE_HDR = ["Kind", "Dispatch_Id", "Kernel_Name", "Start_Timestamp", "End_Timestamp"]
+CTR_HDR = ["Dispatch_Id", "Kernel_Name", "Counter_Name", "Counter_Value"]
+K_FULL = "void pa::(anonymous namespace)::pa_prefill_f32<64, 1, 0, false, 0>(pa::PrefillArgs)"
+K_WIN = "void pa::(anonymous namespace)::pa_prefill_f32<64, 1, 0, false, 1>(pa::PrefillArgs)"
+K_TORCH = "void at::native::vectorized_elementwise_kernel<4, at::native::FillFunctor<float> >"
+
+
+def _write_csv(path, hdr, rows):
+    import csv
+    with open(path, "w", newline="") as f:
+        w = csv.writer(f)
+        w.writerow(hdr)
+        w.writerows(rows)
+
+
+def _fake_run(tmp_path):
+    """A fake profile of 5 steps of (full, window) launches after 3 warm-up
+    steps, torch kernels in between; the timed full launches take 10 us, the
+    window ones 4 us, warm-up launches 99 us."""
+    rows, d, t = [], 1, 0
+    for step in range(8):
+        timed = step >= 3
+        for k, us in ((K_FULL, 10), (K_WIN, 4)):
+            dur = (us if timed else 99) * 1000
+            rows.append(["KERNEL_DISPATCH", d, k, t, t + dur])
+            d, t = d + 1, t + dur + 500
+        rows.append(["KERNEL_DISPATCH", d, K_TORCH, t, t + 7000])
+        d, t = d + 1, t + 8000
+    _write_csv(tmp_path / "run_kernel_trace.csv", TRACE_HDR, rows)
+    return rows
+
+
+def test_trace_table_keeps_only_the_timed_dispatches(tmp_path):
+    _fake_run(tmp_path)
+    per = bench.trace_table(str(tmp_path / "run_kernel_trace.csv"), 10)
+    assert sorted(per) == sorted([K_FULL, K_WIN])
+    assert per[K_FULL] == [10.0] * 5 and per[K_WIN] == [4.0] * 5
+
+
+def test_write_profiles_round_trip(tmp_path, monkeypatch):
+    """Trace and counter summaries written from fake rocprofv3 output are read
+    back by read_traffic, and their numbers are the timed launches' ones."""
+    import json
+    monkeypatch.setattr(bench, "PROFILES", str(tmp_path))
+    _fake_run(tmp_path)
+    line = {"steps": 5, "launches_per_step": 2, "ms_per_step": 0.015,
+            "roofline": {"frac": 0.5}, "algorithmic_bytes_per_step": 1000 * 1024}
+    (tmp_path / "line.json").write_text(json.dumps(line) + "\n")
+    for ctr, full, win in (("FETCH_SIZE", 600.0, 300.0), ("WRITE_SIZE", 200.0, 100.0)):
+        rows = []
+        for d in range(1, 9):           # 3 warm-up + 5 timed dispatches of each kernel
+            rows.append([2 * d - 1, K_FULL, ctr, full if d > 3 else 1e9])
+            rows.append([2 * d, K_WIN, ctr, win if d > 3 else 1e9])
+        os.makedirs(tmp_path / ctr, exist_ok=True)
+        _write_csv(tmp_path / ctr / "run_counter_collection.csv", CTR_HDR, rows)
+        os.makedirs(tmp_path / ("copy_" + ctr), exist_ok=True)
+        _write_csv(tmp_path / ("copy_" + ctr) / "run_counter_collection.csv", CTR_HDR,
+                   [[1, "void at::native::direct_copy_kernel", ctr,
+                     131072.0 if ctr == "FETCH_SIZE" else 262144.0]])
+    args = bench.argparse.Namespace(
+        write_profiles="modernbert_prefill_f32", bench_line=str(tmp_path / "line.json"),
+        trace=str(tmp_path), fetch=str(tmp_path / "FETCH_SIZE"),
+        write=str(tmp_path / "WRITE_SIZE"), copy_fetch=str(tmp_path / "copy_FETCH_SIZE"),
+        copy_write=str(tmp_path / "copy_WRITE_SIZE"), counter_line=str(tmp_path / "line.json"),
+        command="python bench.py ...", counter_commands=["a", "b"])
+    bench.write_profiles(args)
+    md = (tmp_path / "modernbert_prefill_f32_kernel_trace.md").read_text()
+    assert "| 5 | 10.0 | 10.0 | 10.0 |" in md and "| 5 | 4.0 | 4.0 | 4.0 |" in md
+    # per step: fetch (600 + 300) KiB x 2 (calibration) + write (200 + 100) KiB
+    want = (900 * 2 + 300) * 1024
+    assert bench.read_traffic("modernbert_prefill_f32", "pa_prefill.hip",
+                              "hbm_bytes_per_step") == want
+    assert bench.read_traffic("modernbert_prefill_f32", "pa_prefill.hip") == want / 2
