@@ -72,7 +72,16 @@ extern "C" {
 
 #define PA_ABI_VERSION 1
 
-typedef enum { PA_DTYPE_F32 = 0, PA_DTYPE_BF16 = 1 } pa_dtype_t;
+/* The two range enumerators are not dtypes: they make the enum span every
+ * int32 value, so that any integer a caller passes is a valid value of the
+ * type, which the library then rejects as unsupported (in C++ an enum holding
+ * a value outside its enumerators' range is undefined behaviour). */
+typedef enum {
+  PA_DTYPE_F32 = 0,
+  PA_DTYPE_BF16 = 1,
+  PA_DTYPE_RANGE_MIN_ = -0x7fffffff - 1,
+  PA_DTYPE_RANGE_MAX_ = 0x7fffffff
+} pa_dtype_t;
 
 typedef enum {
   PA_OK = 0,

@@ -29,7 +29,9 @@ import os
 import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libpaged_attn.so")
+# PA_LIB points the binding at another build of the same sources (the CPU
+# sanitizer test loads a host-only AddressSanitizer build this way)
+LIB_PATH = os.environ.get("PA_LIB") or os.path.join(_HERE, "libpaged_attn.so")
 LIB_NOBIAS_PATH = os.path.join(_HERE, "libpaged_attn_nobias.so")
 
 PA_DTYPE_F32 = 0

@@ -13,6 +13,7 @@ import torch
 os.environ.setdefault("PA_VALIDATE", "1")      # range-check metadata before each launch
 
 import oracle                                   # noqa: E402
+import parity_log                               # noqa: E402
 import sliding_window_mask_amd as pa            # noqa: E402
 
 TOL = {torch.float32: 1e-5, torch.bfloat16: 2e-2}
@@ -81,6 +82,7 @@ def max_err(gpu_out, ref):
 def assert_close(gpu_out, ref, dtype, what=""):
     e = max_err(gpu_out, ref)
     log("  %s max|err| = %.3e (tol %.0e)" % (what, e, TOL[dtype]))
+    parity_log.add(what, e, TOL[dtype])
     assert e <= TOL[dtype], "%s: max abs error %.3e > %.0e" % (what, e, TOL[dtype])
 
 

@@ -55,12 +55,15 @@ def test_t5_large_cross_decode_null_equals_zero_bias():
 @pytest.mark.parametrize("window,evict", [(-1, False), (1024, True)])
 def test_large_biased_decode_sampled(window, evict):
     """Full-size run (256 x 32 heads, L up to 4096, default launch
-    configuration) checked on a sample of sequences the oracle computes."""
+    configuration) checked on 40 sequences the oracle computes: the longest,
+    the shortest, the first and last, and 36 more spread over the batch."""
     log("large_biased_decode_bf16 window=%d evict=%s" % (window, evict))
     case = workloads.large_biased_decode_bf16(device=DEV, sliding_window=window, evict=evict)
     out = gpu_decode(case)
     L = case.lens
-    seqs = sorted(set([int(np.argmax(L)), int(np.argmin(L)), 0, 1, 127, 255]))
+    spread = np.linspace(1, 254, 36).astype(int).tolist()
+    seqs = sorted(set([int(np.argmax(L)), int(np.argmin(L)), 0, 255] + spread))
+    assert len(seqs) >= 32
     sub = sample_decode(case, seqs)
     ref = oracle_decode(sub)
     assert_close(out[torch.tensor(seqs, device=DEV)], ref, torch.bfloat16, "large sample")

@@ -124,3 +124,15 @@ def test_modernbert_prefill_layer_sampled(layer):
     sub = sample_prefill(case, seqs)
     ref = oracle_prefill(sub)
     assert_close(out[sub.rows.to(DEV)], ref, torch.float32, "layer %d sample" % layer)
+
+
+@pytest.mark.parametrize("layer", [0, 1])
+def test_modernbert_prefill_layer_every_sequence(layer):
+    """A full-attention layer (0) and a window-64 layer (1) of the full-size
+    workload, in the launch configuration the benchmark times, with every
+    one of the 32 sequences (all heads and queries) against the oracle."""
+    log("modernbert layer %d, all sequences" % layer)
+    case = workloads.modernbert_prefill_f32(layer, device=DEV)
+    out = gpu_prefill(case)
+    ref = oracle_prefill(case)
+    assert_close(out, ref, torch.float32, "layer %d all sequences" % layer)
