@@ -511,6 +511,15 @@ def bench_small_decode(args, name):
         work per call) are captured once in a HIP graph and the graph is
         replayed, as a serving loop would launch them; a replay's outputs are
         checked bit for bit against eager calls."""
+        if args.profile_run:
+            # under a profiler the calls are launched one by one (no graph):
+            # the kernels are the same, the host launch gaps are not timed
+            it = [0]
+
+            def step():
+                fn(*layers[it[0] % ncopy])
+                it[0] += 1
+            return time_steps(step, args.steps, args.warmup)
         side = torch.cuda.Stream()
         side.wait_stream(torch.cuda.current_stream())
         with torch.cuda.stream(side):
@@ -812,6 +821,17 @@ def _find(path, suffix):
     return hits[0]
 
 
+def kernel_tag(name):
+    """Short key for a kernel name: 'pa_prefill_f32<64, 1, 0, false, 1>' ->
+    'pa_prefill_f32_64_1_0_false_1'."""
+    import re
+    m = re.search(r"(pa_\w+)(<[^>]*>)?", name)
+    if not m:
+        return re.sub(r"\W+", "_", name).strip("_")
+    args = re.sub(r"[^\w]+", "_", m.group(2) or "").strip("_")
+    return m.group(1) + ("_" + args if args else "")
+
+
 def _ours(name):
     return " pa::" in (" " + name) or name.startswith("pa::")
 
@@ -931,7 +951,7 @@ def write_profiles(a):
             "copy_FETCH_SIZE_KiB = %.1f" % cf, "copy_WRITE_SIZE_KiB = %.1f" % cw,
             "fetch_scale = %.5f" % fs, "write_scale = %.5f" % ws]
     for k in sorted(fpk):
-        tag = k.split("(")[0].split("::")[-1].strip().replace(" ", "")
+        tag = kernel_tag(k)
         f_med = statistics.median(fpk[k])
         w_med = statistics.median(wpk.get(k, [0.0]))
         txt += ["# kernel %s" % k,
@@ -969,11 +989,41 @@ def write_counter_summary(a):
                                                 source_sha(KERNEL_SOURCE[wl])), ""]
     md += ["Command: `%s`" % (a.command or "(not recorded)"), "",
            "| kernel | " + " | ".join(names) + " |", "|---|" + "---|" * len(names)]
+    med = {}
     for k in kernels:
         vals = [statistics.median([by[i][c] for i in ids if by[i]["k"] == k and c in by[i]])
                 if any(by[i]["k"] == k and c in by[i] for i in ids) else float("nan")
                 for c in names]
+        med[k] = dict(zip(names, vals))
         md.append("| `%s` | " % k + " | ".join("%.4g" % v for v in vals) + " |")
+    md += ["", "Medians per dispatch over the last %d dispatches (%d timed steps). Each "
+           "counter is summed by rocprofv3 over the chip; GRBM_GUI_ACTIVE over the 8 XCDs, so "
+           "GRBM_GUI_ACTIVE / 8 is the launch duration in cycles." % (n, line["steps"])]
+    derived = []
+    for k, v in med.items():
+        row = []
+        cyc = v.get("GRBM_GUI_ACTIVE", float("nan")) / 8
+        if "SQ_VALU_MFMA_BUSY_CYCLES" in v:
+            row.append(("MFMA busy (per SIMD per launch cycle)",
+                        "%.1f%%" % (100 * v["SQ_VALU_MFMA_BUSY_CYCLES"] / (cyc * 1024))))
+        if "SQ_INSTS_MFMA" in v and "SQ_INSTS_VALU" in v:
+            row.append(("other VALU insts per MFMA inst",
+                        "%.2f" % ((v["SQ_INSTS_VALU"] - v["SQ_INSTS_MFMA"]) / v["SQ_INSTS_MFMA"])))
+        if "SQ_INSTS_MFMA" in v and "SQ_INSTS_LDS" in v:
+            row.append(("LDS insts per MFMA inst", "%.2f" % (v["SQ_INSTS_LDS"] / v["SQ_INSTS_MFMA"])))
+        if "SQ_WAIT_INST_ANY" in v and "SQ_WAVE_CYCLES" in v:
+            row.append(("SQ_WAIT_INST_ANY / SQ_WAVE_CYCLES",
+                        "%.2f" % (v["SQ_WAIT_INST_ANY"] / v["SQ_WAVE_CYCLES"])))
+        if "SQ_VALU_MFMA_COEXEC_CYCLES" in v:
+            row.append(("VALU-MFMA co-exec (per SIMD per launch cycle)",
+                        "%.1f%%" % (100 * v["SQ_VALU_MFMA_COEXEC_CYCLES"] / (cyc * 1024))))
+        if row:
+            derived.append((k, row))
+        if v.get("SQ_LDS_BANK_CONFLICT") == v.get("SQ_INSTS_MFMA") and "SQ_INSTS_MFMA" in v:
+            md.append("`%s`: SQ_LDS_BANK_CONFLICT reads exactly SQ_INSTS_MFMA in this pass, so it "
+                      "is not taken as a measurement of bank conflicts." % k)
+    for k, row in derived:
+        md += ["", "Derived, `%s`:" % k, ""] + ["- %s: %s" % kv for kv in row]
     open(path, "w").write("\n".join(md) + "\n")
 
 

@@ -96,7 +96,7 @@ def test_read_traffic_requires_the_measured_source(tmp_path, monkeypatch):
 
 def test_committed_traffic_summaries_parse():
     """The committed counter summaries hold the keys the bench lines read."""
-    for wl, key in (("decode_large_biased_bf16", "hbm_bytes_per_launch"),
+    for wl, key in (("large_biased_decode_bf16", "hbm_bytes_per_launch"),
                     ("modernbert_prefill_f32", "hbm_bytes_per_step"),
                     ("modernbert_prefill_bf16", "hbm_bytes_per_step"),
                     ("t5_small_self_decode_bf16", "hbm_bytes_per_launch"),
@@ -199,3 +199,9 @@ def test_write_profiles_round_trip(tmp_path, monkeypatch):
     assert bench.read_traffic("modernbert_prefill_f32", "pa_prefill.hip",
                               "hbm_bytes_per_step") == want
     assert bench.read_traffic("modernbert_prefill_f32", "pa_prefill.hip") == want / 2
+
+
+def test_kernel_tag():
+    assert bench.kernel_tag(K_WIN) == "pa_prefill_f32_64_1_0_false_1"
+    assert bench.kernel_tag("void pa::(anonymous namespace)::pa_kv_write<256>(pa::KvWriteArgs)") \
+        == "pa_kv_write_256"
