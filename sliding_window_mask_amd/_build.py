@@ -17,8 +17,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
-SOURCES = ["pa_api.cpp", "pa_decode.hip", "pa_prefill.hip", "pa_prefill_bf16.hip",
-           "pa_cache.hip"]
+SOURCES = ["pa_api.cpp", "pa_decode.hip", "pa_prefill.hip", "pa_prefill_f32x3.hip",
+           "pa_prefill_bf16.hip", "pa_cache.hip"]
 LIB = os.path.join(HERE, "libpaged_attn.so")
 LIB_NOBIAS = os.path.join(HERE, "libpaged_attn_nobias.so")
 
