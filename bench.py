@@ -69,7 +69,7 @@ KERNEL_SOURCE = {
     "large_biased_decode_bf16": "pa_decode.hip",
     "t5_small_self_decode_bf16": "pa_decode.hip",
     "t5_large_cross_decode_bf16": "pa_decode.hip",
-    "modernbert_prefill_f32": "pa_prefill.hip",
+    "modernbert_prefill_f32": ("pa_prefill.hip", "pa_prefill_f32x3.hip"),
     "modernbert_prefill_bf16": "pa_prefill_bf16.hip",
     "kv_write_modernbert_f32": "pa_cache.hip",
 }
@@ -79,9 +79,15 @@ def log(msg):
     print(msg, file=sys.stderr, flush=True)
 
 
-def source_sha(name):
-    p = os.path.join(ROOT, "sliding_window_mask_amd", "csrc", name)
-    return hashlib.sha256(open(p, "rb").read()).hexdigest()[:16]
+def source_sha(names):
+    """First 16 hex digits of the sha256 of a kernel source file, or of the
+    concatenation of several (a tuple of names)."""
+    if isinstance(names, str):
+        names = (names,)
+    h = hashlib.sha256()
+    for name in names:
+        h.update(open(os.path.join(ROOT, "sliding_window_mask_amd", "csrc", name), "rb").read())
+    return h.hexdigest()[:16]
 
 
 def read_traffic(workload, kernel_src, key="hbm_bytes_per_launch"):
@@ -671,7 +677,13 @@ def bench_prefill(args, dtype_name="f32"):
                   "frac": tflops / peak,
                   # HBM bytes of one step (the 12 launches), from the counters
                   "traffic": read_traffic(wl, KERNEL_SOURCE[wl], "hbm_bytes_per_step"),
-                  "kernel": "pa_prefill_%s (12 launches per step)" % dtype_name})
+                  "kernel": ("pa_prefill_f32x3 (4 full-attention launches: fp32 operands split "
+                             "into three bf16 parts on v_mfma_f32_16x16x32_bf16) + "
+                             "pa_prefill_f32 (8 window-64 launches, v_mfma_f32_16x16x4_f32); "
+                             "achieved and peak count fp32 flops"
+                             if dtype_name == "f32" else
+                             "pa_prefill_bf16_32 (4 full-attention launches) + pa_prefill_bf16 "
+                             "(8 window-64 launches)")})
     if args.profile_run:
         return line
     # per layer kind, and one full-attention layer with a materialised bias
@@ -687,6 +699,13 @@ def bench_prefill(args, dtype_name="f32"):
                      "mfma_frac": fl / (msl * 1e-3) / 1e12 / peak,
                      "GBps": by / (msl * 1e-3) / 1e9,
                      "hbm_frac": by / (msl * 1e-3) / 1e9 / HBM_PEAK_GBPS}
+        if dtype_name == "f32" and kind == "full_attention_layer":
+            # these launches run on the bf16 matrix cores, six bf16 products
+            # per fp32 product (operands split into three bf16 parts)
+            var[kind]["kernel"] = "pa_prefill_f32x3 (v_mfma_f32_16x16x32_bf16, split operands)"
+            var[kind]["bf16_mfma_TFLOPs_executed"] = 6 * fl / (msl * 1e-3) / 1e12
+            var[kind]["bf16_mfma_frac_executed"] = 6 * fl / (msl * 1e-3) / 1e12 / \
+                BF16_MFMA_PEAK_TFLOPS
     c, o = layers[full[0]], outs[full[0]]
     bias = torch.randn(c.num_seqs, 12, c.max_seq_len, c.max_seq_len, device="cuda")
     msb = time_steps(lambda: run_layer(c, o, bias), args.steps, args.warmup)
@@ -907,7 +926,7 @@ def write_profiles(a):
     md = ["# Kernel trace: %s (timed steps only)" % wl, "",
           "Command (on the MI355X box, from the repository root):", "",
           "    " + cmd, "",
-          "%s sha256[:16] = %s" % (src, sha), "",
+          "%s sha256[:16] = %s" % (" + ".join(src) if isinstance(src, tuple) else src, sha), "",
           "Averages over the last %d dispatches of the library's kernels: the %d timed "
           "steps of `--profile-run` (%d launch(es) per step); warm-up and clock-settling "
           "launches are excluded." % (n, line["steps"], line["launches_per_step"]), "",
@@ -985,7 +1004,9 @@ def write_counter_summary(a):
     old = open(path).read() if os.path.exists(path) and a.append else ""
     md = [old.rstrip() + "\n"] if old else ["# Counters: %s (timed steps of --profile-run)" % wl,
                                             "", "%s sha256[:16] = %s" % (
-                                                KERNEL_SOURCE[wl],
+                                                " + ".join(KERNEL_SOURCE[wl])
+                                                if isinstance(KERNEL_SOURCE[wl], tuple)
+                                                else KERNEL_SOURCE[wl],
                                                 source_sha(KERNEL_SOURCE[wl])), ""]
     md += ["Command: `%s`" % (a.command or "(not recorded)"), "",
            "| kernel | " + " | ".join(names) + " |", "|---|" + "---|" * len(names)]
