@@ -589,8 +589,7 @@ hipError_t launch_prefill_f32(const PrefillArgs& a, hipStream_t stream) {
   // bidirectional launches without a window or chunks at head_dim 64 (every
   // row sees every key of its sequence) run on the bf16 matrix cores with
   // operands split into three bf16 parts (pa_prefill_f32x3.hip)
-  if (PA_PREFILL_F32X3 && a.head_dim == 64 && !a.causal && a.window <= 0 && a.chunk <= 0 &&
-      !a.rel.table)
+  if (PA_PREFILL_F32X3 && a.head_dim == 64 && !a.causal && a.window <= 0 && a.chunk <= 0)
     return launch_prefill_f32x3(a, stream);
   return a.head_dim == 64 ? launch_d<64, PA_PREFILL_GROUPS>(a, stream)
                           : launch_d<128, 1>(a, stream);

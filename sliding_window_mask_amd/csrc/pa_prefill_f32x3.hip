@@ -92,9 +92,8 @@ struct IntC {
   static constexpr int value = N;
 };
 
-// BIAS: 0 none, 1 materialised (padded or ragged) fp32 bias. (The in-kernel
-// T5 bias stays on the fp32 kernel: its table would take this kernel past
-// 64 KiB of LDS.)
+// BIAS: 0 none, 1 materialised (padded or ragged) fp32 bias, 2 T5 relative
+// bias from a bucket table (a.rel).
 template <int BIAS>
 __global__ void __launch_bounds__(kThreads, 2)
 pa_prefill_f32x3(PrefillArgs a) {
@@ -145,6 +144,17 @@ pa_prefill_f32x3(PrefillArgs a) {
 
   __shared__ __attribute__((aligned(16))) uint16_t k_lds[2][3][kKT * kKRow];
   __shared__ __attribute__((aligned(16))) uint16_t v_lds[2][3][kKT * kVRow];
+  // T5 bias of relative position r = j - p for r in [-max_distance,
+  // max_distance] (longer distances share the end buckets), multiplied by
+  // scale * log2(e) as a materialised bias entry is; gfx950 gives a workgroup
+  // up to 160 KiB of LDS, and two of these workgroups (65 KiB each) fit a CU
+  __shared__ float rel_lds[BIAS == 2 ? 2 * kMaxRelDistance + 1 : 1];
+  const int rel_md = BIAS == 2 ? a.rel.max_distance : 0;
+  if constexpr (BIAS == 2) {
+    const float* head_row = a.rel.table + (int64_t)h * a.rel.num_buckets;
+    for (int i = tid; i <= 2 * rel_md; i += kThreads)
+      rel_lds[i] = rel_bias(i - rel_md, a.rel, head_row) * cs;
+  }
 
   const float* kc = static_cast<const float*>(a.k_cache);
   const float* vc = static_cast<const float*>(a.v_cache);
@@ -255,6 +265,11 @@ pa_prefill_f32x3(PrefillArgs a) {
       for (int ch = 0; ch < 2; ++ch) {
         const int c0 = base + ch * 16;
         const int j0 = c0 + 4 * g;
+        if constexpr (BIAS == 2) {
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            s[ch][r] = s[ch][r] + rel_lds[min(max(j0 + r - p_row, -rel_md), rel_md) + rel_md];
+        }
         if constexpr (BIAS == 1) {
           if (bias_vec && c0 + 16 <= L) {
 #pragma unroll
@@ -362,14 +377,16 @@ pa_prefill_f32x3(PrefillArgs a) {
 }  // namespace
 
 // Bidirectional launches without a window or chunks at head_dim 64, with a
-// materialised bias or none.
+// materialised bias, an in-kernel T5 bias or none.
 hipError_t launch_prefill_f32x3(PrefillArgs a, hipStream_t stream) {
   a.num_qtiles = (a.max_seq_len + kQT - 1) / kQT;
   const int64_t pairs = (int64_t)a.num_seqs * a.num_heads;
   const int64_t nwg = (pairs + kXcds - 1) / kXcds * kXcds * a.num_qtiles;
   if (nwg > 0x7fffffff) return hipErrorInvalidValue;
   const dim3 grid((unsigned)nwg), block(kThreads);
-  if (a.attn_bias)
+  if (a.rel.table)
+    hipLaunchKernelGGL((pa_prefill_f32x3<2>), grid, block, 0, stream, a);
+  else if (a.attn_bias)
     hipLaunchKernelGGL((pa_prefill_f32x3<1>), grid, block, 0, stream, a);
   else
     hipLaunchKernelGGL((pa_prefill_f32x3<0>), grid, block, 0, stream, a);
