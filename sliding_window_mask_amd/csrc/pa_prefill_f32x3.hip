@@ -21,10 +21,13 @@
 // Work decomposition: one workgroup of 8 wave64s per (128-query tile, head,
 // sequence), numbered and ordered as in the other prefill kernels (XCD-aware,
 // longest sequences first for batches of up to 63). Keys are walked in 32-key
-// tiles through a double-buffered LDS ring: the workgroup loads a tile's fp32
-// K and V rows (16 bytes per thread each), splits them and stores the three
-// bf16 planes of each, one tile ahead of use; the fp32 loads of the tile
-// after that are in flight meanwhile.
+// tiles through double-buffered LDS: the workgroup loads a tile's fp32 K and
+// V rows (16 bytes per thread each), splits them and stores the three bf16
+// planes of each. The loop is software-pipelined: each step issues the S^T
+// products of the next tile before the softmax of the current one, so the
+// matrix cores have independent work while the wave computes and splits the
+// weights. K of a tile is therefore staged two steps before its P.V step and
+// V one step before, and one barrier per step still suffices.
 //
 // Operand layouts (16x16x32, lane l, g = l / 16, c = l % 16), as in the bf16
 // prefill kernel: S^T = K Q^T over two 32-dim steps st, lane l feeding
@@ -168,31 +171,39 @@ pa_prefill_f32x3(PrefillArgs a) {
   // from an in-pool block (K there only feeds masked scores; V is zeroed)
   const int srow = tid >> 4;
   const int scol = (tid & 15) * 4;
-  int tb[2];
-  auto load_table = [&](int tk) {
+  // K and V of a tile are staged at different times (K two tiles ahead of
+  // its P.V step, V one), so each has its own block-table entries
+  int tbk[2], tbv[2];
+  auto load_table = [&](int (&tb)[2], int tk) {
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
       const int blk = tk * (kKT / kBlockSize) + i;
       tb[i] = blk < nblk_seq ? table[blk] : 0;
     }
   };
+  const uint32_t soff = (uint32_t)((srow % kBlockSize) * kD + scol);
   float4_t kst, vst;
-  auto fetch = [&](int tk) {
-    const int64_t blk = ((int64_t)tb[srow / kBlockSize] * H + h) * (kBlockSize * kD);
-    const uint32_t off = (uint32_t)((srow % kBlockSize) * kD + scol);
-    kst = *reinterpret_cast<const float4_t*>(kc + blk + off);
-    vst = *reinterpret_cast<const float4_t*>(vc + blk + off);
+  auto fetch_k = [&]() {
+    kst = *reinterpret_cast<const float4_t*>(
+        kc + ((int64_t)tbk[srow / kBlockSize] * H + h) * (kBlockSize * kD) + soff);
   };
-  // V rows at or past L are zeroed here, a tile after their loads were
-  // issued (a select right after the loads would wait for them at once)
-  auto stash = [&](int buf, int tk) {
-    uint2 k0, k1, k2, v0, v1, v2;
+  auto fetch_v = [&]() {
+    vst = *reinterpret_cast<const float4_t*>(
+        vc + ((int64_t)tbv[srow / kBlockSize] * H + h) * (kBlockSize * kD) + soff);
+  };
+  auto stash_k = [&](int buf) {
+    uint2 k0, k1, k2;
     split4(kst, k0, k1, k2);
-    if (tk * kKT + kKT > L && tk * kKT + srow >= L) vst = float4_t{0, 0, 0, 0};
-    split4(vst, v0, v1, v2);
     *reinterpret_cast<uint2*>(&k_lds[buf][0][srow * kKRow + scol]) = k0;
     *reinterpret_cast<uint2*>(&k_lds[buf][1][srow * kKRow + scol]) = k1;
     *reinterpret_cast<uint2*>(&k_lds[buf][2][srow * kKRow + scol]) = k2;
+  };
+  // V rows at or past L are zeroed here, a tile after their loads were
+  // issued (a select right after the loads would wait for them at once)
+  auto stash_v = [&](int buf, int tk) {
+    uint2 v0, v1, v2;
+    if (tk * kKT + kKT > L && tk * kKT + srow >= L) vst = float4_t{0, 0, 0, 0};
+    split4(vst, v0, v1, v2);
     *reinterpret_cast<uint2*>(&v_lds[buf][0][srow * kVRow + scol]) = v0;
     *reinterpret_cast<uint2*>(&v_lds[buf][1][srow * kVRow + scol]) = v1;
     *reinterpret_cast<uint2*>(&v_lds[buf][2][srow * kVRow + scol]) = v2;
@@ -216,64 +227,102 @@ pa_prefill_f32x3(PrefillArgs a) {
       BIAS == 1 &&
       __builtin_amdgcn_ballot_w64((reinterpret_cast<uintptr_t>(bias_row) & 15) != 0) == 0;
 
+  // ---- S^T = K Q^T of one tile: K_i Q_j for i + j <= 2, two 32-dim steps ----
+  auto qk = [&](auto kb_c, float4_t (&s)[2]) {
+    constexpr int kb = decltype(kb_c)::value;
+    s[0] = s[1] = float4_t{0, 0, 0, 0};
+#pragma unroll
+    for (int st = 0; st < 2; ++st) {
+#pragma unroll
+      for (int ch = 0; ch < 2; ++ch) {
+        const int o = (ch * 16 + c) * kKRow + 16 * g + 8 * st;
+        const bf16x8_t k0 = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(&k_lds[kb][0][o]));
+        const bf16x8_t k1 = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(&k_lds[kb][1][o]));
+        const bf16x8_t k2 = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(&k_lds[kb][2][o]));
+        s[ch] = mfma(k2, qp[0][st], s[ch]);
+        s[ch] = mfma(k1, qp[1][st], s[ch]);
+        s[ch] = mfma(k0, qp[2][st], s[ch]);
+        s[ch] = mfma(k1, qp[0][st], s[ch]);
+        s[ch] = mfma(k0, qp[1][st], s[ch]);
+        s[ch] = mfma(k0, qp[0][st], s[ch]);
+      }
+    }
+  };
+
+  // a lane's 4 bias entries of each 16-key chunk of a tile, loaded a step
+  // ahead (whole chunks, when the rows are 16-byte aligned)
+  float4_t bcur[2];
+  auto load_bias = [&](int tk) {
+#pragma unroll
+    for (int ch = 0; ch < 2; ++ch) {
+      const int c0 = tk * kKT + ch * 16;
+      bcur[ch] = float4_t{0, 0, 0, 0};
+      if (bias_vec && c0 + 16 <= L)
+        bcur[ch] = *reinterpret_cast<const float4_t*>(bias_row + c0 + 4 * g);
+    }
+  };
+
+  // Pipeline (one barrier per tile): entering step k, the scores S_k are in
+  // registers, K of tile k+1 and V of tile k are in LDS, and the loads of K
+  // of tile k+2 and V of tile k+1 are in flight. Step k issues the products
+  // of S_{k+1} before the softmax of tile k, so the matrix cores work on
+  // them while the wave computes the weights, then P.V of tile k; meanwhile
+  // K of tile k+2 goes to the K buffer that tile k left and V of tile k+1 to
+  // the V buffer that tile k-1 left.
+  float4_t s_cur[2];
+  s_cur[0] = s_cur[1] = float4_t{0, 0, 0, 0};
   if (ntiles > 0) {
-    load_table(0);
-    fetch(0);
-    stash(0, 0);
+    load_table(tbk, 0);
+    tbv[0] = tbk[0]; tbv[1] = tbk[1];
+    fetch_k();
+    fetch_v();
+    if (ntiles > 1) load_table(tbk, 1);
+    stash_k(0);
+    stash_v(0, 0);
     if (ntiles > 1) {
-      load_table(1);
-      fetch(1);
-      if (ntiles > 2) load_table(2);
+      fetch_k();
+      stash_k(1);
     }
   }
   __syncthreads();
+  // entering step k, tbv holds the table entries of tile k+2 and tbk those
+  // of tile k+3
+  if (ntiles > 0) {
+    if (wave_active) {
+      qk(IntC<0>{}, s_cur);
+      if constexpr (BIAS == 1) load_bias(0);
+    }
+    if (ntiles > 1) {
+      tbv[0] = tbk[0]; tbv[1] = tbk[1];   // tile 1
+      fetch_v();
+      if (ntiles > 2) {
+        load_table(tbk, 2);
+        fetch_k();
+        tbv[0] = tbk[0]; tbv[1] = tbk[1];   // tile 2
+      }
+      if (ntiles > 3) load_table(tbk, 3);
+    }
+  }
+  __syncthreads();   // every wave has read K of tile 0 before tile 2 replaces it
 
-  auto tile_step = [&](int tk, auto buf_c) {
-    constexpr int buf = decltype(buf_c)::value;
+  // One step. NEXT: a tile follows (its S^T products are issued here);
+  // LAST: the final tile, the only one that can reach past the sequence end.
+  auto tile_step = [&](int tk, auto buf_c, auto next_c, auto last_c) {
+    constexpr int buf = decltype(buf_c)::value;   // tk & 1
+    constexpr bool NEXT = decltype(next_c)::value;
+    constexpr bool LAST = decltype(last_c)::value;
     const int base = tk * kKT;
     if (wave_active) {
-      float4_t bpre[2];
+      float4_t* s = s_cur;
+      // ---- bias (added as a * scale * log2(e)) and the tail mask ----
       if constexpr (BIAS == 1) {
 #pragma unroll
         for (int ch = 0; ch < 2; ++ch) {
-          bpre[ch] = float4_t{0, 0, 0, 0};
-          if (bias_vec && base + ch * 16 + 16 <= L)
-            bpre[ch] = *reinterpret_cast<const float4_t*>(bias_row + base + ch * 16 + 4 * g);
-        }
-      }
-      // ---- S^T = K Q^T: K_i Q_j for i + j <= 2, over two 32-dim steps ----
-      float4_t s[2];
-      s[0] = s[1] = float4_t{0, 0, 0, 0};
+          const int c0 = base + ch * 16;
+          const int j0 = c0 + 4 * g;
+          if (bias_vec && (!LAST || c0 + 16 <= L)) {
 #pragma unroll
-      for (int st = 0; st < 2; ++st) {
-#pragma unroll
-        for (int ch = 0; ch < 2; ++ch) {
-          const int o = (ch * 16 + c) * kKRow + 16 * g + 8 * st;
-          const bf16x8_t k0 = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(&k_lds[buf][0][o]));
-          const bf16x8_t k1 = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(&k_lds[buf][1][o]));
-          const bf16x8_t k2 = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(&k_lds[buf][2][o]));
-          s[ch] = mfma(k2, qp[0][st], s[ch]);
-          s[ch] = mfma(k1, qp[1][st], s[ch]);
-          s[ch] = mfma(k0, qp[2][st], s[ch]);
-          s[ch] = mfma(k1, qp[0][st], s[ch]);
-          s[ch] = mfma(k0, qp[1][st], s[ch]);
-          s[ch] = mfma(k0, qp[0][st], s[ch]);
-        }
-      }
-      // ---- bias (added as a * scale * log2(e)) and the tail mask ----
-#pragma unroll
-      for (int ch = 0; ch < 2; ++ch) {
-        const int c0 = base + ch * 16;
-        const int j0 = c0 + 4 * g;
-        if constexpr (BIAS == 2) {
-#pragma unroll
-          for (int r = 0; r < 4; ++r)
-            s[ch][r] = s[ch][r] + rel_lds[min(max(j0 + r - p_row, -rel_md), rel_md) + rel_md];
-        }
-        if constexpr (BIAS == 1) {
-          if (bias_vec && c0 + 16 <= L) {
-#pragma unroll
-            for (int r = 0; r < 4; ++r) s[ch][r] = s[ch][r] + bpre[ch][r] * cs;
+            for (int r = 0; r < 4; ++r) s[ch][r] = s[ch][r] + bcur[ch][r] * cs;
           } else {
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
@@ -283,7 +332,18 @@ pa_prefill_f32x3(PrefillArgs a) {
             }
           }
         }
-        if (c0 + 16 > L) {   // uniform: only the chunks that reach past the sequence end
+        if constexpr (NEXT) load_bias(tk + 1);   // in flight until the next step
+      }
+#pragma unroll
+      for (int ch = 0; ch < 2; ++ch) {
+        const int c0 = base + ch * 16;
+        const int j0 = c0 + 4 * g;
+        if constexpr (BIAS == 2) {
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            s[ch][r] = s[ch][r] + rel_lds[min(max(j0 + r - p_row, -rel_md), rel_md) + rel_md];
+        }
+        if (LAST && c0 + 16 > L) {
 #pragma unroll
           for (int r = 0; r < 4; ++r)
             s[ch][r] = dq - c0 - r > dlo ? s[ch][r] : -INFINITY;
@@ -309,6 +369,9 @@ pa_prefill_f32x3(PrefillArgs a) {
 #pragma unroll
         for (int dt = 0; dt < kNDT; ++dt) acc[dt] *= alpha;
       }
+      // the next tile's products, independent of the weights computed below
+      float4_t s_next[2];
+      if constexpr (NEXT) qk(IntC<buf ^ 1>{}, s_next);
       // weights, split into three bf16 planes (keys 4g + e of chunk 0, then 1)
       uint32_t w0[4], w1[4], w2[4];
 #pragma unroll
@@ -349,17 +412,38 @@ pa_prefill_f32x3(PrefillArgs a) {
         acc[dt] = mfma(vv[0], p1, acc[dt]);
         acc[dt] = mfma(vv[0], p0, acc[dt]);
       }
+      if constexpr (NEXT) {
+        s_cur[0] = s_next[0];
+        s_cur[1] = s_next[1];
+      }
     }
-    if (tk + 1 < ntiles) stash(buf ^ 1, tk + 1);
-    if (tk + 2 < ntiles) {
-      fetch(tk + 2);
-      if (tk + 3 < ntiles) load_table(tk + 3);
+    if constexpr (NEXT) {
+      // staging: K of tile k+2 into the K buffer of tile k (read at step
+      // k-1), V of tile k+1 into the V buffer of tile k-1 (read at step k-1);
+      // then the loads of V of tile k+2 and K of tile k+3
+      if (tk + 2 < ntiles) stash_k(buf);
+      stash_v(buf ^ 1, tk + 1);
+      if (tk + 2 < ntiles) {
+        fetch_v();
+        if (tk + 3 < ntiles) {
+          fetch_k();
+          tbv[0] = tbk[0]; tbv[1] = tbk[1];   // tile k+3
+          if (tk + 4 < ntiles) load_table(tbk, tk + 4);
+        }
+      }
+      __syncthreads();
     }
-    __syncthreads();
   };
-  for (int tk = 0; tk < ntiles; tk += 2) {
-    tile_step(tk, IntC<0>{});
-    if (tk + 1 < ntiles) tile_step(tk + 1, IntC<1>{});
+  int tk = 0;
+  for (; tk + 2 < ntiles; tk += 2) {
+    tile_step(tk, IntC<0>{}, IntC<true>{}, IntC<false>{});
+    tile_step(tk + 1, IntC<1>{}, IntC<true>{}, IntC<false>{});
+  }
+  if (tk + 1 < ntiles) {
+    tile_step(tk, IntC<0>{}, IntC<true>{}, IntC<false>{});
+    tile_step(tk + 1, IntC<1>{}, IntC<false>{}, IntC<true>{});
+  } else if (tk < ntiles) {
+    tile_step(tk, IntC<0>{}, IntC<false>{}, IntC<true>{});
   }
 
   // ---- epilogue: out = O / l (lanes c, c+16, c+32, c+48 share a query) ----
