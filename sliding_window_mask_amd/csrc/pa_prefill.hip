@@ -584,12 +584,16 @@ hipError_t launch_d(PrefillArgs a, hipStream_t stream) {
 #ifndef PA_PREFILL_F32X3
 #define PA_PREFILL_F32X3 1
 #endif
+#ifndef PA_PREFILL_F32X3_BAND
+#define PA_PREFILL_F32X3_BAND 1
+#endif
 
 hipError_t launch_prefill_f32(const PrefillArgs& a, hipStream_t stream) {
-  // bidirectional launches without a window or chunks at head_dim 64 (every
-  // row sees every key of its sequence) run on the bf16 matrix cores with
-  // operands split into three bf16 parts (pa_prefill_f32x3.hip)
-  if (PA_PREFILL_F32X3 && a.head_dim == 64 && !a.causal && a.window <= 0 && a.chunk <= 0)
+  // launches at head_dim 64 run on the bf16 matrix cores with operands split
+  // into three bf16 parts (pa_prefill_f32x3.hip); PA_PREFILL_F32X3_BAND = 0
+  // keeps causal, windowed and chunked ones here
+  const bool banded = a.causal || a.window > 0 || a.chunk > 0;
+  if (PA_PREFILL_F32X3 && a.head_dim == 64 && (PA_PREFILL_F32X3_BAND || !banded))
     return launch_prefill_f32x3(a, stream);
   return a.head_dim == 64 ? launch_d<64, PA_PREFILL_GROUPS>(a, stream)
                           : launch_d<128, 1>(a, stream);

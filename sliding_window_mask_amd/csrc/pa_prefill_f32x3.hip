@@ -127,14 +127,19 @@ pa_prefill_f32x3(PrefillArgs a) {
 
   // q * scale * log2(e) in fp32, split into three bf16 planes: dims
   // 16 g + 8 st .. + 7 of the lane's query for the two steps st
-  bf16x8_t qp[3][2];
+  // (loaded here, split once the first tiles' loads are in flight)
+  float4_t qx[4];
   {
     const int tq = row_ok ? t_row : t_first;
     const float* qrow = static_cast<const float*>(a.q) + ((int64_t)(q0 + tq) * H + h) * kD + 16 * g;
 #pragma unroll
+    for (int i = 0; i < 4; ++i) qx[i] = *reinterpret_cast<const float4_t*>(qrow + 4 * i);
+  }
+  bf16x8_t qp[3][2];
+  auto split_q = [&]() {
+#pragma unroll
     for (int st = 0; st < 2; ++st) {
-      float4_t x0 = *reinterpret_cast<const float4_t*>(qrow + 8 * st);
-      float4_t x1 = *reinterpret_cast<const float4_t*>(qrow + 8 * st + 4);
+      float4_t x0 = qx[2 * st], x1 = qx[2 * st + 1];
       if (!row_ok) x0 = x1 = float4_t{0, 0, 0, 0};
       uint2 a0, a1, a2, b0, b1, b2;
       split4(x0 * cs, a0, a1, a2);
@@ -143,7 +148,7 @@ pa_prefill_f32x3(PrefillArgs a) {
       qp[1][st] = __builtin_bit_cast(bf16x8_t, make_uint4(a1.x, a1.y, b1.x, b1.y));
       qp[2][st] = __builtin_bit_cast(bf16x8_t, make_uint4(a2.x, a2.y, b2.x, b2.y));
     }
-  }
+  };
 
   __shared__ __attribute__((aligned(16))) uint16_t k_lds[2][3][kKT * kKRow];
   __shared__ __attribute__((aligned(16))) uint16_t v_lds[2][3][kKT * kVRow];
@@ -271,18 +276,30 @@ pa_prefill_f32x3(PrefillArgs a) {
   // the V buffer that tile k-1 left.
   float4_t s_cur[2];
   s_cur[0] = s_cur[1] = float4_t{0, 0, 0, 0};
+  // start-up: the table entries of tiles 0 and 1, then K and V of tile 0
+  // and K of tile 1, all in flight together
   if (ntiles > 0) {
+    int tb1[2] = {0, 0};
     load_table(tbk, 0);
+    if (ntiles > 1) load_table(tb1, 1);
     tbv[0] = tbk[0]; tbv[1] = tbk[1];
     fetch_k();
     fetch_v();
-    if (ntiles > 1) load_table(tbk, 1);
+    float4_t k1 = kst;
+    if (ntiles > 1) {
+      tbk[0] = tb1[0]; tbk[1] = tb1[1];
+      k1 = *reinterpret_cast<const float4_t*>(
+          kc + ((int64_t)tbk[srow / kBlockSize] * H + h) * (kBlockSize * kD) + soff);
+    }
+    split_q();
     stash_k(0);
     stash_v(0, 0);
     if (ntiles > 1) {
-      fetch_k();
+      kst = k1;
       stash_k(1);
     }
+  } else {
+    split_q();
   }
   __syncthreads();
   // entering step k, tbv holds the table entries of tile k+2 and tbk those
@@ -458,17 +475,461 @@ pa_prefill_f32x3(PrefillArgs a) {
     *reinterpret_cast<float4_t*>(orow + 16 * dt + 4 * g) = acc[dt] * inv;
 }
 
+// ---------------------------------------------------------------------------
+// Causal, windowed and chunked launches on the same split operands (BAND 0:
+// causal without a window, 1: window, 2: chunks). A workgroup walks only the
+// key tiles its rows may see ([lo, hi) of its positions, from the 16-key block
+// holding lo), each wave computes only the tiles its own 16 rows may see, and
+// a 16-key chunk that some row of a wave sees only in part is masked per
+// element; chunks inside every row's range take the unmasked path. The tile
+// loop is pipelined as in the kernel above.
+#ifndef PA_X3_BAND_PIPE
+#define PA_X3_BAND_PIPE 1
+#endif
+
+template <int BIAS, bool CAUSAL, int BAND>
+__global__ void __launch_bounds__(kThreads, 4)   // 4 waves per SIMD: two workgroups per CU
+pa_prefill_f32x3_band(PrefillArgs a) {
+  const int H = a.num_heads;
+  int b, h, tile, L, q0, nq;
+  if (!prefill_work_of(blockIdx.x, a, b, h, tile, L, q0, nq)) return;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform
+  const int c = lane & 15;
+  const int g = lane >> 4;
+  const int window = BAND == 1 ? a.window : 0;
+  const int chunk = BAND == 2 ? a.chunk : 0;
+  // The tile loop is pipelined as in the kernel above: the S^T products of
+  // tile k+1 are issued at step k (K of tile k+1 is in LDS then, and the
+  // buffer of tile k is refilled during step k). With kPipe they go before
+  // the softmax of tile k, overlapping it; with a materialised bias they go
+  // after its P.V, and the next tile's bias entries are requested with them,
+  // which keeps those variants within 128 VGPRs (four waves per SIMD)
+  // without spilling.
+  constexpr bool kPipe = BIAS != 1 && PA_X3_BAND_PIPE;
+
+  const int t_first = tile * kQT;
+  if (t_first >= nq) return;
+  const int pos0 = L - nq;
+  const int w_first = t_first + wave * 16;
+  const bool wave_active = w_first < nq;       // uniform over the wave
+
+  // the lane's query row: key j (d = p - j) is visible iff dlo < d < dhi;
+  // for key j = c0 + 4g + r, d = dq - c0 - r. Rows past the query set see no
+  // key (and so read no bias entry).
+  const int t_row = w_first + c;
+  const bool row_ok = t_row < nq;
+  const int p_row = pos0 + t_row;
+  const int dq = p_row - 4 * g;
+  int dlo, dhi;
+  if constexpr (BAND == 0) {
+    dlo = max(p_row - L, -1);
+    dhi = 0x7fffffff;
+  } else {
+    prefill_row_bounds(p_row, L, window, chunk, CAUSAL, dlo, dhi);
+  }
+  if (!row_ok) dlo = 0x7fffffff;
+  const float cs = a.scale_log2;
+
+  // keys [lo, hi) the workgroup's rows may see, walked in 32-key tiles from
+  // the 16-key block holding lo
+  int lo, hi;
+  prefill_key_range(pos0 + t_first, pos0 + min(t_first + kQT, nq) - 1, L, window, chunk, CAUSAL,
+                    lo, hi);
+  const int kstart = lo & ~(kBlockSize - 1);
+  const int ntiles = hi > kstart ? (hi - kstart + kKT - 1) / kKT : 0;
+  const int nblk = (hi + kBlockSize - 1) / kBlockSize;   // blocks backing keys below hi
+  // the wave's keys [wlo, whi), its tiles wt0 .. wt1, and the keys [cwlo,
+  // cwhi) every one of its rows sees (uniform)
+  int wlo = 0, whi = 0, wt0 = 1, wt1 = 0, cwlo = 0, cwhi = 0;
+  if (wave_active) {
+    const int pw0 = pos0 + w_first, pw1 = pos0 + min(w_first + 16, nq) - 1;
+    prefill_key_range(pw0, pw1, L, window, chunk, CAUSAL, wlo, whi);
+    if (whi > wlo) {
+      wt0 = (wlo - kstart) / kKT;
+      wt1 = (whi - 1 - kstart) / kKT;
+    }
+    if constexpr (BAND == 0) {
+      cwlo = 0;
+      cwhi = L;
+    } else {
+      prefill_common_keys(pw0, pw1, window, chunk, cwlo, cwhi);
+      cwhi = min(cwhi, L);
+    }
+    if (CAUSAL) cwhi = min(cwhi, pw0 + 1);
+  }
+  auto chunk_whole = [&](int c0) { return c0 >= cwlo && c0 + 16 <= cwhi; };
+  auto chunk_live = [&](int c0) { return c0 < whi && c0 + 16 > wlo; };
+
+  // q * scale * log2(e) in fp32, split into three bf16 planes
+  // (loaded here, split once the first tiles' loads are in flight)
+  float4_t qx[4];
+  {
+    const int tq = row_ok ? t_row : t_first;
+    const float* qrow = static_cast<const float*>(a.q) + ((int64_t)(q0 + tq) * H + h) * kD + 16 * g;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) qx[i] = *reinterpret_cast<const float4_t*>(qrow + 4 * i);
+  }
+  bf16x8_t qp[3][2];
+  auto split_q = [&]() {
+#pragma unroll
+    for (int st = 0; st < 2; ++st) {
+      float4_t x0 = qx[2 * st], x1 = qx[2 * st + 1];
+      if (!row_ok) x0 = x1 = float4_t{0, 0, 0, 0};
+      uint2 a0, a1, a2, b0, b1, b2;
+      split4(x0 * cs, a0, a1, a2);
+      split4(x1 * cs, b0, b1, b2);
+      qp[0][st] = __builtin_bit_cast(bf16x8_t, make_uint4(a0.x, a0.y, b0.x, b0.y));
+      qp[1][st] = __builtin_bit_cast(bf16x8_t, make_uint4(a1.x, a1.y, b1.x, b1.y));
+      qp[2][st] = __builtin_bit_cast(bf16x8_t, make_uint4(a2.x, a2.y, b2.x, b2.y));
+    }
+  };
+
+  __shared__ __attribute__((aligned(16))) uint16_t k_lds[2][3][kKT * kKRow];
+  __shared__ __attribute__((aligned(16))) uint16_t v_lds[2][3][kKT * kVRow];
+  __shared__ float rel_lds[BIAS == 2 ? 2 * kMaxRelDistance + 1 : 1];
+  const int rel_md = BIAS == 2 ? a.rel.max_distance : 0;
+  if constexpr (BIAS == 2) {
+    const float* head_row = a.rel.table + (int64_t)h * a.rel.num_buckets;
+    for (int i = tid; i <= 2 * rel_md; i += kThreads)
+      rel_lds[i] = rel_bias(i - rel_md, a.rel, head_row) * cs;
+  }
+
+  const float* kc = static_cast<const float*>(a.k_cache);
+  const float* vc = static_cast<const float*>(a.v_cache);
+  const int32_t* table = a.block_tables + (int64_t)b * a.max_blocks;
+
+  // staging as in the kernel above; blocks at or past hi come from an
+  // in-pool block (K there only feeds masked scores; V is zeroed), so no
+  // table entry backing only keys the workgroup cannot see is read
+  const int srow = tid >> 4;
+  const int scol = (tid & 15) * 4;
+  int tbk[2], tbv[2];
+  auto load_table = [&](int (&tb)[2], int tk) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int blk = kstart / kBlockSize + tk * (kKT / kBlockSize) + i;
+      tb[i] = blk < nblk ? table[blk] : 0;
+    }
+  };
+  const uint32_t soff = (uint32_t)((srow % kBlockSize) * kD + scol);
+  float4_t kst, vst;
+  auto fetch_k = [&]() {
+    kst = *reinterpret_cast<const float4_t*>(
+        kc + ((int64_t)tbk[srow / kBlockSize] * H + h) * (kBlockSize * kD) + soff);
+  };
+  auto fetch_v = [&]() {
+    vst = *reinterpret_cast<const float4_t*>(
+        vc + ((int64_t)tbv[srow / kBlockSize] * H + h) * (kBlockSize * kD) + soff);
+  };
+  auto stash_k = [&](int buf) {
+    uint2 k0, k1, k2;
+    split4(kst, k0, k1, k2);
+    *reinterpret_cast<uint2*>(&k_lds[buf][0][srow * kKRow + scol]) = k0;
+    *reinterpret_cast<uint2*>(&k_lds[buf][1][srow * kKRow + scol]) = k1;
+    *reinterpret_cast<uint2*>(&k_lds[buf][2][srow * kKRow + scol]) = k2;
+  };
+  auto stash_v = [&](int buf, int tk) {
+    const int base = kstart + tk * kKT;
+    if (base + kKT > hi && base + srow >= hi) vst = float4_t{0, 0, 0, 0};
+    uint2 v0, v1, v2;
+    split4(vst, v0, v1, v2);
+    *reinterpret_cast<uint2*>(&v_lds[buf][0][srow * kVRow + scol]) = v0;
+    *reinterpret_cast<uint2*>(&v_lds[buf][1][srow * kVRow + scol]) = v1;
+    *reinterpret_cast<uint2*>(&v_lds[buf][2][srow * kVRow + scol]) = v2;
+  };
+
+  float4_t acc[kNDT];
+#pragma unroll
+  for (int dt = 0; dt < kNDT; ++dt) acc[dt] = float4_t{0, 0, 0, 0};
+  float m_ref = -INFINITY, neg_m = 0.0f, l_run = 0.0f;
+  const float* bias_row = nullptr;
+  if (BIAS == 1) {
+    // rows past the query set take the wave's first row: they read entries
+    // only on chunks every row of the wave sees
+    const int tb_row = row_ok ? t_row : w_first;
+    bias_row = a.bias_start
+                   ? a.attn_bias + a.bias_start[b] + ((int64_t)h * nq + tb_row) * L
+                   : a.attn_bias +
+                         (((int64_t)b * H + h) * a.max_seq_len + pos0 + tb_row) * a.max_seq_len;
+  }
+  const bool bias_vec =
+      BIAS == 1 &&
+      __builtin_amdgcn_ballot_w64((reinterpret_cast<uintptr_t>(bias_row) & 15) != 0) == 0;
+  // a lane's 4 bias entries of each chunk inside every row's range (16-byte
+  // loads, when the rows are 16-byte aligned)
+  float4_t bcur[2];
+  auto load_bias = [&](int tk) {
+#pragma unroll
+    for (int ch = 0; ch < 2; ++ch) {
+      const int c0 = kstart + tk * kKT + ch * 16;
+      bcur[ch] = float4_t{0, 0, 0, 0};
+      if (bias_vec && chunk_whole(c0))
+        bcur[ch] = *reinterpret_cast<const float4_t*>(bias_row + c0 + 4 * g);
+    }
+  };
+
+  auto qk = [&](auto kb_c, float4_t (&s)[2]) {
+    constexpr int kb = decltype(kb_c)::value;
+    s[0] = s[1] = float4_t{0, 0, 0, 0};
+#pragma unroll
+    for (int st = 0; st < 2; ++st) {
+#pragma unroll
+      for (int ch = 0; ch < 2; ++ch) {
+        const int o = (ch * 16 + c) * kKRow + 16 * g + 8 * st;
+        const bf16x8_t k0 = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(&k_lds[kb][0][o]));
+        const bf16x8_t k1 = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(&k_lds[kb][1][o]));
+        const bf16x8_t k2 = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(&k_lds[kb][2][o]));
+        s[ch] = mfma(k2, qp[0][st], s[ch]);
+        s[ch] = mfma(k1, qp[1][st], s[ch]);
+        s[ch] = mfma(k0, qp[2][st], s[ch]);
+        s[ch] = mfma(k1, qp[0][st], s[ch]);
+        s[ch] = mfma(k0, qp[1][st], s[ch]);
+        s[ch] = mfma(k0, qp[0][st], s[ch]);
+      }
+    }
+  };
+
+  float4_t s_cur[2];
+  s_cur[0] = s_cur[1] = float4_t{0, 0, 0, 0};
+  // start-up: the table entries of tiles 0 and 1, then K and V of tile 0
+  // and K of tile 1, all in flight together
+  if (ntiles > 0) {
+    int tb1[2] = {0, 0};
+    load_table(tbk, 0);
+    if (ntiles > 1) load_table(tb1, 1);
+    tbv[0] = tbk[0]; tbv[1] = tbk[1];
+    fetch_k();
+    fetch_v();
+    float4_t k1 = kst;
+    if (ntiles > 1) {
+      tbk[0] = tb1[0]; tbk[1] = tb1[1];
+      k1 = *reinterpret_cast<const float4_t*>(
+          kc + ((int64_t)tbk[srow / kBlockSize] * H + h) * (kBlockSize * kD) + soff);
+    }
+    split_q();
+    stash_k(0);
+    stash_v(0, 0);
+    if (ntiles > 1) {
+      kst = k1;
+      stash_k(1);
+    }
+  } else {
+    split_q();
+  }
+  __syncthreads();
+  if (ntiles > 0) {
+    if (wave_active && wt0 == 0) {
+      qk(IntC<0>{}, s_cur);
+      if constexpr (BIAS == 1) load_bias(0);
+    }
+    if (ntiles > 1) {
+      tbv[0] = tbk[0]; tbv[1] = tbk[1];   // tile 1
+      fetch_v();
+      if (ntiles > 2) {
+        load_table(tbk, 2);
+        fetch_k();
+        tbv[0] = tbk[0]; tbv[1] = tbk[1];   // tile 2
+      }
+      if (ntiles > 3) load_table(tbk, 3);
+    }
+  }
+  __syncthreads();
+
+  typedef __attribute__((address_space(3))) i16x4_t lds_i16x4_t;
+  // softmax and P.V of tile tk (in the wave's range); NEXT: tile tk + 1 is in
+  // the wave's range too, and its products are issued here
+  auto body = [&](int tk, auto buf_c, auto next_c) {
+    constexpr int buf = decltype(buf_c)::value;
+    constexpr bool NEXT = decltype(next_c)::value;
+    const int base = kstart + tk * kKT;
+    float4_t* s = s_cur;
+#pragma unroll
+    for (int ch = 0; ch < 2; ++ch) {
+      const int c0 = base + ch * 16;
+      const int j0 = c0 + 4 * g;
+      if constexpr (BIAS == 2) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          s[ch][r] = s[ch][r] + rel_lds[min(max(j0 + r - p_row, -rel_md), rel_md) + rel_md];
+      }
+      if (chunk_whole(c0)) {   // uniform
+        if constexpr (BIAS == 1) {
+          if (bias_vec) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) s[ch][r] = s[ch][r] + bcur[ch][r] * cs;
+          } else {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) s[ch][r] = s[ch][r] + bias_row[j0 + r] * cs;
+          }
+        }
+      } else if (chunk_live(c0)) {
+        const int d0 = dq - c0;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int d = d0 - r;
+          float x = -INFINITY;
+          if (d > dlo && d < dhi) {
+            x = s[ch][r];
+            if constexpr (BIAS == 1) x = x + bias_row[j0 + r] * cs;
+          }
+          s[ch][r] = x;
+        }
+      } else {
+        s[ch] = float4_t{-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+      }
+    }
+    float mt = vmax(vmax(vmax(s[0][0], s[0][1]), vmax(s[0][2], s[0][3])),
+                    vmax(vmax(s[1][0], s[1][1]), vmax(s[1][2], s[1][3])));
+    {
+      const auto x16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(mt),
+                                                        __float_as_uint(mt), false, false);
+      mt = vmax(__uint_as_float(x16[0]), __uint_as_float(x16[1]));
+      const auto x32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(mt),
+                                                        __float_as_uint(mt), false, false);
+      mt = vmax(__uint_as_float(x32[0]), __uint_as_float(x32[1]));
+    }
+    const bool move = mt > m_ref + 8.0f;
+    if (__builtin_amdgcn_ballot_w64(move) != 0) {
+      const float alpha = move ? __builtin_amdgcn_exp2f(m_ref - mt) : 1.0f;
+      m_ref = move ? mt : m_ref;
+      neg_m = move ? -mt : neg_m;
+      l_run *= alpha;
+#pragma unroll
+      for (int dt = 0; dt < kNDT; ++dt) acc[dt] *= alpha;
+    }
+    float4_t s_next[2];
+    if constexpr (NEXT && kPipe) qk(IntC<buf ^ 1>{}, s_next);
+    uint32_t w0[4], w1[4], w2[4];
+#pragma unroll
+    for (int ch = 0; ch < 2; ++ch) {
+      float pr[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        pr[r] = __builtin_amdgcn_exp2f(s[ch][r] + neg_m);
+        l_run += pr[r];
+      }
+      uint2 a0, a1, a2;
+      split4(float4_t{pr[0], pr[1], pr[2], pr[3]}, a0, a1, a2);
+      w0[2 * ch] = a0.x; w0[2 * ch + 1] = a0.y;
+      w1[2 * ch] = a1.x; w1[2 * ch + 1] = a1.y;
+      w2[2 * ch] = a2.x; w2[2 * ch + 1] = a2.y;
+    }
+    const bf16x8_t p0 = __builtin_bit_cast(bf16x8_t, make_uint4(w0[0], w0[1], w0[2], w0[3]));
+    const bf16x8_t p1 = __builtin_bit_cast(bf16x8_t, make_uint4(w1[0], w1[1], w1[2], w1[3]));
+    const bf16x8_t p2 = __builtin_bit_cast(bf16x8_t, make_uint4(w2[0], w2[1], w2[2], w2[3]));
+#pragma unroll
+    for (int dt = 0; dt < kNDT; ++dt) {
+      bf16x8_t vv[3];
+#pragma unroll
+      for (int pl = 0; pl < 3; ++pl) {
+        const uint16_t* pp = &v_lds[buf][pl][(4 * g + (c >> 2)) * kVRow + 16 * dt + 4 * (c & 3)];
+        const uint2 lo2 = __builtin_bit_cast(
+            uint2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)pp));
+        const uint2 hi2 = __builtin_bit_cast(
+            uint2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(pp + 16 * kVRow)));
+        vv[pl] = __builtin_bit_cast(bf16x8_t, make_uint4(lo2.x, lo2.y, hi2.x, hi2.y));
+      }
+      acc[dt] = mfma(vv[2], p0, acc[dt]);
+      acc[dt] = mfma(vv[1], p1, acc[dt]);
+      acc[dt] = mfma(vv[0], p2, acc[dt]);
+      acc[dt] = mfma(vv[1], p0, acc[dt]);
+      acc[dt] = mfma(vv[0], p1, acc[dt]);
+      acc[dt] = mfma(vv[0], p0, acc[dt]);
+    }
+    if constexpr (NEXT) {
+      if constexpr (kPipe) {
+        s_cur[0] = s_next[0];
+        s_cur[1] = s_next[1];
+      } else {
+        qk(IntC<buf ^ 1>{}, s_cur);
+        if constexpr (BIAS == 1) load_bias(tk + 1);   // in flight until the next step
+      }
+    }
+  };
+  auto tile_step = [&](int tk, auto buf_c) {
+    constexpr int buf = decltype(buf_c)::value;   // tk & 1
+    const bool cur = wave_active && tk >= wt0 && tk <= wt1;            // uniform
+    const bool nxt = wave_active && tk + 1 >= wt0 && tk + 1 <= wt1;    // uniform
+    if (cur) {
+      if (nxt)
+        body(tk, buf_c, IntC<1>{});
+      else
+        body(tk, buf_c, IntC<0>{});
+    } else if (nxt) {   // the wave's first tile follows
+      qk(IntC<buf ^ 1>{}, s_cur);
+      if constexpr (BIAS == 1) load_bias(tk + 1);
+    }
+    if (tk + 1 < ntiles) {
+      // staging as in the kernel above
+      if (tk + 2 < ntiles) stash_k(buf);
+      stash_v(buf ^ 1, tk + 1);
+      if (tk + 2 < ntiles) {
+        fetch_v();
+        if (tk + 3 < ntiles) {
+          fetch_k();
+          tbv[0] = tbk[0]; tbv[1] = tbk[1];   // tile k+3
+          if (tk + 4 < ntiles) load_table(tbk, tk + 4);
+        }
+      }
+      __syncthreads();
+    }
+  };
+  for (int tk = 0; tk < ntiles; tk += 2) {
+    tile_step(tk, IntC<0>{});
+    if (tk + 1 < ntiles) tile_step(tk + 1, IntC<1>{});
+  }
+
+  float l_tot = l_run;
+  l_tot += __shfl_xor(l_tot, 16);
+  l_tot += __shfl_xor(l_tot, 32);
+  if (!row_ok) return;
+  const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
+  float* orow = static_cast<float*>(a.out) + ((int64_t)(q0 + t_row) * H + h) * kD;
+#pragma unroll
+  for (int dt = 0; dt < kNDT; ++dt)
+    *reinterpret_cast<float4_t*>(orow + 16 * dt + 4 * g) = acc[dt] * inv;
+}
+
+template <int BIAS>
+void launch_band(const PrefillArgs& a, dim3 grid, hipStream_t stream) {
+  const dim3 block(kThreads);
+  if (a.window > 0) {
+    if (a.causal)
+      hipLaunchKernelGGL((pa_prefill_f32x3_band<BIAS, true, 1>), grid, block, 0, stream, a);
+    else
+      hipLaunchKernelGGL((pa_prefill_f32x3_band<BIAS, false, 1>), grid, block, 0, stream, a);
+  } else if (a.chunk > 0) {
+    if (a.causal)
+      hipLaunchKernelGGL((pa_prefill_f32x3_band<BIAS, true, 2>), grid, block, 0, stream, a);
+    else
+      hipLaunchKernelGGL((pa_prefill_f32x3_band<BIAS, false, 2>), grid, block, 0, stream, a);
+  } else {
+    hipLaunchKernelGGL((pa_prefill_f32x3_band<BIAS, true, 0>), grid, block, 0, stream, a);
+  }
+}
+
 }  // namespace
 
-// Bidirectional launches without a window or chunks at head_dim 64, with a
-// materialised bias, an in-kernel T5 bias or none.
+// Launches at head_dim 64, with a materialised bias, an in-kernel T5 bias or
+// none: bidirectional ones without a window or chunks take the first kernel,
+// causal, windowed and chunked ones the banded one.
 hipError_t launch_prefill_f32x3(PrefillArgs a, hipStream_t stream) {
   a.num_qtiles = (a.max_seq_len + kQT - 1) / kQT;
   const int64_t pairs = (int64_t)a.num_seqs * a.num_heads;
   const int64_t nwg = (pairs + kXcds - 1) / kXcds * kXcds * a.num_qtiles;
   if (nwg > 0x7fffffff) return hipErrorInvalidValue;
   const dim3 grid((unsigned)nwg), block(kThreads);
-  if (a.rel.table)
+  if (a.causal || a.window > 0 || a.chunk > 0) {
+    if (a.rel.table)
+      launch_band<2>(a, grid, stream);
+    else if (a.attn_bias)
+      launch_band<1>(a, grid, stream);
+    else
+      launch_band<0>(a, grid, stream);
+  } else if (a.rel.table)
     hipLaunchKernelGGL((pa_prefill_f32x3<2>), grid, block, 0, stream, a);
   else if (a.attn_bias)
     hipLaunchKernelGGL((pa_prefill_f32x3<1>), grid, block, 0, stream, a);
