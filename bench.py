@@ -677,10 +677,10 @@ def bench_prefill(args, dtype_name="f32"):
                   "frac": tflops / peak,
                   # HBM bytes of one step (the 12 launches), from the counters
                   "traffic": read_traffic(wl, KERNEL_SOURCE[wl], "hbm_bytes_per_step"),
-                  "kernel": ("pa_prefill_f32x3 (4 full-attention launches: fp32 operands split "
-                             "into three bf16 parts on v_mfma_f32_16x16x32_bf16) + "
-                             "pa_prefill_f32 (8 window-64 launches, v_mfma_f32_16x16x4_f32); "
-                             "achieved and peak count fp32 flops"
+                  "kernel": ("pa_prefill_f32x3 (4 full-attention launches) + "
+                             "pa_prefill_f32x3_band (8 window-64 launches), both with fp32 "
+                             "operands split into three bf16 parts on "
+                             "v_mfma_f32_16x16x32_bf16; achieved and peak count fp32 flops"
                              if dtype_name == "f32" else
                              "pa_prefill_bf16_32 (4 full-attention launches) + pa_prefill_bf16 "
                              "(8 window-64 launches)")})
@@ -699,6 +699,8 @@ def bench_prefill(args, dtype_name="f32"):
                      "mfma_frac": fl / (msl * 1e-3) / 1e12 / peak,
                      "GBps": by / (msl * 1e-3) / 1e9,
                      "hbm_frac": by / (msl * 1e-3) / 1e9 / HBM_PEAK_GBPS}
+        if dtype_name == "f32" and kind == "window_64_layer":
+            var[kind]["kernel"] = "pa_prefill_f32x3_band (v_mfma_f32_16x16x32_bf16, split operands)"
         if dtype_name == "f32" and kind == "full_attention_layer":
             # these launches run on the bf16 matrix cores, six bf16 products
             # per fp32 product (operands split into three bf16 parts)
@@ -753,7 +755,8 @@ def bench_chunked_prefill(args, dtype_name="f32"):
                  launches_per_step=1, algorithmic_flops_per_step=flops,
                  roofline={"bound": "mfma", "achieved": tflops, "peak": peak,
                            "unit": "TFLOP/s", "frac": tflops / peak, "traffic": None,
-                           "kernel": "pa_prefill_%s (banded variant, one launch)" % dtype_name})
+                           "kernel": "pa_prefill_f32x3_band (one launch, split bf16 operands)"
+                           if dtype_name == "f32" else "pa_prefill_bf16 (banded variant, one launch)"})
 
 
 def bench_copy(args):
