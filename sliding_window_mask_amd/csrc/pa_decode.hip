@@ -165,11 +165,17 @@ __device__ __forceinline__ uint4 load16(const char* p) {
 #endif
 }
 
-// 16-token blocks each wave keeps in flight per loop iteration
+// 16-token blocks each wave keeps in flight per loop iteration: 8 for bf16
+// at head_dim 64 (2 KiB per block and head, 16 loads of 16 bytes per lane,
+// within 5+ waves per SIMD), 4 otherwise
 #ifndef PA_DECODE_UNROLL
 #define PA_DECODE_UNROLL 4
 #endif
-constexpr int kUnroll = PA_DECODE_UNROLL;
+#ifndef PA_DECODE_UNROLL_BF16_64
+#define PA_DECODE_UNROLL_BF16_64 8
+#endif
+template <int DT, int D>
+constexpr int unroll_of() { return DT == 1 && D == 64 ? PA_DECODE_UNROLL_BF16_64 : PA_DECODE_UNROLL; }
 // bias entries per thread fetched before the key pass
 constexpr int kBiasPre = 4;
 
@@ -190,6 +196,7 @@ template <int DT, int D, int BIAS, bool SINGLE>
 __global__ void __launch_bounds__(kDecodeThreads)
 pa_decode_partition(DecodeArgs a) {
   using G = Geo<DT, D>;
+  constexpr int kUnroll = unroll_of<DT, D>();
   const int h = blockIdx.x;
   const int part = blockIdx.y;
   const int b = blockIdx.z;
