@@ -193,7 +193,10 @@ pa_status_t paged_attn_decode_noalloc(void* out, const void* q, const void* k_ca
  *   attn_bias       [num_seqs, num_heads, max_seq_len, max_seq_len] fp32, or NULL
  *   causal          0 or 1
  *   dtype           PA_DTYPE_F32 or PA_DTYPE_BF16 (bf16: bf16 MFMA with fp32
- *                   accumulation; the softmax weights enter P.V as bf16)
+ *                   accumulation; the softmax weights enter P.V as bf16.
+ *                   fp32: fp32 accuracy; at head_dim 64 both contractions run
+ *                   on the bf16 matrix cores with every fp32 operand split
+ *                   exactly into three bf16 parts, at 128 on fp32 MFMA)
  *   Other arguments as for paged_attn_decode. No workspace is needed.
  *   total_q = 0 computes nothing and returns PA_OK after the scalar checks;
  *   then no device pointer is read and any of them may be NULL (the same
