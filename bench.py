@@ -29,7 +29,11 @@ Prints ONE JSON line. Options:
                   modernbert_chunked_prefill_bf16 (one layer, 128-token chunks) |
                   t5_small_self_decode_bf16 | t5_large_cross_decode_bf16 (calls rotating
                   over input copies > 1 GiB) | kv_write_modernbert_f32 | copy_probe (a plain
-                  device copy of known size, for calibrating the rocprofv3 byte counters)
+                  device copy of known size, for calibrating the rocprofv3 byte counters) |
+                  prefill_window_sweep | probe_mfma | probe_lds | probe_stream |
+                  probe_gather (hardware rates from
+                  bench_probes.hip: matrix instructions, LDS reads, a streaming read, the
+                  decode's K/V gather without arithmetic)
   --no-cpu-baseline   skip the oracle timing
   --no-variants       skip the window / chunk / null-bias / no-bias-build variants
   --no-configs        default workload only: skip the other workloads' entries
@@ -824,6 +828,168 @@ def bench_configs(args):
     return out
 
 
+def bench_prefill_window_sweep(args):
+    """One ModernBERT-shaped layer (32 sequences, lengths U[64, 1024], 12
+    heads, head_dim 64, no bias) through the product prefill call at a range
+    of sliding windows, in both dtypes."""
+    import torch
+    import sliding_window_mask_amd as pa
+    lib = pa.lib()
+    rows = []
+    for dtype_name, dtype, esize in (("f32", torch.float32, 4), ("bf16", torch.bfloat16, 2)):
+        c = modernbert_layers(dtype)[0]
+        o = torch.empty_like(c.q)
+        torch.cuda.synchronize()
+        by = prefill_bytes(c.lens, 12, 64, esize)
+        for w in (1, 16, 32, 64, 128, 256, 512, -1):
+            msl = time_steps(lambda: lib.paged_attn_prefill(
+                c.q, c.k_cache, c.v_cache, c.block_tables, c.context_lens, c.query_start_loc,
+                None, w, False, c.scale, max_seq_len=c.max_seq_len, out=o),
+                args.steps, args.warmup)
+            fl = prefill_flops(c.lens, 12, 64, w)
+            rows.append({"dtype": dtype_name, "sliding_window": w, "us_per_layer": msl * 1e3,
+                         "TFLOPs": fl / (msl * 1e-3) / 1e12,
+                         "GBps": by / (msl * 1e-3) / 1e9})
+    return {"metric": "prefill layer time by sliding window", "rows": rows,
+            "note": "one layer of the 12-layer ModernBERT-shaped step; GBps counts q, K, V "
+                    "read once and the output written once"}
+
+
+# ----------------------------------------------------------------------------
+# hardware probes (bench_probes.hip, built by __graft_entry__.build())
+# ----------------------------------------------------------------------------
+def _probe_lib():
+    import ctypes
+    path = os.path.join(ROOT, "bench_probes.so")
+    if not os.path.exists(path):
+        raise SystemExit("bench_probes.so is not built: run __graft_entry__.build()")
+    lib = ctypes.CDLL(path)
+    P, I, I64 = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64
+    lib.pb_mfma.argtypes = [I, I, I, I, I, P, P]
+    lib.pb_lds.argtypes = [I, I, I, P, P]
+    lib.pb_stream.argtypes = [P, I64, I, P, P]
+    lib.pb_gather.argtypes = [I, P, P, P, P, I, I, I, I, P, P]
+    for f in (lib.pb_mfma, lib.pb_lds, lib.pb_stream, lib.pb_gather):
+        f.restype = I
+    return lib
+
+
+def _probe_call(rc):
+    if rc != 0:
+        raise RuntimeError("probe launch failed (%d)" % rc)
+
+
+def bench_probe_mfma(args):
+    """Rate each matrix instruction sustains with independent accumulator
+    chains in every wave (registers only), at several waves per SIMD, and
+    with v_exp_f32 work interleaved."""
+    import torch
+    lib = _probe_lib()
+    stream = torch.cuda.current_stream().cuda_stream
+    kinds = {0: ("v_mfma_f32_16x16x32_bf16", 2 * 16 * 16 * 32, BF16_MFMA_PEAK_TFLOPS),
+             1: ("v_mfma_f32_32x32x16_bf16", 2 * 32 * 32 * 16, BF16_MFMA_PEAK_TFLOPS),
+             2: ("v_mfma_f32_16x16x4_f32", 2 * 16 * 16 * 4, FP32_MFMA_PEAK_TFLOPS),
+             3: ("v_mfma_f32_32x32x2_f32", 2 * 32 * 32 * 2, FP32_MFMA_PEAK_TFLOPS)}
+    cases = [(k, wps, ch, 0) for k in kinds for wps, ch in ((2, 4), (4, 4), (8, 4), (4, 8))]
+    cases += [(k, 4, ch, e) for k in (0, 1) for ch, e in ((4, 1), (4, 2), (2, 2), (2, 4))]
+    iters = 8000
+    rows = []
+    out = torch.empty(256 * 8 * 256, dtype=torch.float32, device="cuda")
+    for kind, wps, ch, ex in cases:
+        grid = 256 * wps                    # 4-wave workgroups: wps waves per SIMD
+        ms = time_steps(lambda: _probe_call(lib.pb_mfma(kind, ch, ex, grid, iters,
+                                                        out.data_ptr(), stream)),
+                        args.steps, args.warmup)
+        name, flops, peak = kinds[kind]
+        tf = flops * ch * iters * grid * 4 / (ms * 1e-3) / 1e12
+        rows.append({"instruction": name, "waves_per_simd": wps, "chains_per_wave": ch,
+                     "exp_per_product": ex, "ms": ms, "TFLOPs": tf, "frac_of_peak": tf / peak})
+    return {"metric": "probe: sustained matrix-instruction rates", "rows": rows,
+            "note": "independent accumulator chains per wave, registers only; grid = 256 "
+                    "CUs x waves_per_simd 4-wave workgroups, %d iterations" % iters}
+
+
+def bench_probe_lds(args):
+    """LDS read rate per CU: conflict-free 16-byte reads (ds_read_b128) and
+    transposing 8-byte reads (ds_read_b64_tr_b16)."""
+    import torch
+    lib = _probe_lib()
+    stream = torch.cuda.current_stream().cuda_stream
+    iters = 4000
+    out = torch.empty(256 * 8 * 256, dtype=torch.float32, device="cuda")
+    rows = []
+    for wgs in (2, 4, 8):
+        for kind, name, size in ((0, "ds_read_b128", 16), (1, "ds_read_b64_tr_b16", 8)):
+            grid = 256 * wgs
+            ms = time_steps(lambda: _probe_call(lib.pb_lds(kind, grid, iters, out.data_ptr(),
+                                                           stream)), args.steps, args.warmup)
+            nbytes = grid * 256 * iters * 8 * size
+            rows.append({"read": name, "workgroups_per_cu": wgs, "ms": ms,
+                         "TBps": nbytes / (ms * 1e-3) / 1e12,
+                         "bytes_per_clk_per_cu_at_2.4GHz": nbytes / (ms * 1e-3) / 256 / 2.4e9})
+    return {"metric": "probe: LDS read rate", "rows": rows,
+            "note": "4-wave workgroups, each wave reading 1 KiB LDS rows; %d x 8 reads per "
+                    "thread" % iters}
+
+
+def bench_probe_stream(args):
+    """A streaming read of 8 GiB with non-temporal 16-byte loads."""
+    import torch
+    lib = _probe_lib()
+    stream = torch.cuda.current_stream().cuda_stream
+    nbytes = 8 << 30
+    src = torch.zeros(nbytes, dtype=torch.uint8, device="cuda")
+    rows = []
+    for grid in (256 * 8, 256 * 16, 256 * 32):
+        out = torch.empty(grid * 256, dtype=torch.float32, device="cuda")
+        ms = time_steps(lambda: _probe_call(lib.pb_stream(src.data_ptr(), nbytes, grid,
+                                                          out.data_ptr(), stream)),
+                        args.steps, args.warmup)
+        gbps = nbytes / (ms * 1e-3) / 1e9
+        rows.append({"workgroups": grid, "ms": ms, "GBps": gbps, "hbm_frac": gbps / HBM_PEAK_GBPS})
+    return {"metric": "probe: streaming read GB/s", "value": max(r["GBps"] for r in rows),
+            "rows": rows, "bytes": nbytes,
+            "note": "non-temporal 16-byte loads, 4 in flight per thread, 256-thread workgroups"}
+
+
+def bench_probe_gather(args):
+    """The large decode's K/V gather (same block tables, 4 blocks in flight
+    per wave, K pass then V pass, non-temporal loads) with no arithmetic and
+    no bias, next to the decode call on the same inputs."""
+    import torch
+    import sliding_window_mask_amd as pa
+    import workloads
+    lib = _probe_lib()
+    stream = torch.cuda.current_stream().cuda_stream
+    case = workloads.large_biased_decode_bf16(device="cuda")
+    torch.cuda.synchronize()
+    B, H, D = case.q.shape
+    block_bytes = 16 * D * case.k_cache.element_size()
+    out = torch.empty(B * H * 256, dtype=torch.float32, device="cuda")
+    kv = 2 * H * block_bytes * int(np.sum((case.lens + 15) // 16))
+    modes = {}
+    for mode, name in ((0, "k_then_v_nontemporal"), (1, "k_then_v_ordinary_loads"),
+                       (2, "k_and_v_together_nontemporal")):
+        msm = time_steps(lambda: _probe_call(lib.pb_gather(
+            mode, case.k_cache.data_ptr(), case.v_cache.data_ptr(),
+            case.block_tables.data_ptr(), case.context_lens.data_ptr(), B, H, block_bytes,
+            case.block_tables.shape[1], out.data_ptr(), stream)), args.steps, args.warmup)
+        modes[name] = {"ms": msm, "kv_GBps": kv / (msm * 1e-3) / 1e9}
+    ms = modes["k_then_v_nontemporal"]["ms"]
+    o = torch.empty_like(case.q)
+    dec = pa.lib()
+    ws = dec.workspace_for(case.q, case.max_seq_len, case.sliding_window)
+    ms_dec = time_steps(lambda: dec.paged_attn_decode(
+        case.q, case.k_cache, case.v_cache, case.block_tables, case.context_lens,
+        case.attn_bias, -1, case.scale, max_seq_len=case.max_seq_len, out=o, workspace=ws),
+        args.steps, args.warmup)
+    return {"metric": "probe: decode K/V gather without arithmetic", "ms_gather": ms,
+            "kv_GBps": kv / (ms * 1e-3) / 1e9, "orders": modes, "ms_decode_call": ms_dec,
+            "decode_kv_GBps": kv / (ms_dec * 1e-3) / 1e9, "kv_bytes": kv,
+            "note": "large biased decode inputs (256 x 32 heads, head_dim 128, bf16); the "
+                    "decode call also reads the bias and q and writes the output"}
+
+
 # ----------------------------------------------------------------------------
 # profile summaries (rocprofv3 output -> profiles/)
 # ----------------------------------------------------------------------------
@@ -1110,6 +1276,16 @@ def main():
         line = bench_kv_write(args)
     elif args.workload == "copy_probe":
         line = bench_copy(args)
+    elif args.workload == "prefill_window_sweep":
+        line = bench_prefill_window_sweep(args)
+    elif args.workload == "probe_mfma":
+        line = bench_probe_mfma(args)
+    elif args.workload == "probe_lds":
+        line = bench_probe_lds(args)
+    elif args.workload == "probe_stream":
+        line = bench_probe_stream(args)
+    elif args.workload == "probe_gather":
+        line = bench_probe_gather(args)
     else:
         raise SystemExit("unknown workload %s" % args.workload)
     print(json.dumps(line), flush=True)
