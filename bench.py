@@ -31,7 +31,7 @@ Prints ONE JSON line. Options:
                   over input copies > 1 GiB) | kv_write_modernbert_f32 | copy_probe (a plain
                   device copy of known size, for calibrating the rocprofv3 byte counters) |
                   prefill_window_sweep | probe_mfma | probe_lds | probe_stream |
-                  probe_gather (hardware rates from
+                  probe_gather | probe_gather_t5 | probe_bias (hardware rates from
                   bench_probes.hip: matrix instructions, LDS reads, a streaming read, the
                   decode's K/V gather without arithmetic)
   --no-cpu-baseline   skip the oracle timing
@@ -869,7 +869,8 @@ def _probe_lib():
     lib.pb_lds.argtypes = [I, I, I, P, P]
     lib.pb_stream.argtypes = [P, I64, I, P, P]
     lib.pb_gather.argtypes = [I, P, P, P, P, I, I, I, I, P, P]
-    for f in (lib.pb_mfma, lib.pb_lds, lib.pb_stream, lib.pb_gather):
+    lib.pb_bias.argtypes = [P, P, I, I, I, I, I, P, P]
+    for f in (lib.pb_mfma, lib.pb_lds, lib.pb_stream, lib.pb_gather, lib.pb_bias):
         f.restype = I
     return lib
 
@@ -950,6 +951,110 @@ def bench_probe_stream(args):
     return {"metric": "probe: streaming read GB/s", "value": max(r["GBps"] for r in rows),
             "rows": rows, "bytes": nbytes,
             "note": "non-temporal 16-byte loads, 4 in flight per thread, 256-thread workgroups"}
+
+
+def bench_probe_bias(args):
+    """The materialised prefill bias of one ModernBERT-shaped full-attention
+    layer ([32, 12, 1024, 1024] fp32, lengths U[64, 1024]) read with no
+    arithmetic in the order the prefill kernels walk it (each wave its 32
+    query rows, advancing along the keys), at several widths per row and
+    iteration (W bytes, G contiguous bytes per row and load)."""
+    import torch
+    lib = _probe_lib()
+    stream = torch.cuda.current_stream().cuda_stream
+    c = modernbert_layers(torch.bfloat16)[0]
+    H, M = 12, c.max_seq_len
+    bias = torch.randn(c.num_seqs, H, M, M, device="cuda")
+    lens = c.context_lens
+    out = torch.empty((M // 128) * H * c.num_seqs * 256, dtype=torch.float32, device="cuda")
+    torch.cuda.synchronize()
+    rows = []
+    for w, g in ((128, 128), (256, 256), (512, 128), (512, 512)):
+        ms = time_steps(lambda: _probe_call(lib.pb_bias(
+            bias.data_ptr(), lens.data_ptr(), c.num_seqs, H, M, w, g, out.data_ptr(), stream)),
+            args.steps, args.warmup)
+        L = c.lens.astype(np.int64)
+        nbytes = int(np.sum(L * ((L + w // 4 - 1) // (w // 4) * (w // 4)))) * 4 * H
+        rows.append({"W_bytes_per_row_per_iteration": w, "G_contiguous_bytes_per_load": g,
+                     "us": ms * 1e3, "GBps": nbytes / (ms * 1e-3) / 1e9, "bytes": nbytes})
+    return {"metric": "probe: prefill bias access pattern", "rows": rows,
+            "note": "one workgroup of 4 waves per (128-query tile, head, sequence); wave w "
+                    "reads rows 32w..32w+31 of its tile, W/32 non-temporal 16-byte loads per "
+                    "lane in flight per iteration"}
+
+
+def bench_probe_gather_t5(args):
+    """The T5-large cross-attention decode's K/V gather without arithmetic
+    (pb_gather, the decode kernel's order and loads), next to the decode call,
+    both as back-to-back calls over rotating copies of the inputs (over 1 GiB)
+    replayed from a HIP graph, as the T5 decode lines time them."""
+    import torch
+    import sliding_window_mask_amd as pa
+    import workloads
+    lib = _probe_lib()
+    dec = pa.lib()
+    case = workloads.t5_large_cross_decode_bf16(device="cuda", bias=None)
+    B, H, D = case.q.shape
+    block_bytes = 16 * D * case.k_cache.element_size()
+    per_copy = sum(t.numel() * t.element_size() for t in (case.q, case.k_cache, case.v_cache))
+    ncopy = max(4, -(-(1 << 30) // per_copy))
+    layers = [(case.q.clone(), case.k_cache.clone(), case.v_cache.clone(),
+               torch.empty_like(case.q)) for _ in range(ncopy)]
+    ws = dec.workspace_for(case.q, case.max_seq_len, case.sliding_window)
+    pout = torch.empty(B * H * 256, dtype=torch.float32, device="cuda")
+    torch.cuda.synchronize()
+
+    def graph_ms(fn):
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            for c in layers:
+                fn(*c)
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for i in range(args.steps):
+                fn(*layers[i % ncopy])
+        return time_steps(g.replay, 1, args.warmup) / args.steps
+
+    def gather(mode):
+        def fn(q, k, v, o):
+            _probe_call(lib.pb_gather(mode, k.data_ptr(), v.data_ptr(),
+                                      case.block_tables.data_ptr(),
+                                      case.context_lens.data_ptr(), B, H, block_bytes,
+                                      case.block_tables.shape[1], pout.data_ptr(),
+                                      torch.cuda.current_stream().cuda_stream))
+        return fn
+    kv = 2 * H * block_bytes * int(np.sum((case.lens + 15) // 16))
+    res = {}
+    for mode, name in ((0, "k_then_v_nontemporal"), (2, "k_and_v_together_nontemporal")):
+        ms = graph_ms(gather(mode))
+        res[name] = {"us": ms * 1e3, "kv_GBps": kv / (ms * 1e-3) / 1e9}
+    msd = graph_ms(lambda q, k, v, o: dec.paged_attn_decode(
+        q, k, v, case.block_tables, case.context_lens, None, case.sliding_window, case.scale,
+        max_seq_len=case.max_seq_len, out=o, workspace=ws))
+    # a contiguous read of the same number of bytes per call, over as many
+    # rotating buffers
+    nbytes = (kv + 15) // 16 * 16
+    bufs = [torch.zeros(nbytes, dtype=torch.uint8, device="cuda") for _ in range(ncopy)]
+    sgrid = 256 * 16
+    sout = torch.empty(sgrid * 256, dtype=torch.float32, device="cuda")
+    layers_bak = layers
+    layers = [(b_, None, None, None) for b_ in bufs]
+
+    def stream_fn(buf, *_):
+        _probe_call(lib.pb_stream(buf.data_ptr(), nbytes, sgrid, sout.data_ptr(),
+                                  torch.cuda.current_stream().cuda_stream))
+    mss = graph_ms(stream_fn)
+    layers = layers_bak
+    return {"metric": "probe: T5-large cross decode K/V gather without arithmetic",
+            "orders": res, "us_decode_call": msd * 1e3,
+            "us_contiguous_read_same_bytes": mss * 1e3,
+            "contiguous_GBps": nbytes / (mss * 1e-3) / 1e9,
+            "decode_kv_GBps": kv / (msd * 1e-3) / 1e9, "kv_bytes": kv, "copies": ncopy,
+            "note": "256 sequences x 16 heads, head_dim 64, bf16, encoder lengths U[128, 512]; "
+                    "graph-replayed back-to-back calls over rotating input copies"}
 
 
 def bench_probe_gather(args):
@@ -1286,6 +1391,10 @@ def main():
         line = bench_probe_stream(args)
     elif args.workload == "probe_gather":
         line = bench_probe_gather(args)
+    elif args.workload == "probe_gather_t5":
+        line = bench_probe_gather_t5(args)
+    elif args.workload == "probe_bias":
+        line = bench_probe_bias(args)
     else:
         raise SystemExit("unknown workload %s" % args.workload)
     print(json.dumps(line), flush=True)

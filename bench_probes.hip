@@ -227,6 +227,44 @@ pb_gather_kernel(const char* k_cache, const char* v_cache, const int32_t* block_
   out[((int64_t)b * heads + h) * kProbeThreads + threadIdx.x] = (float)acc;
 }
 
+// A materialised prefill bias read by (128-query tile, head, sequence)
+// workgroups as the prefill kernels walk it: wave w reads rows 32 w .. +31 of
+// its tile (rows below L only), W bytes of each row per iteration from the
+// first key on, with 16-byte non-temporal loads in which G consecutive bytes
+// of a row are read by G / 16 consecutive lanes; all W / 32 loads of an
+// iteration are in flight together. bias: [seqs, heads, max_len, max_len]
+// fp32; max_len a multiple of W / 4.
+template <int W, int G>
+__global__ void __launch_bounds__(kProbeThreads)
+pb_bias_kernel(const float* bias, const int32_t* lens, int heads, int max_len, float* out) {
+  constexpr int kInst = W / 32;               // 1 KiB loads per wave and iteration
+  constexpr int kLanesPerRow = G / 16;
+  constexpr int kRowsPerInst = 64 / kLanesPerRow;
+  constexpr int kRowBlocks = 32 / kRowsPerInst;
+  const int tile = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  const int L = lens[b];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int row0 = tile * 128 + wave * 32;
+  unsigned acc = 0;
+  if (row0 < L) {
+    const float* base = bias + (((int64_t)b * heads + h) * max_len) * max_len;
+    const int nkeys = (L + W / 4 - 1) / (W / 4) * (W / 4);
+    for (int k0 = 0; k0 < nkeys; k0 += W / 4) {
+      uint4 x[kInst];
+#pragma unroll
+      for (int n = 0; n < kInst; ++n) {
+        const int row = row0 + (n % kRowBlocks) * kRowsPerInst + lane / kLanesPerRow;
+        const int col = k0 + ((n / kRowBlocks) * G + (lane % kLanesPerRow) * 16) / 4;
+        x[n] = row < L ? nt_load16(reinterpret_cast<const char*>(base + (int64_t)row * max_len + col))
+                       : make_uint4(0u, 0u, 0u, 0u);
+      }
+#pragma unroll
+      for (int n = 0; n < kInst; ++n) acc ^= x[n].x ^ x[n].y ^ x[n].z ^ x[n].w;
+    }
+  }
+  out[(((int64_t)b * heads + h) * gridDim.x + tile) * kProbeThreads + threadIdx.x] = (float)acc;
+}
+
 template <int KIND, int CH, int NEXP>
 int launch_mfma(float* out, int grid, int iters, hipStream_t s) {
   hipLaunchKernelGGL((pb_mfma_kernel<KIND, CH, NEXP>), dim3(grid), dim3(kProbeThreads), 0, s,
@@ -293,6 +331,31 @@ int pb_gather(int mode, const void* k_cache, const void* v_cache, const int32_t*
   else if (mode == 2)
     hipLaunchKernelGGL(pb_gather_kernel<2>, grid, dim3(kProbeThreads), 0, s, k, v, block_tables,
                        context_lens, heads, block_bytes, max_blocks, out);
+  else
+    return -1;
+  return (int)hipGetLastError();
+}
+
+// bias [seqs, heads, max_len, max_len] fp32, lens [seqs]; (w, g) one of
+// (128, 128), (512, 128), (512, 512), (256, 256); out: ceil(max_len / 128) *
+// heads * seqs * 256 floats.
+int pb_bias(const float* bias, const int32_t* lens, int seqs, int heads, int max_len, int w,
+            int g, float* out, void* stream) {
+  if (max_len % 128 != 0) return -1;
+  const dim3 grid(max_len / 128, heads, seqs);
+  hipStream_t s = (hipStream_t)stream;
+  if (w == 128 && g == 128)
+    hipLaunchKernelGGL((pb_bias_kernel<128, 128>), grid, dim3(kProbeThreads), 0, s, bias, lens,
+                       heads, max_len, out);
+  else if (w == 512 && g == 128)
+    hipLaunchKernelGGL((pb_bias_kernel<512, 128>), grid, dim3(kProbeThreads), 0, s, bias, lens,
+                       heads, max_len, out);
+  else if (w == 512 && g == 512)
+    hipLaunchKernelGGL((pb_bias_kernel<512, 512>), grid, dim3(kProbeThreads), 0, s, bias, lens,
+                       heads, max_len, out);
+  else if (w == 256 && g == 256)
+    hipLaunchKernelGGL((pb_bias_kernel<256, 256>), grid, dim3(kProbeThreads), 0, s, bias, lens,
+                       heads, max_len, out);
   else
     return -1;
   return (int)hipGetLastError();

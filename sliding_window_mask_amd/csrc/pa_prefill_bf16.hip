@@ -701,19 +701,41 @@ pa_prefill_bf16_32(PrefillArgs a) {
   // a lane's bias entries of a tile are 4 runs of 4 contiguous keys: 16-byte
   // loads on tiles that lie wholly inside the sequence, if every lane's row
   // is 16-byte aligned (uniform)
-  const bool bias_vec =
-      BIAS == 1 &&
-      __builtin_amdgcn_ballot_w64((reinterpret_cast<uintptr_t>(bias_row) & 15) != 0) == 0;
   const bf16x2_t one2 = __builtin_bit_cast(bf16x2_t, 0x3f803f80u);
-  // bias entries of the next tile lying wholly inside the sequence (16-byte
-  // loads), requested one tile ahead
+  // Bias entries of tiles lying wholly inside the sequence are read with
+  // whole 128-byte row segments per 8 lanes: load q of a tile takes rows
+  // lane/8 + 8q of the wave's 32 (a row past the last query repeats the
+  // last query's row), 16 bytes per lane, one tile ahead; the wave then
+  // passes them through its own LDS block (rows padded to 36 floats, so the
+  // reads of 16 lanes cover all banks once) to the lanes that own the rows.
+  // Reading a lane's own 4 runs of 4 entries directly would touch 32 rows in
+  // every load instruction, 32 bytes each. The block is the wave's alone and
+  // its LDS operations complete in order, so no barrier is involved.
+  constexpr int kBRow = 36;
+  __shared__ __attribute__((aligned(16))) float b_lds[BIAS == 1 ? (kQT32 / 32) * 32 * kBRow : 4];
+  float* bw = &b_lds[BIAS == 1 ? wave * 32 * kBRow : 0];
+  const float* bbase = nullptr;   // the bias row of the wave's first query
+  int boff[4] = {0, 0, 0, 0};     // element offsets of the lane's 4 load rows
+  bool bias_vec = false;          // uniform: every row 16-byte aligned
+  if (BIAS == 1 && wave_active) {
+    const int64_t pitch = a.bias_start ? L : a.max_seq_len;
+    bbase = a.bias_start
+                ? a.attn_bias + a.bias_start[b] + ((int64_t)h * nq + w_first) * L
+                : a.attn_bias +
+                      (((int64_t)b * H + h) * a.max_seq_len + pos0 + w_first) * a.max_seq_len;
+    bias_vec = (reinterpret_cast<uintptr_t>(bbase) & 15) == 0 && (pitch & 3) == 0;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int rr = min(w_first + (lane >> 3) + 8 * q, nq - 1) - w_first;
+      boff[q] = (int)(rr * pitch) + 4 * (lane & 7);
+    }
+  }
   float4_t bnext[4];
 #pragma unroll
-  for (int u = 0; u < 4; ++u) bnext[u] = float4_t{0, 0, 0, 0};
-  if (BIAS == 1 && bias_vec && wave_active && kKT <= L) {
+  for (int q = 0; q < 4; ++q) bnext[q] = float4_t{0, 0, 0, 0};
+  if (BIAS == 1 && bias_vec && kKT <= L) {
 #pragma unroll
-    for (int u = 0; u < 4; ++u)
-      bnext[u] = *reinterpret_cast<const float4_t*>(bias_row + 8 * u + 4 * hh);
+    for (int q = 0; q < 4; ++q) bnext[q] = *reinterpret_cast<const float4_t*>(bbase + boff[q]);
   }
 
   if (ntiles > 0) {
@@ -749,15 +771,21 @@ pa_prefill_bf16_32(PrefillArgs a) {
       if constexpr (BIAS == 1) {
         if (bias_whole) {
 #pragma unroll
-          for (int u = 0; u < 4; ++u)
+          for (int q = 0; q < 4; ++q)
+            *reinterpret_cast<float4_t*>(&bw[((lane >> 3) + 8 * q) * kBRow + 4 * (lane & 7)]) =
+                bnext[q];
 #pragma unroll
-            for (int r = 0; r < 4; ++r) s[4 * u + r] = fmaf(bnext[u][r], bmul, s[4 * u + r]);
+          for (int u = 0; u < 4; ++u) {
+            const float4_t bv =
+                *reinterpret_cast<const float4_t*>(&bw[j * kBRow + 8 * u + 4 * hh]);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) s[4 * u + r] = fmaf(bv[r], bmul, s[4 * u + r]);
+          }
           // the next tile's entries, a whole tile of work ahead of their use
-          if (bias_vec && c0 + 2 * kKT <= L) {
+          if (c0 + 2 * kKT <= L) {
 #pragma unroll
-            for (int u = 0; u < 4; ++u)
-              bnext[u] =
-                  *reinterpret_cast<const float4_t*>(bias_row + c0 + kKT + 8 * u + 4 * hh);
+            for (int q = 0; q < 4; ++q)
+              bnext[q] = *reinterpret_cast<const float4_t*>(bbase + boff[q] + c0 + kKT);
           }
         } else {
 #pragma unroll
@@ -866,6 +894,371 @@ pa_prefill_bf16_32(PrefillArgs a) {
   }
 }
 
+// ---------------------------------------------------------------------------
+// The same launches at head_dim 64, software-pipelined. Each wave's tile
+// work is a chain (S^T products, then the softmax, then the P.V products),
+// and in the kernel above the matrix cores sit idle while a wave computes its
+// weights unless another resident wave happens to be multiplying. Here each
+// step issues the S^T products of the next tile right after the current
+// tile's row maximum, so they run on the matrix cores while the same wave
+// computes the current weights; then the P.V products of the current tile.
+// K of a tile is therefore staged two steps before its P.V step and V one
+// step before, still with one barrier per step: entering step k, S_k is in
+// registers, K of tile k+1 and V of tile k are in LDS, and the loads of K of
+// tile k+2 and V of tile k+1 are in flight; step k stores those into the K
+// buffer that tile k left and the V buffer that tile k-1 left, then issues
+// the loads of V of tile k+2 and K of tile k+3. Operand layouts, softmax and
+// rounding are those of the kernel above, so the two give identical results.
+#ifndef PA_PREFILL_BF16_PIPE
+#define PA_PREFILL_BF16_PIPE 0
+#endif
+
+template <int D, int BIAS>
+__global__ void __launch_bounds__(kThreads32, 4)
+pa_prefill_bf16_32p(PrefillArgs a) {
+  constexpr int kThreads = kThreads32;
+  constexpr int kKRow = D + 8;                 // K row stride in LDS (bf16)
+  constexpr int kVRow = D + 32;                // V row stride in LDS (bf16)
+  constexpr int kSteps = D / 16;               // 16-dim steps of S^T
+  constexpr int kNDT = D / 32;                 // 32-dim output slices
+  constexpr int kKLoads = kKT * D / 8 / kThreads;        // 16-byte K loads per thread
+  static_assert(kKLoads >= 1, "tile shape");
+
+  const int H = a.num_heads;
+  int b, h, tile, L, q0, nq;
+  if (!prefill_work_of(blockIdx.x, a, b, h, tile, L, q0, nq)) return;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform
+  const int j = lane & 31;
+  const int hh = lane >> 5;
+  const int jj = lane & 15;
+  const int g1 = (lane >> 4) & 1;
+
+  const int t_first = tile * kQT32;
+  if (t_first >= nq) return;
+  const int pos0 = L - nq;
+  const int w_first = t_first + wave * 32;
+  const bool wave_active = w_first < nq;   // uniform over the wave
+
+  const float cs = a.scale_log2 == 0.0f ? 1.0f : fabsf(a.scale_log2);
+  const float bmul = a.scale_log2 == 0.0f ? 0.0f : (a.scale_log2 < 0.0f ? -1.0f : 1.0f);
+
+  const int t_row = w_first + j;
+  const bool row_ok = t_row < nq;
+  const int p_row = pos0 + t_row;
+  const int dq = p_row - 4 * hh;
+  const int dlo = p_row - L;
+
+  bf16x8_t qv[kSteps];
+  {
+    const int tq = row_ok ? t_row : t_first;
+    const bool qzero = !row_ok || bmul == 0.0f;
+    const uint32_t qsign = bmul < 0.0f ? 0x80008000u : 0u;
+    const uint4* qrow = reinterpret_cast<const uint4*>(
+        static_cast<const uint16_t*>(a.q) + ((int64_t)(q0 + tq) * H + h) * D + 8 * hh);
+#pragma unroll
+    for (int st = 0; st < kSteps; ++st) {
+      uint4 v = qrow[2 * st];
+      v = qzero ? make_uint4(0u, 0u, 0u, 0u)
+                : make_uint4(v.x ^ qsign, v.y ^ qsign, v.z ^ qsign, v.w ^ qsign);
+      qv[st] = __builtin_bit_cast(bf16x8_t, v);
+    }
+  }
+
+  __shared__ __attribute__((aligned(16))) uint16_t k_lds[2][kKT * kKRow];
+  __shared__ __attribute__((aligned(16))) uint16_t v_lds[2][kKT * kVRow];
+  __shared__ float rel_lds[BIAS == 2 ? 2 * kMaxRelDistance + 1 : 1];
+  const int rel_md = BIAS == 2 ? a.rel.max_distance : 0;
+  if constexpr (BIAS == 2) {
+    const float* head_row = a.rel.table + (int64_t)h * a.rel.num_buckets;
+    for (int i = tid; i <= 2 * rel_md; i += kThreads)
+      rel_lds[i] = bmul == 0.0f ? 0.0f : rel_bias(i - rel_md, a.rel, head_row) * bmul;
+  }
+
+  const uint16_t* kc = static_cast<const uint16_t*>(a.k_cache);
+  const uint16_t* vc = static_cast<const uint16_t*>(a.v_cache);
+  const int32_t* table = a.block_tables + (int64_t)b * a.max_blocks;
+  const int ntiles = (L + kKT - 1) / kKT;
+  const int nblk_seq = (L + kBlockSize - 1) / kBlockSize;
+
+  // staging as in the kernel above; K and V of a tile are loaded at
+  // different steps, so each has its own block-table entries
+  int tbk[2], tbv[2];
+  auto load_table = [&](int (&tb)[2], int tk) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int blk = tk * (kKT / kBlockSize) + i;
+      tb[i] = blk < nblk_seq ? table[blk] : 0;
+    }
+  };
+  typedef uint32_t st_t __attribute__((ext_vector_type(4 * kKLoads)));
+  st_t kst, vst;
+  auto fetch = [&](st_t& dst, const uint16_t* src, const int (&tb)[2]) {
+#pragma unroll
+    for (int i = 0; i < kKLoads; ++i) {
+      const int e = i * kThreads + tid;
+      const int r = e / (D / 8), col = (e % (D / 8)) * 8;
+      const int sel = (i * kThreads + wave * 64) / (D / 8) / kBlockSize;
+      const int64_t blk = ((int64_t)tb[sel] * H + h) * (kBlockSize * D);
+      const uint32_t off = (uint32_t)((r % kBlockSize) * D + col);
+      const uint4 x = *reinterpret_cast<const uint4*>(src + blk + off);
+      dst[4 * i] = x.x;
+      dst[4 * i + 1] = x.y;
+      dst[4 * i + 2] = x.z;
+      dst[4 * i + 3] = x.w;
+    }
+  };
+  auto stash_k = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < kKLoads; ++i) {
+      const int e = i * kThreads + tid;
+      const int r = e / (D / 8), col = (e % (D / 8)) * 8;
+      *reinterpret_cast<uint4*>(&k_lds[buf][r * kKRow + col]) =
+          make_uint4(kst[4 * i], kst[4 * i + 1], kst[4 * i + 2], kst[4 * i + 3]);
+    }
+  };
+  // V rows at or past L come from an in-pool block and are zeroed here, a
+  // step after their loads were issued
+  auto stash_v = [&](int buf, int tk) {
+    const int base = tk * kKT;
+#pragma unroll
+    for (int i = 0; i < kKLoads; ++i) {
+      const int e = i * kThreads + tid;
+      const int r = e / (D / 8), col = (e % (D / 8)) * 8;
+      uint4 x = make_uint4(vst[4 * i], vst[4 * i + 1], vst[4 * i + 2], vst[4 * i + 3]);
+      if (base + kKT > L && base + r >= L) x = make_uint4(0u, 0u, 0u, 0u);
+      *reinterpret_cast<uint4*>(&v_lds[buf][r * kVRow + col]) = x;
+    }
+  };
+
+  auto qk = [&](auto kb_c, float16_t& s) {
+    constexpr int kb = decltype(kb_c)::value;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) s[i] = 0.0f;
+#pragma unroll
+    for (int st = 0; st < kSteps; ++st) {
+      const uint4 kv = *reinterpret_cast<const uint4*>(&k_lds[kb][j * kKRow + 16 * st + 8 * hh]);
+      s = mfma32_bf16(__builtin_bit_cast(bf16x8_t, kv), qv[st], s);
+    }
+  };
+
+  float16_t acc[kNDT];
+#pragma unroll
+  for (int dt = 0; dt < kNDT; ++dt)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) acc[dt][i] = 0.0f;
+  float lsum = 0.0f;
+  float m_ref = -INFINITY, neg_m = 0.0f;
+  const float* bias_row = nullptr;
+  if (BIAS == 1) {
+    const int tb_row = row_ok ? t_row : t_first;
+    bias_row = a.bias_start
+                   ? a.attn_bias + a.bias_start[b] + ((int64_t)h * nq + tb_row) * L
+                   : a.attn_bias +
+                         (((int64_t)b * H + h) * a.max_seq_len + pos0 + tb_row) * a.max_seq_len;
+  }
+  const bool bias_vec =
+      BIAS == 1 &&
+      __builtin_amdgcn_ballot_w64((reinterpret_cast<uintptr_t>(bias_row) & 15) != 0) == 0;
+  const bf16x2_t one2 = __builtin_bit_cast(bf16x2_t, 0x3f803f80u);
+  float4_t bnext[4];
+#pragma unroll
+  for (int u = 0; u < 4; ++u) bnext[u] = float4_t{0, 0, 0, 0};
+  if (BIAS == 1 && bias_vec && wave_active && kKT <= L) {
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+      bnext[u] = *reinterpret_cast<const float4_t*>(bias_row + 8 * u + 4 * hh);
+  }
+
+  // start-up: K and V of tile 0 and K of tile 1 to LDS, the S^T products of
+  // tile 0, then the loads of V of tile 1 and K of tile 2 in flight
+  float16_t s_cur;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) s_cur[i] = 0.0f;
+  if (ntiles > 0) {
+    int tb1[2] = {0, 0};
+    load_table(tbk, 0);
+    if (ntiles > 1) load_table(tb1, 1);
+    fetch(kst, kc, tbk);
+    fetch(vst, vc, tbk);
+    st_t k1 = kst;
+    if (ntiles > 1) fetch(k1, kc, tb1);
+    stash_k(0);
+    stash_v(0, 0);
+    if (ntiles > 1) {
+      kst = k1;
+      stash_k(1);
+    }
+    tbk[0] = tb1[0];
+    tbk[1] = tb1[1];
+  }
+  __syncthreads();
+  // entering step k, tbv holds the table entries of tile k+2 and tbk those
+  // of tile k+3
+  if (ntiles > 0) {
+    if (wave_active) qk(IntC<0>{}, s_cur);
+    if (ntiles > 1) {
+      tbv[0] = tbk[0];
+      tbv[1] = tbk[1];   // tile 1
+      fetch(vst, vc, tbv);
+      if (ntiles > 2) {
+        load_table(tbk, 2);
+        fetch(kst, kc, tbk);
+        tbv[0] = tbk[0];
+        tbv[1] = tbk[1];   // tile 2
+      }
+      if (ntiles > 3) load_table(tbk, 3);
+    }
+  }
+  __syncthreads();   // every wave has read K of tile 0 before tile 2 replaces it
+
+  auto tile_step = [&](int tk, auto buf_c, auto next_c) {
+    constexpr int buf = decltype(buf_c)::value;   // tk & 1
+    constexpr bool NEXT = decltype(next_c)::value;
+    const int c0 = tk * kKT;
+    if (wave_active) {
+      // ---- bias (unscaled scores) and the tail mask, as above ----
+      if constexpr (BIAS == 1) {
+        if (bias_vec && c0 + kKT <= L) {
+#pragma unroll
+          for (int u = 0; u < 4; ++u)
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+              s_cur[4 * u + r] = fmaf(bnext[u][r], bmul, s_cur[4 * u + r]);
+          if (c0 + 2 * kKT <= L) {
+#pragma unroll
+            for (int u = 0; u < 4; ++u)
+              bnext[u] =
+                  *reinterpret_cast<const float4_t*>(bias_row + c0 + kKT + 8 * u + 4 * hh);
+          }
+        } else {
+#pragma unroll
+          for (int u = 0; u < 4; ++u)
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+              s_cur[4 * u + r] =
+                  fmaf(bias_row[min(c0 + 8 * u + 4 * hh + r, L - 1)], bmul, s_cur[4 * u + r]);
+        }
+      }
+      if constexpr (BIAS == 2) {
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const int j0 = c0 + 8 * u + 4 * hh;
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            s_cur[4 * u + r] += rel_lds[min(max(j0 + r - p_row, -rel_md), rel_md) + rel_md];
+        }
+      }
+      if (c0 + kKT > L) {   // uniform: only the last tile
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            s_cur[4 * u + r] = dq - c0 - 8 * u - r > dlo ? s_cur[4 * u + r] : -INFINITY;
+      }
+      // ---- row maximum and the lazily moved reference (base 2) ----
+      float mt = s_cur[0];
+#pragma unroll
+      for (int i = 1; i < 16; ++i) mt = vmax(mt, s_cur[i]);
+      {
+        const auto x32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(mt),
+                                                          __float_as_uint(mt), false, false);
+        mt = vmax(__uint_as_float(x32[0]), __uint_as_float(x32[1])) * cs;
+      }
+      const bool move = mt > m_ref + 8.0f;
+      if (__builtin_amdgcn_ballot_w64(move) != 0) {
+        const float alpha = move ? __builtin_amdgcn_exp2f(m_ref - mt) : 1.0f;
+        m_ref = move ? mt : m_ref;
+        neg_m = move ? -mt : neg_m;
+        lsum *= alpha;
+#pragma unroll
+        for (int dt = 0; dt < kNDT; ++dt) acc[dt] *= alpha;
+      }
+      // ---- the next tile's products, independent of the weights below ----
+      float16_t s_next;
+      if constexpr (NEXT) qk(IntC<buf ^ 1>{}, s_next);
+      bf16x8_t pw[2];
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          pw[ks][e] = (__bf16)__builtin_amdgcn_exp2f(fmaf(s_cur[8 * ks + e], cs, neg_m));
+        const uint4 pu = __builtin_bit_cast(uint4, pw[ks]);
+        lsum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, pu.x), one2, lsum,
+                                               false);
+        lsum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, pu.y), one2, lsum,
+                                               false);
+        lsum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, pu.z), one2, lsum,
+                                               false);
+        lsum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, pu.w), one2, lsum,
+                                               false);
+      }
+      // ---- O^T += V^T P^T over the tile's two 16-key steps ----
+      typedef __attribute__((address_space(3))) i16x4_t lds_i16x4_t;
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+#pragma unroll
+        for (int dt = 0; dt < kNDT; ++dt) {
+          const uint16_t* p = &v_lds[buf][(16 * ks + 4 * hh + (jj >> 2)) * kVRow + 32 * dt +
+                                          16 * g1 + 4 * (jj & 3)];
+          const uint2 lo = __builtin_bit_cast(
+              uint2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)p));
+          const uint2 hi = __builtin_bit_cast(
+              uint2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(p + 8 * kVRow)));
+          acc[dt] = mfma32_bf16(__builtin_bit_cast(bf16x8_t, make_uint4(lo.x, lo.y, hi.x, hi.y)),
+                                pw[ks], acc[dt]);
+        }
+      }
+      if constexpr (NEXT) s_cur = s_next;
+    }
+    if constexpr (NEXT) {
+      if (tk + 2 < ntiles) stash_k(buf);
+      stash_v(buf ^ 1, tk + 1);
+      if (tk + 2 < ntiles) {
+        fetch(vst, vc, tbv);   // V of tile k+2
+        if (tk + 3 < ntiles) {
+          fetch(kst, kc, tbk);   // K of tile k+3
+          tbv[0] = tbk[0];
+          tbv[1] = tbk[1];
+          if (tk + 4 < ntiles) load_table(tbk, tk + 4);
+        }
+      }
+      __syncthreads();
+    }
+  };
+  int tk = 0;
+  for (; tk + 2 < ntiles; tk += 2) {
+    tile_step(tk, IntC<0>{}, IntC<true>{});
+    tile_step(tk + 1, IntC<1>{}, IntC<true>{});
+  }
+  if (tk + 1 < ntiles) {
+    tile_step(tk, IntC<0>{}, IntC<true>{});
+    tile_step(tk + 1, IntC<1>{}, IntC<false>{});
+  } else if (tk < ntiles) {
+    tile_step(tk, IntC<0>{}, IntC<false>{});
+  }
+
+  // ---- epilogue: out = O / l, rounded to bf16 (the swap runs in every lane) ----
+  const auto xl = __builtin_amdgcn_permlane32_swap(__float_as_uint(lsum), __float_as_uint(lsum),
+                                                   false, false);
+  const float l_tot = __uint_as_float(xl[0]) + __uint_as_float(xl[1]);
+  if (!row_ok) return;
+  const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
+  uint16_t* orow = static_cast<uint16_t*>(a.out) + ((int64_t)(q0 + t_row) * H + h) * D;
+#pragma unroll
+  for (int dt = 0; dt < kNDT; ++dt) {
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
+      bf16x4_t o = {(__bf16)(acc[dt][4 * u] * inv), (__bf16)(acc[dt][4 * u + 1] * inv),
+                    (__bf16)(acc[dt][4 * u + 2] * inv), (__bf16)(acc[dt][4 * u + 3] * inv)};
+      *reinterpret_cast<bf16x4_t*>(orow + 32 * dt + 8 * u + 4 * hh) = o;
+    }
+  }
+}
+
 // Bidirectional launches without a window or chunks take the
 // 32-query-per-wave kernel; causal, windowed and chunked ones the
 // 16-query-per-wave kernel.
@@ -881,7 +1274,10 @@ void launch_bias(const PrefillArgs& a, dim3 grid, hipStream_t stream) {
   } else if (banded) {
     hipLaunchKernelGGL((pa_prefill_bf16<D, BIAS, false, true>), grid, block, 0, stream, a);
   } else {
-    hipLaunchKernelGGL((pa_prefill_bf16_32<D, BIAS>), grid, dim3(kThreads32), 0, stream, a);
+    if constexpr (PA_PREFILL_BF16_PIPE && D == 64 && BIAS == 0)
+      hipLaunchKernelGGL((pa_prefill_bf16_32p<64, 0>), grid, dim3(kThreads32), 0, stream, a);
+    else
+      hipLaunchKernelGGL((pa_prefill_bf16_32<D, BIAS>), grid, dim3(kThreads32), 0, stream, a);
   }
 }
 
