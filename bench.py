@@ -31,7 +31,7 @@ Prints ONE JSON line. Options:
                   over input copies > 1 GiB) | kv_write_modernbert_f32 | copy_probe (a plain
                   device copy of known size, for calibrating the rocprofv3 byte counters) |
                   prefill_window_sweep | probe_mfma | probe_lds | probe_stream |
-                  probe_gather | probe_gather_t5 | probe_bias (hardware rates from
+                  probe_gather | probe_gather_t5 | probe_bias | probe_mix (hardware rates from
                   bench_probes.hip: matrix instructions, LDS reads, a streaming read, the
                   decode's K/V gather without arithmetic)
   --no-cpu-baseline   skip the oracle timing
@@ -870,7 +870,8 @@ def _probe_lib():
     lib.pb_stream.argtypes = [P, I64, I, P, P]
     lib.pb_gather.argtypes = [I, P, P, P, P, I, I, I, I, P, P]
     lib.pb_bias.argtypes = [P, P, I, I, I, I, I, P, P]
-    for f in (lib.pb_mfma, lib.pb_lds, lib.pb_stream, lib.pb_gather, lib.pb_bias):
+    lib.pb_mix.argtypes = [I, I, I, P, P]
+    for f in (lib.pb_mfma, lib.pb_lds, lib.pb_stream, lib.pb_gather, lib.pb_bias, lib.pb_mix):
         f.restype = I
     return lib
 
@@ -908,6 +909,28 @@ def bench_probe_mfma(args):
     return {"metric": "probe: sustained matrix-instruction rates", "rows": rows,
             "note": "independent accumulator chains per wave, registers only; grid = 256 "
                     "CUs x waves_per_simd 4-wave workgroups, %d iterations" % iters}
+
+
+def bench_probe_mix(args):
+    """Whether matrix-core work of some waves overlaps vector work of other
+    waves on the same SIMD: 8-wave workgroups whose waves 0-3 run MFMA
+    chains and waves 4-7 an exp/fma loop, timed alone and together."""
+    import torch
+    lib = _probe_lib()
+    stream = torch.cuda.current_stream().cuda_stream
+    rows = []
+    for wgs in (1, 2):
+        grid = 256 * wgs
+        out = torch.empty(grid * 512, dtype=torch.float32, device="cuda")
+        t = {}
+        for mode, name in ((0, "mfma_waves_only"), (1, "valu_waves_only"), (2, "both")):
+            t[name] = time_steps(lambda: _probe_call(lib.pb_mix(mode, grid, 4000, out.data_ptr(),
+                                                               stream)),
+                                 args.steps, args.warmup) * 1e3
+        rows.append({"workgroups_per_cu": wgs, **{k + "_us": v for k, v in t.items()},
+                     "both_over_max": t["both"] / max(t["mfma_waves_only"], t["valu_waves_only"]),
+                     "both_over_sum": t["both"] / (t["mfma_waves_only"] + t["valu_waves_only"])})
+    return {"metric": "probe: matrix/vector overlap across waves of one SIMD", "rows": rows}
 
 
 def bench_probe_lds(args):
@@ -1385,6 +1408,8 @@ def main():
         line = bench_prefill_window_sweep(args)
     elif args.workload == "probe_mfma":
         line = bench_probe_mfma(args)
+    elif args.workload == "probe_mix":
+        line = bench_probe_mix(args)
     elif args.workload == "probe_lds":
         line = bench_probe_lds(args)
     elif args.workload == "probe_stream":

@@ -14,6 +14,10 @@
 //                  bytes [16 l, 16 l + 16) of every 1 KiB slice, K pass then V
 //                  pass, non-temporal loads) with no arithmetic, and two
 //                  variants of it (ordinary loads; K and V read together)
+//   pb_bias        a materialised prefill bias read in the order the prefill
+//                  kernels walk it, with no arithmetic
+//   pb_mix         waves running only matrix instructions beside waves
+//                  running only vector instructions on the same SIMDs
 //
 // Every probe writes one 32-bit value per thread of its grid to `out`
 // (vector stores), so the caller sizes `out` as grid * block values; all
@@ -265,6 +269,55 @@ pb_bias_kernel(const float* bias, const int32_t* lens, int heads, int max_len, f
   out[(((int64_t)b * heads + h) * gridDim.x + tile) * kProbeThreads + threadIdx.x] = (float)acc;
 }
 
+// Whether matrix and vector work of different waves on one SIMD overlap:
+// 8-wave workgroups (waves w and w + 4 share a SIMD); waves 0-3 run four
+// independent v_mfma_f32_32x32x16_bf16 chains, waves 4-7 a vector loop of
+// 8 v_exp_f32 and 16 v_fma_f32 per iteration, both `iters` iterations.
+// MODE 0: only the matrix waves work, 1: only the vector waves, 2: both.
+template <int MODE>
+__global__ void __launch_bounds__(512) pb_mix_kernel(float* out, int iters, float seed) {
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6;
+  float r = 0.0f;
+  if (wave < 4 && MODE != 1) {
+    bf16x8_t a, b;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      a[i] = (__bf16)(seed * (float)(tid + i));
+      b[i] = (__bf16)(seed * (float)(i - tid));
+    }
+    f16_t acc[4];
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) acc[c][i] = 0.0f;
+    for (int it = 0; it < iters; ++it) {
+#pragma unroll
+      for (int c = 0; c < 4; ++c) acc[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc[c], 0, 0, 0);
+    }
+#pragma unroll
+    for (int c = 0; c < 4; ++c) r += acc[c][0] + acc[c][15];
+  }
+  if (wave >= 4 && MODE != 0) {
+    float e[8], f[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      e[i] = seed * (float)(tid + i) * 1e-3f;
+      f[i] = seed * (float)(tid - i);
+    }
+    for (int it = 0; it < iters; ++it) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        e[i] = __builtin_amdgcn_exp2f(e[i]) * -0.5f;
+        f[i] = fmaf(f[i], 0.999f, e[i]);
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) r += e[i] + f[i];
+  }
+  out[(int64_t)blockIdx.x * 512 + tid] = r;
+}
+
 template <int KIND, int CH, int NEXP>
 int launch_mfma(float* out, int grid, int iters, hipStream_t s) {
   hipLaunchKernelGGL((pb_mfma_kernel<KIND, CH, NEXP>), dim3(grid), dim3(kProbeThreads), 0, s,
@@ -356,6 +409,20 @@ int pb_bias(const float* bias, const int32_t* lens, int seqs, int heads, int max
   else if (w == 256 && g == 256)
     hipLaunchKernelGGL((pb_bias_kernel<256, 256>), grid, dim3(kProbeThreads), 0, s, bias, lens,
                        heads, max_len, out);
+  else
+    return -1;
+  return (int)hipGetLastError();
+}
+
+// mode 0, 1 or 2 as for pb_mix_kernel; out: grid * 512 floats.
+int pb_mix(int mode, int grid, int iters, float* out, void* stream) {
+  hipStream_t s = (hipStream_t)stream;
+  if (mode == 0)
+    hipLaunchKernelGGL(pb_mix_kernel<0>, dim3(grid), dim3(512), 0, s, out, iters, 0.01f);
+  else if (mode == 1)
+    hipLaunchKernelGGL(pb_mix_kernel<1>, dim3(grid), dim3(512), 0, s, out, iters, 0.01f);
+  else if (mode == 2)
+    hipLaunchKernelGGL(pb_mix_kernel<2>, dim3(grid), dim3(512), 0, s, out, iters, 0.01f);
   else
     return -1;
   return (int)hipGetLastError();
