@@ -198,6 +198,11 @@ pa_status_t paged_attn_decode_noalloc(void* out, const void* q, const void* k_ca
  *                   on the bf16 matrix cores with every fp32 operand split
  *                   exactly into three bf16 parts, at 128 on fp32 MFMA)
  *   Other arguments as for paged_attn_decode. No workspace is needed.
+ *   The launch has one workgroup per (sequence, head) and per 64 or 128
+ *   query rows of max_seq_len; those past a sequence's own length only read
+ *   its metadata and exit, so a max_seq_len far above the batch's longest
+ *   sequence costs launch time (e.g. 256 sequences of 128 tokens: 2.6x the
+ *   time with max_seq_len 1024 as with 128).
  *   total_q = 0 computes nothing and returns PA_OK after the scalar checks;
  *   then no device pointer is read and any of them may be NULL (the same
  *   holds for the ragged-bias variant below; the relpos variant still checks
