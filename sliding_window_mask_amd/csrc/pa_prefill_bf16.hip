@@ -723,7 +723,9 @@ pa_prefill_bf16_32(PrefillArgs a) {
                 ? a.attn_bias + a.bias_start[b] + ((int64_t)h * nq + w_first) * L
                 : a.attn_bias +
                       (((int64_t)b * H + h) * a.max_seq_len + pos0 + w_first) * a.max_seq_len;
-    bias_vec = (reinterpret_cast<uintptr_t>(bbase) & 15) == 0 && (pitch & 3) == 0;
+    // (32-bit row offsets: rows of up to 2^26 entries)
+    bias_vec = (reinterpret_cast<uintptr_t>(bbase) & 15) == 0 && (pitch & 3) == 0 &&
+               pitch < (1 << 26);
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       const int rr = min(w_first + (lane >> 3) + 8 * q, nq - 1) - w_first;
