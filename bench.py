@@ -30,6 +30,7 @@ Prints ONE JSON line. Options:
                   t5_small_self_decode_bf16 | t5_large_cross_decode_bf16 (calls rotating
                   over input copies > 1 GiB) | kv_write_modernbert_f32 | copy_probe (a plain
                   device copy of known size, for calibrating the rocprofv3 byte counters) |
+                  prefill_layer (one layer: --layer-dtype, --layer-window) |
                   prefill_window_sweep | probe_mfma | probe_lds | probe_stream |
                   probe_gather | probe_gather_t5 | probe_bias | probe_mix (hardware rates from
                   bench_probes.hip: matrix instructions, LDS reads, a streaming read, the
@@ -76,7 +77,14 @@ KERNEL_SOURCE = {
     "modernbert_prefill_f32": ("pa_prefill.hip", "pa_prefill_f32x3.hip"),
     "modernbert_prefill_bf16": "pa_prefill_bf16.hip",
     "kv_write_modernbert_f32": "pa_cache.hip",
+    "prefill_layer_f32": ("pa_prefill.hip", "pa_prefill_f32x3.hip"),
+    "prefill_layer_bf16": "pa_prefill_bf16.hip",
 }
+
+
+def kernel_source_of(wl):
+    """Kernel sources of a workload; `<workload>_w<W>` names one window of it."""
+    return KERNEL_SOURCE[wl] if wl in KERNEL_SOURCE else KERNEL_SOURCE[wl.rsplit("_w", 1)[0]]
 
 
 def log(msg):
@@ -828,6 +836,30 @@ def bench_configs(args):
     return out
 
 
+def bench_prefill_layer(args):
+    """One ModernBERT-shaped prefill layer (32 sequences, lengths U[64, 1024],
+    12 heads, head_dim 64, no bias) at --layer-window, in --layer-dtype: the
+    unit the counter passes of single layers are taken over."""
+    import torch
+    import sliding_window_mask_amd as pa
+    lib = pa.lib()
+    dn = args.layer_dtype
+    dt = torch.float32 if dn == "f32" else torch.bfloat16
+    c = modernbert_layers(dt)[0]
+    o = torch.empty_like(c.q)
+    torch.cuda.synchronize()
+    w = args.layer_window
+    ms = time_steps(lambda: lib.paged_attn_prefill(
+        c.q, c.k_cache, c.v_cache, c.block_tables, c.context_lens, c.query_start_loc,
+        None, w, False, c.scale, max_seq_len=c.max_seq_len, out=o), args.steps, args.warmup)
+    fl = prefill_flops(c.lens, 12, 64, w)
+    by = prefill_bytes(c.lens, 12, 64, 4 if dn == "f32" else 2)
+    return {"metric": "one prefill layer", "workload": "prefill_layer_" + dn,
+            "sliding_window": w, "steps": args.steps, "warmup": args.warmup,
+            "launches_per_step": 1, "ms_per_step": ms, "us_per_layer": ms * 1e3,
+            "TFLOPs": fl / (ms * 1e-3) / 1e12, "GBps": by / (ms * 1e-3) / 1e9}
+
+
 def bench_prefill_window_sweep(args):
     """One ModernBERT-shaped layer (32 sequences, lengths U[64, 1024], 12
     heads, head_dim 64, no bias) through the product prefill call at a range
@@ -1304,12 +1336,11 @@ def write_counter_summary(a):
     kernels = sorted({by[i]["k"] for i in ids})
     path = os.path.join(PROFILES, "%s_counters.md" % wl)
     old = open(path).read() if os.path.exists(path) and a.append else ""
+    ks = kernel_source_of(wl)
     md = [old.rstrip() + "\n"] if old else ["# Counters: %s (timed steps of --profile-run)" % wl,
                                             "", "%s sha256[:16] = %s" % (
-                                                " + ".join(KERNEL_SOURCE[wl])
-                                                if isinstance(KERNEL_SOURCE[wl], tuple)
-                                                else KERNEL_SOURCE[wl],
-                                                source_sha(KERNEL_SOURCE[wl])), ""]
+                                                " + ".join(ks) if isinstance(ks, tuple) else ks,
+                                                source_sha(ks)), ""]
     md += ["Command: `%s`" % (a.command or "(not recorded)"), "",
            "| kernel | " + " | ".join(names) + " |", "|---|" + "---|" * len(names)]
     med = {}
@@ -1337,6 +1368,21 @@ def write_counter_summary(a):
         if "SQ_WAIT_INST_ANY" in v and "SQ_WAVE_CYCLES" in v:
             row.append(("SQ_WAIT_INST_ANY / SQ_WAVE_CYCLES",
                         "%.2f" % (v["SQ_WAIT_INST_ANY"] / v["SQ_WAVE_CYCLES"])))
+        if "TCC_HIT_sum" in v and "TCC_MISS_sum" in v:
+            row.append(("L2 hit rate (TCC_HIT / (TCC_HIT + TCC_MISS))", "%.1f%%" % (
+                100 * v["TCC_HIT_sum"] / max(1.0, v["TCC_HIT_sum"] + v["TCC_MISS_sum"]))))
+        if "TCP_TCC_READ_REQ_LATENCY_sum" in v and "TCP_TCC_READ_REQ_sum" in v:
+            row.append(("mean L1-to-L2 read latency (cycles per request)", "%.0f" % (
+                v["TCP_TCC_READ_REQ_LATENCY_sum"] / max(1.0, v["TCP_TCC_READ_REQ_sum"]))))
+        if "TA_BUSY_avr" in v:
+            row.append(("TA busy (per TA, share of the launch)",
+                        "%.1f%%" % (100 * v["TA_BUSY_avr"] / cyc)))
+        if "TD_TD_BUSY_sum" in v:
+            row.append(("TD busy (per CU, share of the launch)",
+                        "%.1f%%" % (100 * v["TD_TD_BUSY_sum"] / (cyc * 256))))
+        if "SQ_WAIT_ANY" in v and "SQ_WAVE_CYCLES" in v:
+            row.append(("SQ_WAIT_ANY / SQ_WAVE_CYCLES",
+                        "%.2f" % (v["SQ_WAIT_ANY"] / v["SQ_WAVE_CYCLES"])))
         if "SQ_VALU_MFMA_COEXEC_CYCLES" in v:
             row.append(("VALU-MFMA co-exec (per SIMD per launch cycle)",
                         "%.1f%%" % (100 * v["SQ_VALU_MFMA_COEXEC_CYCLES"] / (cyc * 1024))))
@@ -1357,6 +1403,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="large_biased_decode_bf16")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--layer-dtype", default="f32", choices=("f32", "bf16"))
+    ap.add_argument("--layer-window", type=int, default=-1)
     ap.add_argument("--no-variants", action="store_true")
     ap.add_argument("--no-configs", action="store_true")
     ap.add_argument("--profile-run", action="store_true")
@@ -1404,6 +1452,8 @@ def main():
         line = bench_kv_write(args)
     elif args.workload == "copy_probe":
         line = bench_copy(args)
+    elif args.workload == "prefill_layer":
+        line = bench_prefill_layer(args)
     elif args.workload == "prefill_window_sweep":
         line = bench_prefill_window_sweep(args)
     elif args.workload == "probe_mfma":
