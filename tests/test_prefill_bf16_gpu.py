@@ -127,3 +127,48 @@ def test_prefill_bf16_bidirectional_128_query_tiles(D, bias, partial):
     ref = oracle.prefill_relpos(h.q, h.k_cache, h.v_cache, h.block_tables, h.context_lens,
                                 h.query_start_loc, table, nb, md, 1, -1, 0, h.scale, msl)
     assert_close(out, ref, BF, "bf16 128-query tiles relpos D=%d partial=%s" % (D, partial))
+
+
+def _pack_rows(dense, lens, q_lens):
+    """The ragged layout of a padded prefill bias: per sequence, the rows of
+    its n_q queries over its L keys, heads outermost."""
+    parts, starts, off = [], [], 0
+    for b, (L, nq) in enumerate(zip(lens, q_lens)):
+        L, nq = int(L), int(nq)
+        parts.append(dense[b, :, L - nq:L, :L].reshape(-1))
+        starts.append(off)
+        off += dense.shape[1] * nq * L
+    return torch.cat(parts).contiguous(), torch.tensor(starts, dtype=torch.int64)
+
+
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("partial", [False, True])
+def test_prefill_bf16_bias_read_paths_agree(D, partial):
+    # bidirectional launches without a window read the bias of whole 32-key
+    # tiles as 128-byte row segments passed between lanes through LDS when
+    # every row is 16-byte aligned, and entry by entry otherwise: a padded
+    # bias with row pitch 320 (aligned), the same values with pitch 306 (not
+    # aligned) and the ragged layout (rows of L entries, aligned or not) must
+    # give bit-identical outputs, and match the oracle
+    lens = [31, 32, 64, 100, 129, 256, 257, 300]
+    q_lens = lens if not partial else [1, 32, 33, 99, 2, 200, 129, 300]
+    log("bf16 bias read paths D=%d partial=%s" % (D, partial))
+    case = to_device(workloads.prefill_case(1600 + D + partial, num_seqs=len(lens), num_heads=2,
+                                            head_dim=D, lens=lens, max_seq_len=320, dtype=BF,
+                                            bias="normal", q_lens=q_lens))
+    out_a = gpu_prefill(case)
+    bias_b = case.attn_bias[:, :, :306, :306].contiguous()
+    out_b = pa.paged_attn_prefill(case.q, case.k_cache, case.v_cache, case.block_tables,
+                                  case.context_lens, case.query_start_loc, bias_b, -1, False,
+                                  case.scale, max_seq_len=306)
+    packed, starts = _pack_rows(case.attn_bias.cpu(), case.lens, case.q_lens)
+    out_c = pa.paged_attn_prefill_ragged_bias(case.q, case.k_cache, case.v_cache,
+                                              case.block_tables, case.context_lens,
+                                              case.query_start_loc, packed.to(DEV),
+                                              starts.to(DEV), -1, False, case.scale,
+                                              max_seq_len=320)
+    torch.cuda.synchronize()
+    assert_close(out_a, oracle_prefill(case), BF,
+                 "bf16 bias read paths D=%d partial=%s" % (D, partial))
+    assert torch.equal(out_a.view(torch.int16), out_b.view(torch.int16))
+    assert torch.equal(out_a.view(torch.int16), out_c.view(torch.int16))
