@@ -32,7 +32,7 @@ Prints ONE JSON line. Options:
                   device copy of known size, for calibrating the rocprofv3 byte counters) |
                   prefill_layer (one layer: --layer-dtype, --layer-window) |
                   prefill_window_sweep | probe_mfma | probe_lds | probe_stream |
-                  probe_gather | probe_gather_t5 | probe_bias | probe_mix (hardware rates from
+                  probe_gather | probe_gather_t5 | probe_bias | probe_mix | probe_valu (hardware rates from
                   bench_probes.hip: matrix instructions, LDS reads, a streaming read, the
                   decode's K/V gather without arithmetic)
   --no-cpu-baseline   skip the oracle timing
@@ -903,7 +903,9 @@ def _probe_lib():
     lib.pb_gather.argtypes = [I, P, P, P, P, I, I, I, I, P, P]
     lib.pb_bias.argtypes = [P, P, I, I, I, I, I, P, P]
     lib.pb_mix.argtypes = [I, I, I, P, P]
-    for f in (lib.pb_mfma, lib.pb_lds, lib.pb_stream, lib.pb_gather, lib.pb_bias, lib.pb_mix):
+    lib.pb_valu.argtypes = [I, I, I, P, P]
+    for f in (lib.pb_mfma, lib.pb_lds, lib.pb_stream, lib.pb_gather, lib.pb_bias, lib.pb_mix,
+              lib.pb_valu):
         f.restype = I
     return lib
 
@@ -941,6 +943,25 @@ def bench_probe_mfma(args):
     return {"metric": "probe: sustained matrix-instruction rates", "rows": rows,
             "note": "independent accumulator chains per wave, registers only; grid = 256 "
                     "CUs x waves_per_simd 4-wave workgroups, %d iterations" % iters}
+
+
+def bench_probe_valu(args):
+    """SIMD cycles per wave64 vector instruction: 8 independent chains per
+    thread of v_add_f32, v_fma_f32 or v_exp_f32, 8192 workgroups of 4 waves
+    (cycles at 2.4 GHz over the chip's 1024 SIMDs)."""
+    import torch
+    lib = _probe_lib()
+    stream = torch.cuda.current_stream().cuda_stream
+    grid, iters = 8192, 1024
+    out = torch.empty(grid * 256, dtype=torch.float32, device="cuda")
+    rows = []
+    for kind, name in ((0, "v_add_f32"), (1, "v_fma_f32"), (2, "v_exp_f32")):
+        ms = time_steps(lambda: _probe_call(lib.pb_valu(kind, grid, iters, out.data_ptr(),
+                                                        stream)), args.steps, args.warmup)
+        insts = grid * 4 * iters * 8
+        rows.append({"instruction": name, "us": ms * 1e3,
+                     "simd_cycles_per_wave_instruction": ms * 1e-3 * 2.4e9 * 1024 / insts})
+    return {"metric": "probe: vector instruction rate", "rows": rows}
 
 
 def bench_probe_mix(args):
@@ -1458,6 +1479,8 @@ def main():
         line = bench_prefill_window_sweep(args)
     elif args.workload == "probe_mfma":
         line = bench_probe_mfma(args)
+    elif args.workload == "probe_valu":
+        line = bench_probe_valu(args)
     elif args.workload == "probe_mix":
         line = bench_probe_mix(args)
     elif args.workload == "probe_lds":

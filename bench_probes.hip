@@ -18,6 +18,7 @@
 //                  kernels walk it, with no arithmetic
 //   pb_mix         waves running only matrix instructions beside waves
 //                  running only vector instructions on the same SIMDs
+//   pb_valu        independent chains of one vector instruction
 //
 // Every probe writes one 32-bit value per thread of its grid to `out`
 // (vector stores), so the caller sizes `out` as grid * block values; all
@@ -318,6 +319,28 @@ __global__ void __launch_bounds__(512) pb_mix_kernel(float* out, int iters, floa
   out[(int64_t)blockIdx.x * 512 + tid] = r;
 }
 
+// Vector instruction rate: 8 independent chains per thread of v_add_f32
+// (KIND 0), v_fma_f32 (1) or v_exp_f32 on the negated value (2).
+template <int KIND>
+__global__ void __launch_bounds__(kProbeThreads) pb_valu_kernel(float* out, int iters, float seed) {
+  const int tid = threadIdx.x;
+  float x[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) x[i] = seed * (float)(tid + i);
+  for (int it = 0; it < iters; ++it) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      if constexpr (KIND == 0) x[i] = x[i] + 0.5f;
+      else if constexpr (KIND == 1) x[i] = fmaf(x[i], 0.999f, 0.25f);
+      else x[i] = __builtin_amdgcn_exp2f(-x[i]);
+    }
+  }
+  float r = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) r += x[i];
+  out[(int64_t)blockIdx.x * kProbeThreads + tid] = r;
+}
+
 template <int KIND, int CH, int NEXP>
 int launch_mfma(float* out, int grid, int iters, hipStream_t s) {
   hipLaunchKernelGGL((pb_mfma_kernel<KIND, CH, NEXP>), dim3(grid), dim3(kProbeThreads), 0, s,
@@ -409,6 +432,20 @@ int pb_bias(const float* bias, const int32_t* lens, int seqs, int heads, int max
   else if (w == 256 && g == 256)
     hipLaunchKernelGGL((pb_bias_kernel<256, 256>), grid, dim3(kProbeThreads), 0, s, bias, lens,
                        heads, max_len, out);
+  else
+    return -1;
+  return (int)hipGetLastError();
+}
+
+// kind 0, 1 or 2 as for pb_valu_kernel; out: grid * 256 floats.
+int pb_valu(int kind, int grid, int iters, float* out, void* stream) {
+  hipStream_t s = (hipStream_t)stream;
+  if (kind == 0)
+    hipLaunchKernelGGL(pb_valu_kernel<0>, dim3(grid), dim3(kProbeThreads), 0, s, out, iters, 0.01f);
+  else if (kind == 1)
+    hipLaunchKernelGGL(pb_valu_kernel<1>, dim3(grid), dim3(kProbeThreads), 0, s, out, iters, 0.01f);
+  else if (kind == 2)
+    hipLaunchKernelGGL(pb_valu_kernel<2>, dim3(grid), dim3(kProbeThreads), 0, s, out, iters, 0.01f);
   else
     return -1;
   return (int)hipGetLastError();
