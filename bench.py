@@ -32,7 +32,7 @@ Prints ONE JSON line. Options:
                   device copy of known size, for calibrating the rocprofv3 byte counters) |
                   prefill_layer (one layer: --layer-dtype, --layer-window) |
                   prefill_window_sweep | probe_mfma | probe_lds | probe_stream |
-                  probe_gather | probe_gather_t5 | probe_bias | probe_mix | probe_valu (hardware rates from
+                  probe_gather | probe_gather_t5 | probe_bias | probe_mix | probe_valu | probe_clock (hardware rates from
                   bench_probes.hip: matrix instructions, LDS reads, a streaming read, the
                   decode's K/V gather without arithmetic)
   --no-cpu-baseline   skip the oracle timing
@@ -904,8 +904,9 @@ def _probe_lib():
     lib.pb_bias.argtypes = [P, P, I, I, I, I, I, P, P]
     lib.pb_mix.argtypes = [I, I, I, P, P]
     lib.pb_valu.argtypes = [I, I, I, P, P]
+    lib.pb_clock.argtypes = [I, I, I, P, P]
     for f in (lib.pb_mfma, lib.pb_lds, lib.pb_stream, lib.pb_gather, lib.pb_bias, lib.pb_mix,
-              lib.pb_valu):
+              lib.pb_valu, lib.pb_clock):
         f.restype = I
     return lib
 
@@ -943,6 +944,33 @@ def bench_probe_mfma(args):
     return {"metric": "probe: sustained matrix-instruction rates", "rows": rows,
             "note": "independent accumulator chains per wave, registers only; grid = 256 "
                     "CUs x waves_per_simd 4-wave workgroups, %d iterations" % iters}
+
+
+def bench_probe_clock(args):
+    """The shader clock while every SIMD runs matrix (four 32x32x16 chains per
+    wave) or vector (v_exp_f32 chains) work at 4 waves per SIMD: s_memtime
+    cycles over s_memrealtime's constant 100 MHz ticks, per workgroup."""
+    import torch
+    lib = _probe_lib()
+    stream = torch.cuda.current_stream().cuda_stream
+    grid = 256 * 4
+    out = torch.zeros(2 * grid, dtype=torch.float32, device="cuda")
+    rows = []
+    for kind, name, iters in ((0, "v_mfma_f32_32x32x16_bf16 x4 chains", 20000),
+                              (1, "v_exp_f32 x8 chains", 40000)):
+        ms = time_steps(lambda: _probe_call(lib.pb_clock(kind, grid, iters, out.data_ptr(),
+                                                         stream)), args.steps, args.warmup)
+        v = out.view(grid, 2).double().cpu().numpy()
+        ghz = v[:, 0] / np.maximum(v[:, 1], 1.0) * 0.1
+        row = {"work": name, "us": ms * 1e3, "clock_GHz_median": float(np.median(ghz)),
+               "clock_GHz_min": float(np.min(ghz)), "clock_GHz_max": float(np.max(ghz))}
+        if kind == 0:
+            tf = 2 * 32 * 32 * 16 * 4 * iters * grid * 4 / (ms * 1e-3) / 1e12
+            row["TFLOPs"] = tf
+            row["cycles_per_mfma_at_measured_clock"] = (ms * 1e-3 * row["clock_GHz_median"] * 1e9 /
+                                                        (4 * iters))
+        rows.append(row)
+    return {"metric": "probe: shader clock under load", "rows": rows}
 
 
 def bench_probe_valu(args):
@@ -1479,6 +1507,8 @@ def main():
         line = bench_prefill_window_sweep(args)
     elif args.workload == "probe_mfma":
         line = bench_probe_mfma(args)
+    elif args.workload == "probe_clock":
+        line = bench_probe_clock(args)
     elif args.workload == "probe_valu":
         line = bench_probe_valu(args)
     elif args.workload == "probe_mix":

@@ -19,6 +19,8 @@
 //   pb_mix         waves running only matrix instructions beside waves
 //                  running only vector instructions on the same SIMDs
 //   pb_valu        independent chains of one vector instruction
+//   pb_clock       the shader clock under matrix or vector load (s_memtime
+//                  against the constant s_memrealtime counter)
 //
 // Every probe writes one 32-bit value per thread of its grid to `out`
 // (vector stores), so the caller sizes `out` as grid * block values; all
@@ -319,6 +321,57 @@ __global__ void __launch_bounds__(512) pb_mix_kernel(float* out, int iters, floa
   out[(int64_t)blockIdx.x * 512 + tid] = r;
 }
 
+// Shader clock under load: each workgroup runs four v_mfma_f32_32x32x16_bf16
+// chains per wave (KIND 0) or eight v_exp_f32 chains per thread (KIND 1) for
+// `iters` iterations, and thread 0 writes the shader-clock (s_memtime) and
+// constant 100 MHz (s_memrealtime) counter differences across that work to
+// out[2 blockIdx], out[2 blockIdx + 1] (vector stores).
+template <int KIND>
+__global__ void __launch_bounds__(kProbeThreads) pb_clock_kernel(float* out, int iters, float seed) {
+  const int tid = threadIdx.x;
+  const uint64_t t0 = __builtin_amdgcn_s_memtime();
+  const uint64_t r0 = __builtin_amdgcn_s_memrealtime();
+  float r = 0.0f;
+  if constexpr (KIND == 0) {
+    bf16x8_t a, b;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      a[i] = (__bf16)(seed * (float)(tid + i));
+      b[i] = (__bf16)(seed * (float)(i - tid));
+    }
+    f16_t acc[4];
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) acc[c][i] = 0.0f;
+    for (int it = 0; it < iters; ++it) {
+#pragma unroll
+      for (int c = 0; c < 4; ++c) acc[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc[c], 0, 0, 0);
+    }
+#pragma unroll
+    for (int c = 0; c < 4; ++c) r += acc[c][0];
+  } else {
+    float x[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) x[i] = seed * (float)(tid + i);
+    for (int it = 0; it < iters; ++it) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) x[i] = __builtin_amdgcn_exp2f(-x[i]);
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) r += x[i];
+  }
+  // the counters are read after the work's results exist
+  __builtin_amdgcn_s_waitcnt(0);
+  const float rr = __builtin_amdgcn_readfirstlane(__float_as_uint(r)) == 0x7fc00001u ? 1.0f : 0.0f;
+  const uint64_t t1 = __builtin_amdgcn_s_memtime();
+  const uint64_t r1 = __builtin_amdgcn_s_memrealtime();
+  if (tid == 0) {
+    out[2 * blockIdx.x] = (float)(t1 - t0) + rr;
+    out[2 * blockIdx.x + 1] = (float)(r1 - r0);
+  }
+}
+
 // Vector instruction rate: 8 independent chains per thread of v_add_f32
 // (KIND 0), v_fma_f32 (1) or v_exp_f32 on the negated value (2).
 template <int KIND>
@@ -432,6 +485,18 @@ int pb_bias(const float* bias, const int32_t* lens, int seqs, int heads, int max
   else if (w == 256 && g == 256)
     hipLaunchKernelGGL((pb_bias_kernel<256, 256>), grid, dim3(kProbeThreads), 0, s, bias, lens,
                        heads, max_len, out);
+  else
+    return -1;
+  return (int)hipGetLastError();
+}
+
+// kind 0 or 1 as for pb_clock_kernel; out: 2 * grid floats.
+int pb_clock(int kind, int grid, int iters, float* out, void* stream) {
+  hipStream_t s = (hipStream_t)stream;
+  if (kind == 0)
+    hipLaunchKernelGGL(pb_clock_kernel<0>, dim3(grid), dim3(kProbeThreads), 0, s, out, iters, 0.01f);
+  else if (kind == 1)
+    hipLaunchKernelGGL(pb_clock_kernel<1>, dim3(grid), dim3(kProbeThreads), 0, s, out, iters, 0.01f);
   else
     return -1;
   return (int)hipGetLastError();
