@@ -995,7 +995,8 @@ def bench_probe_valu(args):
 def bench_probe_mix(args):
     """Whether matrix-core work of some waves overlaps vector work of other
     waves on the same SIMD: 8-wave workgroups whose waves 0-3 run MFMA
-    chains and waves 4-7 an exp/fma loop, timed alone and together."""
+    chains (four independent ones, or one dependent chain) and waves 4-7 an
+    exp/fma loop, timed alone and together."""
     import torch
     lib = _probe_lib()
     stream = torch.cuda.current_stream().cuda_stream
@@ -1004,13 +1005,16 @@ def bench_probe_mix(args):
         grid = 256 * wgs
         out = torch.empty(grid * 512, dtype=torch.float32, device="cuda")
         t = {}
-        for mode, name in ((0, "mfma_waves_only"), (1, "valu_waves_only"), (2, "both")):
+        for mode, name in ((0, "mfma_waves_only"), (1, "valu_waves_only"), (2, "both"),
+                           (3, "chained_mfma_waves_only"), (4, "chained_mfma_and_valu")):
             t[name] = time_steps(lambda: _probe_call(lib.pb_mix(mode, grid, 4000, out.data_ptr(),
                                                                stream)),
                                  args.steps, args.warmup) * 1e3
         rows.append({"workgroups_per_cu": wgs, **{k + "_us": v for k, v in t.items()},
                      "both_over_max": t["both"] / max(t["mfma_waves_only"], t["valu_waves_only"]),
-                     "both_over_sum": t["both"] / (t["mfma_waves_only"] + t["valu_waves_only"])})
+                     "both_over_sum": t["both"] / (t["mfma_waves_only"] + t["valu_waves_only"]),
+                     "chained_both_over_sum": t["chained_mfma_and_valu"] / (
+                         t["chained_mfma_waves_only"] + t["valu_waves_only"])})
     return {"metric": "probe: matrix/vector overlap across waves of one SIMD", "rows": rows}
 
 

@@ -276,13 +276,31 @@ pb_bias_kernel(const float* bias, const int32_t* lens, int heads, int max_len, f
 // 8-wave workgroups (waves w and w + 4 share a SIMD); waves 0-3 run four
 // independent v_mfma_f32_32x32x16_bf16 chains, waves 4-7 a vector loop of
 // 8 v_exp_f32 and 16 v_fma_f32 per iteration, both `iters` iterations.
-// MODE 0: only the matrix waves work, 1: only the vector waves, 2: both.
+// MODE 0: only the matrix waves work, 1: only the vector waves, 2: both;
+// MODE 3 and 4 as 0 and 2 with the four products of an iteration chained
+// into one accumulator (each depends on the one before).
 template <int MODE>
 __global__ void __launch_bounds__(512) pb_mix_kernel(float* out, int iters, float seed) {
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
   float r = 0.0f;
-  if (wave < 4 && MODE != 1) {
+  if (wave < 4 && (MODE == 3 || MODE == 4)) {
+    bf16x8_t a, b;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      a[i] = (__bf16)(seed * (float)(tid + i));
+      b[i] = (__bf16)(seed * (float)(i - tid));
+    }
+    f16_t acc;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) acc[i] = 0.0f;
+    for (int it = 0; it < iters; ++it) {
+#pragma unroll
+      for (int c = 0; c < 4; ++c) acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc, 0, 0, 0);
+    }
+    r += acc[0] + acc[15];
+  }
+  if (wave < 4 && (MODE == 0 || MODE == 2)) {
     bf16x8_t a, b;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
@@ -301,7 +319,7 @@ __global__ void __launch_bounds__(512) pb_mix_kernel(float* out, int iters, floa
 #pragma unroll
     for (int c = 0; c < 4; ++c) r += acc[c][0] + acc[c][15];
   }
-  if (wave >= 4 && MODE != 0) {
+  if (wave >= 4 && (MODE == 1 || MODE == 2 || MODE == 4)) {
     float e[8], f[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
@@ -516,7 +534,7 @@ int pb_valu(int kind, int grid, int iters, float* out, void* stream) {
   return (int)hipGetLastError();
 }
 
-// mode 0, 1 or 2 as for pb_mix_kernel; out: grid * 512 floats.
+// mode 0 to 4 as for pb_mix_kernel; out: grid * 512 floats.
 int pb_mix(int mode, int grid, int iters, float* out, void* stream) {
   hipStream_t s = (hipStream_t)stream;
   if (mode == 0)
@@ -525,6 +543,10 @@ int pb_mix(int mode, int grid, int iters, float* out, void* stream) {
     hipLaunchKernelGGL(pb_mix_kernel<1>, dim3(grid), dim3(512), 0, s, out, iters, 0.01f);
   else if (mode == 2)
     hipLaunchKernelGGL(pb_mix_kernel<2>, dim3(grid), dim3(512), 0, s, out, iters, 0.01f);
+  else if (mode == 3)
+    hipLaunchKernelGGL(pb_mix_kernel<3>, dim3(grid), dim3(512), 0, s, out, iters, 0.01f);
+  else if (mode == 4)
+    hipLaunchKernelGGL(pb_mix_kernel<4>, dim3(grid), dim3(512), 0, s, out, iters, 0.01f);
   else
     return -1;
   return (int)hipGetLastError();
