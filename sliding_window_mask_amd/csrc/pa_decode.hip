@@ -11,13 +11,13 @@
 // their block-table entries (the same review notes that in-window iteration
 // may skip evicted blocks).
 //
-// Kernel 1 (pa_decode_partition): one workgroup of 4 wave64s per
-// (head, partition, sequence). A partition is `partition` consecutive tokens
-// starting at the 16-aligned block that holds the first visible token. The
-// workgroup
+// Kernel 1 (pa_decode_partition): one workgroup of 4 wave64s (8 in launches
+// of under 1024 workgroups) per (head, partition, sequence). A partition is
+// `partition` consecutive tokens starting at the 16-aligned block that holds
+// the first visible token. The workgroup
 //   1. stages q and the partition's block-table entries in LDS;
-//   2. K pass: each wave takes every 4th 16-token block (4 blocks in flight
-//      per wave, non-temporal loads); a block of one head
+//   2. K pass: each of the W waves takes every W-th 16-token block (4 or 8
+//      blocks in flight per wave, non-temporal loads); a block of one head
 //      is 16*D contiguous elements, read with 16-byte loads where lane l reads
 //      bytes [16 l, 16 l + 16) of every 1 KiB slice, so each load instruction
 //      is one fully coalesced 1 KiB segment; a token's row spans LPT lanes,
@@ -192,11 +192,14 @@ __device__ __forceinline__ void store_out(void* out, int64_t idx, float v) {
 // ---------------------------------------------------------------------------
 // BIAS: 0 none, 1 materialised row attn_bias[b, h, :], 2 T5 relative-position
 // bias from a bucket table (a.rel).
-template <int DT, int D, int BIAS, bool SINGLE>
-__global__ void __launch_bounds__(kDecodeThreads)
+// W: waves per workgroup (4, or 8 for launches too small to fill the chip)
+template <int DT, int D, int BIAS, bool SINGLE, int W>
+__global__ void __launch_bounds__(64 * W)
 pa_decode_partition(DecodeArgs a) {
   using G = Geo<DT, D>;
   constexpr int kUnroll = unroll_of<DT, D>();
+  constexpr int kDecodeThreads = 64 * W;   // shadows the 4-wave default
+  constexpr int kDecodeWaves = W;
   const int h = blockIdx.x;
   const int part = blockIdx.y;
   const int b = blockIdx.z;
@@ -225,8 +228,8 @@ pa_decode_partition(DecodeArgs a) {
   //      relative-position bias by distance (BIAS == 2)
   extern __shared__ uint4 smem_u4[];
   uint4* q_lds = smem_u4;                              // [LPT] 16-byte slices
-  float* red_lds = reinterpret_cast<float*>(q_lds + G::kLPT);   // [8]
-  float* o_lds = red_lds + 8;                          // [4][D]
+  float* red_lds = reinterpret_cast<float*>(q_lds + G::kLPT);   // [2 W]
+  float* o_lds = red_lds + 2 * W;                      // [W][D]
   float* s_lds = o_lds + kDecodeWaves * D;             // [P] scores, then weights
   int* tbl_lds = reinterpret_cast<int*>(s_lds + P);    // [P/16] physical ids
   float* rel_lds = reinterpret_cast<float*>(tbl_lds + P / kBlockSize);  // [max_distance + 1]
@@ -344,11 +347,11 @@ pa_decode_partition(DecodeArgs a) {
   }
   sum = wave_sum(sum);
   __syncthreads();                                      // red_lds reuse + s_lds
-  if (lane == 0) red_lds[4 + wave] = sum;
+  if (lane == 0) red_lds[W + wave] = sum;
   __syncthreads();
   float l = 0.0f;
 #pragma unroll
-  for (int w = 0; w < kDecodeWaves; ++w) l += red_lds[4 + w];
+  for (int w = 0; w < kDecodeWaves; ++w) l += red_lds[W + w];
 
   // ---- V pass ----
   float acc[G::kEPL];
@@ -444,25 +447,44 @@ __global__ void __launch_bounds__(D) pa_decode_merge(DecodeArgs a) {
   store_out<DT>(a.out, row * D + tid, den > 0.0f ? num / den : 0.0f);
 }
 
-template <int DT, int D, int BIAS>
-hipError_t launch_typed(const DecodeArgs& a, hipStream_t stream) {
+// Launches of fewer workgroups than this (4 per CU) take 8 waves per
+// workgroup: each (sequence, head) then has twice the blocks in flight, which
+// launches too small to fill the chip need more than occupancy. Measured on
+// T5-small-shaped self-attention (512 workgroups): 10.7 against 11.45 us;
+// at 4096 workgroups (T5-large-shaped) 8 waves lose (62 against 55.5 us).
+// 0 keeps every launch at 4 waves.
+#ifndef PA_DECODE_WIDE_BELOW
+#define PA_DECODE_WIDE_BELOW 1024
+#endif
+
+template <int DT, int D, int BIAS, int W>
+hipError_t launch_waves(const DecodeArgs& a, hipStream_t stream) {
   using G = Geo<DT, D>;
   size_t lds = sizeof(float) * a.partition + sizeof(int) * (a.partition / kBlockSize) +
-               sizeof(float) * (kDecodeWaves * D + 8) + 16 * G::kLPT;
+               sizeof(float) * (W * D + 2 * W) + 16 * G::kLPT;
   if (BIAS == 2) lds += sizeof(float) * (a.rel.max_distance + 1);
   dim3 grid(a.num_heads, a.num_partitions, a.num_seqs);
   if (a.num_partitions == 1) {
-    hipLaunchKernelGGL((pa_decode_partition<DT, D, BIAS, true>), grid, dim3(kDecodeThreads),
-                       lds, stream, a);
+    hipLaunchKernelGGL((pa_decode_partition<DT, D, BIAS, true, W>), grid, dim3(64 * W), lds,
+                       stream, a);
     return hipGetLastError();
   }
-  hipLaunchKernelGGL((pa_decode_partition<DT, D, BIAS, false>), grid, dim3(kDecodeThreads), lds,
+  hipLaunchKernelGGL((pa_decode_partition<DT, D, BIAS, false, W>), grid, dim3(64 * W), lds,
                      stream, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL((pa_decode_merge<DT, D>), dim3((unsigned)a.num_seqs * a.num_heads),
                      dim3(D), 0, stream, a);
   return hipGetLastError();
+}
+
+template <int DT, int D, int BIAS>
+hipError_t launch_typed(const DecodeArgs& a, hipStream_t stream) {
+  if constexpr (PA_DECODE_WIDE_BELOW > 0) {
+    const int64_t wgs = (int64_t)a.num_heads * a.num_partitions * a.num_seqs;
+    if (wgs < PA_DECODE_WIDE_BELOW) return launch_waves<DT, D, BIAS, 8>(a, stream);
+  }
+  return launch_waves<DT, D, BIAS, kDecodeWaves>(a, stream);
 }
 
 template <int DT, int D>
