@@ -207,3 +207,24 @@ def test_kernel_tag():
     assert bench.kernel_tag(K_WIN) == "pa_prefill_f32_64_1_0_false_1"
     assert bench.kernel_tag("void pa::(anonymous namespace)::pa_kv_write<256>(pa::KvWriteArgs)") \
         == "pa_kv_write_256"
+
+
+def test_probe_library_exports_its_entry_points():
+    # bench_probes.so (built by __graft_entry__.build()) backs the probe_*
+    # workloads; every entry point bench.py binds must be exported
+    import ctypes
+    path = os.path.join(ROOT, "bench_probes.so")
+    if not os.path.exists(path):
+        pytest.skip("bench_probes.so not built")
+    lib = ctypes.CDLL(path)
+    for name in ("pb_mfma", "pb_lds", "pb_stream", "pb_gather", "pb_bias", "pb_mix",
+                 "pb_valu", "pb_clock"):
+        assert hasattr(lib, name), name
+
+
+def test_kernel_source_of_window_tags():
+    # counter summaries of single layers are named <workload>_w<W>
+    assert bench.kernel_source_of("prefill_layer_f32_w64") == bench.KERNEL_SOURCE[
+        "prefill_layer_f32"]
+    assert bench.kernel_source_of("prefill_layer_bf16_wfull") == "pa_prefill_bf16.hip"
+    assert bench.kernel_source_of("modernbert_prefill_bf16") == "pa_prefill_bf16.hip"
