@@ -220,11 +220,15 @@ def decode_bytes(lens, H, D, esize, window, with_bias, chunk=0):
     return int(H * np.sum(n_vis * per_tok + 2 * D * esize))
 
 
-def prefill_flops(lens, H, D, window, chunk=0):
-    """Algorithmic flops of a bidirectional prefill layer: 4*D per visible
-    (query, key) pair, every pair of a sequence, |i - j| < W with a window, or
-    pairs inside one chunk of C positions with chunked local attention."""
+def prefill_flops(lens, H, D, window, chunk=0, causal=False):
+    """Algorithmic flops of a prefill layer: 4*D per visible (query, key)
+    pair, every pair of a sequence, |i - j| < W with a window, or pairs inside
+    one chunk of C positions with chunked local attention; causal (without a
+    window or chunks): the pairs j <= i."""
     L = lens.astype(np.int64)
+    if causal:
+        assert window <= 0 and chunk <= 0
+        return int(4 * D * H * np.sum(L * (L + 1) // 2))
     if chunk > 0:
         full, rem = L // chunk, L % chunk
         return int(4 * D * H * np.sum(full * chunk * chunk + rem * rem))
@@ -732,6 +736,17 @@ def bench_prefill(args, dtype_name="f32"):
         "bias_GBps": bias_bytes / (msb * 1e-3) / 1e9,
         "slowdown_vs_no_bias": msb / var["full_attention_layer"]["ms_per_layer"] - 1.0}
     del bias
+    # the same layer under a causal mask (decoder-style prefill: the queries
+    # see the keys at or before their own position)
+    msc = time_steps(lambda: lib.paged_attn_prefill(
+        c.q, c.k_cache, c.v_cache, c.block_tables, c.context_lens, c.query_start_loc, None, -1,
+        True, c.scale, max_seq_len=c.max_seq_len, out=o), args.steps, args.warmup)
+    flc = prefill_flops(c.lens, 12, 64, -1, causal=True)
+    var["causal_layer"] = {
+        "ms_per_layer": msc, "TFLOPs": flc / (msc * 1e-3) / 1e12,
+        "mfma_frac": flc / (msc * 1e-3) / 1e12 / peak,
+        "kernel": "pa_prefill_f32x3_band (causal)" if dtype_name == "f32" else
+                  "pa_prefill_bf16 (16x16x32, causal)"}
     line["variants"] = var
     if not args.no_cpu_baseline:
         step()

@@ -4,9 +4,9 @@ The roofline fields of the benchmark lines rest on two counts: the algorithmic
 bytes of a decode call and the algorithmic flops of a prefill layer. Both are
 compared here with brute-force counts over every (sequence, head, key) or
 (sequence, head, query, key) of small cases, using the visibility rules of the
-decode (the W newest tokens) and of bidirectional prefill (|i - j| < W). The
-counter-summary reader must hand out a value only for the kernel source it was
-measured on.
+decode (the W newest tokens), of bidirectional prefill (|i - j| < W) and of
+causal prefill (j <= i). The counter-summary reader must hand out a value only
+for the kernel source it was measured on.
 """
 import os
 import subprocess
@@ -36,11 +36,13 @@ def brute_decode_bytes(lens, H, D, esize, window, with_bias, chunk=0):
     return total
 
 
-def brute_prefill_flops(lens, H, D, window, chunk=0):
+def brute_prefill_flops(lens, H, D, window, chunk=0, causal=False):
     pairs = 0
     for L in lens:
         for i in range(L):
             for j in range(L):
+                if causal and j > i:
+                    continue
                 if window > 0 and abs(i - j) >= window:
                     continue
                 if chunk > 0 and i // chunk != j // chunk:
@@ -77,6 +79,14 @@ def test_chunked_prefill_flops_match_brute_force(chunk):
     lens = np.array([1, 3, 16, 29, 64, 70, 130], dtype=np.int32)
     got = bench.prefill_flops(lens, 2, 64, -1, chunk=chunk)
     assert got == brute_prefill_flops(lens.tolist(), 2, 64, -1, chunk=chunk)
+
+
+def test_causal_prefill_flops_match_brute_force():
+    lens = np.array([1, 2, 3, 16, 29, 64, 70, 130], dtype=np.int32)
+    got = bench.prefill_flops(lens, 2, 64, -1, causal=True)
+    assert got == brute_prefill_flops(lens.tolist(), 2, 64, -1, causal=True)
+    # about half the bidirectional pairs, plus the diagonal
+    assert 2 * got - bench.prefill_flops(lens, 2, 64, -1) == 4 * 64 * 2 * int(lens.sum())
 
 
 def test_read_traffic_requires_the_measured_source(tmp_path, monkeypatch):
