@@ -30,7 +30,7 @@ Prints ONE JSON line. Options:
                   t5_small_self_decode_bf16 | t5_large_cross_decode_bf16 (calls rotating
                   over input copies > 1 GiB) | kv_write_modernbert_f32 | copy_probe (a plain
                   device copy of known size, for calibrating the rocprofv3 byte counters) |
-                  prefill_layer (one layer: --layer-dtype, --layer-window) |
+                  prefill_layer (one layer: --layer-dtype, --layer-window, --layer-causal) |
                   prefill_window_sweep | probe_mfma | probe_lds | probe_stream |
                   probe_gather | probe_gather_t5 | probe_bias | probe_mix | probe_valu | probe_clock (hardware rates from
                   bench_probes.hip: matrix instructions, LDS reads, a streaming read, the
@@ -83,8 +83,13 @@ KERNEL_SOURCE = {
 
 
 def kernel_source_of(wl):
-    """Kernel sources of a workload; `<workload>_w<W>` names one window of it."""
-    return KERNEL_SOURCE[wl] if wl in KERNEL_SOURCE else KERNEL_SOURCE[wl.rsplit("_w", 1)[0]]
+    """Kernel sources of a workload; `<workload>_w<W>` names one window of it
+    and `<workload>_causal` its causal form."""
+    if wl in KERNEL_SOURCE:
+        return KERNEL_SOURCE[wl]
+    if wl.endswith("_causal"):
+        return kernel_source_of(wl[:-len("_causal")])
+    return KERNEL_SOURCE[wl.rsplit("_w", 1)[0]]
 
 
 def log(msg):
@@ -453,7 +458,8 @@ def bench_decode(args):
                             "GBps": bn / (msn * 1e-3) / 1e9}
         # the same shape with a T5 bias computed in the kernel (32 buckets,
         # max distance 128) instead of the materialised [256, 32, 4096] stream
-        t5_tab = torch.randn(H, 32, device="cuda") * 0.5
+        t5_tab = torch.randn(H, 32, device="cuda",
+                             generator=torch.Generator(device="cuda").manual_seed(5)) * 0.5
         msr = time_steps(lambda: lib.paged_attn_decode_relpos(
             case.q, case.k_cache, case.v_cache, case.block_tables, case.context_lens, t5_tab,
             32, 128, 0, -1, case.scale, max_seq_len=case.max_seq_len, out=out, workspace=ws),
@@ -725,7 +731,8 @@ def bench_prefill(args, dtype_name="f32"):
             var[kind]["bf16_mfma_frac_executed"] = 6 * fl / (msl * 1e-3) / 1e12 / \
                 BF16_MFMA_PEAK_TFLOPS
     c, o = layers[full[0]], outs[full[0]]
-    bias = torch.randn(c.num_seqs, 12, c.max_seq_len, c.max_seq_len, device="cuda")
+    bias = torch.randn(c.num_seqs, 12, c.max_seq_len, c.max_seq_len, device="cuda",
+                       generator=torch.Generator(device="cuda").manual_seed(12))
     msb = time_steps(lambda: run_layer(c, o, bias), args.steps, args.warmup)
     fl = prefill_flops(c.lens, 12, 64, -1)
     bias_bytes = 4 * 12 * int(np.sum(c.lens.astype(np.int64) ** 2))
@@ -746,7 +753,7 @@ def bench_prefill(args, dtype_name="f32"):
         "ms_per_layer": msc, "TFLOPs": flc / (msc * 1e-3) / 1e12,
         "mfma_frac": flc / (msc * 1e-3) / 1e12 / peak,
         "kernel": "pa_prefill_f32x3_band (causal)" if dtype_name == "f32" else
-                  "pa_prefill_bf16 (16x16x32, causal)"}
+                  "pa_prefill_bf16_32 (32x32x16, causal)"}
     line["variants"] = var
     if not args.no_cpu_baseline:
         step()
@@ -812,8 +819,9 @@ def bench_kv_write(args):
     bt = case.block_tables.cpu()
     slots = torch.cat([bt[b, torch.arange(int(L[b])) // 16].long() * 16 +
                        torch.arange(int(L[b])) % 16 for b in range(case.num_seqs)]).to("cuda")
-    kn = torch.randn(T, H, D, device="cuda")
-    vn = torch.randn(T, H, D, device="cuda")
+    gen = torch.Generator(device="cuda").manual_seed(7)
+    kn = torch.randn(T, H, D, device="cuda", generator=gen)
+    vn = torch.randn(T, H, D, device="cuda", generator=gen)
     lib = pa.lib()
     ms = time_steps(lambda: lib.paged_kv_write(case.k_cache, case.v_cache, kn, vn, slots),
                     args.steps, args.warmup)
@@ -853,8 +861,9 @@ def bench_configs(args):
 
 def bench_prefill_layer(args):
     """One ModernBERT-shaped prefill layer (32 sequences, lengths U[64, 1024],
-    12 heads, head_dim 64, no bias) at --layer-window, in --layer-dtype: the
-    unit the counter passes of single layers are taken over."""
+    12 heads, head_dim 64, no bias) at --layer-window, in --layer-dtype,
+    causal with --layer-causal: the unit the counter passes of single layers
+    are taken over."""
     import torch
     import sliding_window_mask_amd as pa
     lib = pa.lib()
@@ -863,14 +872,14 @@ def bench_prefill_layer(args):
     c = modernbert_layers(dt)[0]
     o = torch.empty_like(c.q)
     torch.cuda.synchronize()
-    w = args.layer_window
+    w, causal = args.layer_window, args.layer_causal
     ms = time_steps(lambda: lib.paged_attn_prefill(
         c.q, c.k_cache, c.v_cache, c.block_tables, c.context_lens, c.query_start_loc,
-        None, w, False, c.scale, max_seq_len=c.max_seq_len, out=o), args.steps, args.warmup)
-    fl = prefill_flops(c.lens, 12, 64, w)
+        None, w, causal, c.scale, max_seq_len=c.max_seq_len, out=o), args.steps, args.warmup)
+    fl = prefill_flops(c.lens, 12, 64, w, causal=causal)
     by = prefill_bytes(c.lens, 12, 64, 4 if dn == "f32" else 2)
     return {"metric": "one prefill layer", "workload": "prefill_layer_" + dn,
-            "sliding_window": w, "steps": args.steps, "warmup": args.warmup,
+            "sliding_window": w, "causal": causal, "steps": args.steps, "warmup": args.warmup,
             "launches_per_step": 1, "ms_per_step": ms, "us_per_layer": ms * 1e3,
             "TFLOPs": fl / (ms * 1e-3) / 1e12, "GBps": by / (ms * 1e-3) / 1e9}
 
@@ -1087,7 +1096,8 @@ def bench_probe_bias(args):
     stream = torch.cuda.current_stream().cuda_stream
     c = modernbert_layers(torch.bfloat16)[0]
     H, M = 12, c.max_seq_len
-    bias = torch.randn(c.num_seqs, H, M, M, device="cuda")
+    bias = torch.randn(c.num_seqs, H, M, M, device="cuda",
+                       generator=torch.Generator(device="cuda").manual_seed(13))
     lens = c.context_lens
     out = torch.empty((M // 128) * H * c.num_seqs * 256, dtype=torch.float32, device="cuda")
     torch.cuda.synchronize()
@@ -1473,6 +1483,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--layer-dtype", default="f32", choices=("f32", "bf16"))
     ap.add_argument("--layer-window", type=int, default=-1)
+    ap.add_argument("--layer-causal", action="store_true")
     ap.add_argument("--no-variants", action="store_true")
     ap.add_argument("--no-configs", action="store_true")
     ap.add_argument("--profile-run", action="store_true")

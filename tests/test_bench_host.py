@@ -238,3 +238,4 @@ def test_kernel_source_of_window_tags():
         "prefill_layer_f32"]
     assert bench.kernel_source_of("prefill_layer_bf16_wfull") == "pa_prefill_bf16.hip"
     assert bench.kernel_source_of("modernbert_prefill_bf16") == "pa_prefill_bf16.hip"
+    assert bench.kernel_source_of("prefill_layer_bf16_causal") == "pa_prefill_bf16.hip"

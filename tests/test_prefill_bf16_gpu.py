@@ -82,18 +82,20 @@ def test_prefill_bf16_deterministic():
     assert torch.equal(gpu_prefill(case).view(torch.int16), a.view(torch.int16))
 
 
-@pytest.mark.parametrize("layer", [0, 1])
-def test_modernbert_shaped_bf16_layer_every_sequence(layer):
+@pytest.mark.parametrize("layer,causal", [(0, False), (1, False), (0, True)])
+def test_modernbert_shaped_bf16_layer_every_sequence(layer, causal):
     """A full-attention (0) and a window-64 (1) layer of the bf16 ModernBERT-
-    shaped prefill, as the benchmark launches them, with every one of the 32
-    sequences (all heads and queries) against the oracle."""
-    log("bf16 modernbert-shaped layer %d, all sequences" % layer)
+    shaped prefill, and the full-attention one under a causal mask, as the
+    benchmark launches them, with every one of the 32 sequences (all heads and
+    queries) against the oracle."""
+    log("bf16 modernbert-shaped layer %d causal=%s, all sequences" % (layer, causal))
     case = workloads.prefill_case(4, num_seqs=32, num_heads=12, head_dim=64, lens=(64, 1024),
                                   max_seq_len=1024, dtype=BF,
                                   sliding_window=workloads.modernbert_window(layer),
-                                  device=DEV, layer_seed=[4, layer])
+                                  causal=causal, device=DEV, layer_seed=[4, layer])
     out = gpu_prefill(case)
-    assert_close(out, oracle_prefill(case), BF, "bf16 layer %d all sequences" % layer)
+    assert_close(out, oracle_prefill(case), BF,
+                 "bf16 layer %d causal=%s all sequences" % (layer, causal))
 
 
 @pytest.mark.parametrize("D", [64, 128])
@@ -127,6 +129,26 @@ def test_prefill_bf16_bidirectional_128_query_tiles(D, bias, partial):
     ref = oracle.prefill_relpos(h.q, h.k_cache, h.v_cache, h.block_tables, h.context_lens,
                                 h.query_start_loc, table, nb, md, 1, -1, 0, h.scale, msl)
     assert_close(out, ref, BF, "bf16 128-query tiles relpos D=%d partial=%s" % (D, partial))
+
+
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("partial", [False, True])
+def test_prefill_bf16_causal_128_query_tiles(D, partial):
+    # causal launches without a window or bias at head_dim 64 also run in
+    # workgroups of 128 queries: the workgroup stages keys up to its last row,
+    # each wave stops after the tile holding its own last row and masks only
+    # the tiles crossing its diagonal; query sets that start part-way into the
+    # sequence move the diagonal off the tile grid
+    lens = [1, 31, 32, 33, 97, 127, 128, 129, 160, 255, 257, 300]
+    q_lens = [L for L in lens] if not partial else [1, 30, 1, 32, 96, 1, 127, 128, 33, 200,
+                                                    129, 171]
+    log("bf16 causal 128-query tiles D=%d partial=%s" % (D, partial))
+    case = to_device(workloads.prefill_case(1600 + D + 3 * partial, num_seqs=len(lens),
+                                            num_heads=2, head_dim=D, lens=lens, max_seq_len=304,
+                                            dtype=BF, causal=True, q_lens=q_lens,
+                                            scale=-0.09 if partial else None))
+    assert_close(gpu_prefill(case), oracle_prefill(case), BF,
+                 "bf16 causal 128-query tiles D=%d partial=%s" % (D, partial))
 
 
 def _pack_rows(dense, lens, q_lens):
