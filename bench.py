@@ -754,6 +754,17 @@ def bench_prefill(args, dtype_name="f32"):
         "mfma_frac": flc / (msc * 1e-3) / 1e12 / peak,
         "kernel": "pa_prefill_f32x3_band (causal)" if dtype_name == "f32" else
                   "pa_prefill_bf16_32 (32x32x16, causal)"}
+    # and with the in-kernel T5 bias of a decoder (32 buckets, max distance
+    # 128, one direction): a T5 decoder's prompt
+    t5_tab = torch.randn(12, 32, device="cuda",
+                         generator=torch.Generator(device="cuda").manual_seed(5)) * 0.5
+    mst = time_steps(lambda: lib.paged_attn_prefill_relpos(
+        c.q, c.k_cache, c.v_cache, c.block_tables, c.context_lens, c.query_start_loc, t5_tab,
+        32, 128, 0, -1, True, c.scale, max_seq_len=c.max_seq_len, out=o), args.steps, args.warmup)
+    var["causal_layer_t5_bias"] = {
+        "ms_per_layer": mst, "TFLOPs": flc / (mst * 1e-3) / 1e12,
+        "slowdown_vs_causal_no_bias": mst / msc - 1.0,
+        "t5_bias": "[12, 32] N(0, 0.25) bucket table, unidirectional, max distance 128"}
     line["variants"] = var
     if not args.no_cpu_baseline:
         step()

@@ -17,9 +17,9 @@
 // and multiplier 1.
 //
 // Two kernels share this design. Bidirectional launches without a window,
-// and causal ones without a window or bias at head_dim 64, go to a
-// 32-query-per-wave kernel on v_mfma_f32_32x32x16_bf16 (second half of this
-// file); other causal launches and windowed ones to the kernel below.
+// and causal ones without a window or a materialised bias at head_dim 64, go
+// to a 32-query-per-wave kernel on v_mfma_f32_32x32x16_bf16 (second half of
+// this file); other causal launches and windowed ones to the kernel below.
 //
 // One workgroup per (64-query tile, head, sequence), numbered so that all
 // query tiles of a (sequence, head) share an XCD, longest sequences first
@@ -518,11 +518,13 @@ pa_prefill_bf16(PrefillArgs a) {
 // many queries). Measured on ModernBERT-shaped layers it is 6-9% faster than
 // the kernel above for these launches, and slower for windowed ones (a longer
 // band per workgroup, fewer resident waves), which stay on the kernel above.
-// With CAUSAL (no bias, head_dim 64) it also takes causal launches without a
-// window: the workgroup stages keys up to its last row, each wave stops after
-// the tile holding its own last row and masks only the tiles crossing its
-// diagonal; a ModernBERT-shaped causal layer runs 12% faster than on the
-// kernel above.
+// With CAUSAL (head_dim 64, no bias or the in-kernel T5 bias) it also takes
+// causal launches without a window: the workgroup stages keys up to its last
+// row, each wave stops after the tile holding its own last row and masks only
+// the tiles crossing its diagonal; a ModernBERT-shaped causal layer runs 12%
+// faster than on the kernel above, with or without the T5 bias. A
+// materialised bias stays on the kernel above: the coalesced walk below would
+// read entries past a row's diagonal.
 //
 // Operand layout (32x32x16, lane l, j = l % 32, hh = l / 32; A[i][k] comes
 // from lane i + 32 (k/8) element k%8, B[k][j] from lane j + 32 (k/8) element
@@ -563,7 +565,7 @@ constexpr int min_waves32() { return D == 64 && BIAS == 0 ? 5 : 1; }
 template <int D, int BIAS, bool CAUSAL>
 __global__ void __launch_bounds__(kThreads32, (min_waves32<D, BIAS>()))
 pa_prefill_bf16_32(PrefillArgs a) {
-  static_assert(!CAUSAL || BIAS == 0, "causal launches here carry no bias");
+  static_assert(!CAUSAL || BIAS != 1, "causal launches here carry no materialised bias");
   constexpr int kThreads = kThreads32;
   constexpr int kKRow = D + 8;                 // K row stride in LDS (bf16)
   constexpr int kVRow = D + 32;                // V row stride in LDS (bf16)
@@ -1282,19 +1284,19 @@ pa_prefill_bf16_32p(PrefillArgs a) {
 
 // Bidirectional launches without a window or chunks take the
 // 32-query-per-wave kernel, and so do causal ones without a window, chunks or
-// bias at head_dim 64 (switch below); other causal, windowed and chunked ones
-// the 16-query-per-wave kernel.
+// materialised bias at head_dim 64 (switch below); other causal, windowed and
+// chunked ones the 16-query-per-wave kernel.
 #ifndef PA_PREFILL_BF16_CAUSAL32
 #define PA_PREFILL_BF16_CAUSAL32 1
 #endif
 
 template <int D, int BIAS>
-constexpr bool causal_on_32() { return PA_PREFILL_BF16_CAUSAL32 && D == 64 && BIAS == 0; }
+constexpr bool causal_on_32() { return PA_PREFILL_BF16_CAUSAL32 && D == 64 && BIAS != 1; }
 
 bool wide_tiles(const PrefillArgs& a, int D, int bias) {
   if (a.window > 0 || a.chunk > 0) return false;
   if (!a.causal) return true;
-  return PA_PREFILL_BF16_CAUSAL32 && D == 64 && bias == 0;
+  return PA_PREFILL_BF16_CAUSAL32 && D == 64 && bias != 1;
 }
 
 template <int D, int BIAS>

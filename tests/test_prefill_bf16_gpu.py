@@ -132,23 +132,38 @@ def test_prefill_bf16_bidirectional_128_query_tiles(D, bias, partial):
 
 
 @pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("bias", [None, "relpos"])
 @pytest.mark.parametrize("partial", [False, True])
-def test_prefill_bf16_causal_128_query_tiles(D, partial):
-    # causal launches without a window or bias at head_dim 64 also run in
-    # workgroups of 128 queries: the workgroup stages keys up to its last row,
-    # each wave stops after the tile holding its own last row and masks only
-    # the tiles crossing its diagonal; query sets that start part-way into the
-    # sequence move the diagonal off the tile grid
+def test_prefill_bf16_causal_128_query_tiles(D, bias, partial):
+    # causal launches without a window or a materialised bias at head_dim 64
+    # also run in workgroups of 128 queries: the workgroup stages keys up to
+    # its last row, each wave stops after the tile holding its own last row and
+    # masks only the tiles crossing its diagonal; query sets that start
+    # part-way into the sequence move the diagonal off the tile grid
     lens = [1, 31, 32, 33, 97, 127, 128, 129, 160, 255, 257, 300]
     q_lens = [L for L in lens] if not partial else [1, 30, 1, 32, 96, 1, 127, 128, 33, 200,
                                                     129, 171]
-    log("bf16 causal 128-query tiles D=%d partial=%s" % (D, partial))
+    msl = 304
+    log("bf16 causal 128-query tiles D=%d bias=%s partial=%s" % (D, bias, partial))
     case = to_device(workloads.prefill_case(1600 + D + 3 * partial, num_seqs=len(lens),
-                                            num_heads=2, head_dim=D, lens=lens, max_seq_len=304,
+                                            num_heads=2, head_dim=D, lens=lens, max_seq_len=msl,
                                             dtype=BF, causal=True, q_lens=q_lens,
                                             scale=-0.09 if partial else None))
-    assert_close(gpu_prefill(case), oracle_prefill(case), BF,
-                 "bf16 causal 128-query tiles D=%d partial=%s" % (D, partial))
+    what = "bf16 causal 128-query tiles D=%d bias=%s partial=%s" % (D, bias, partial)
+    if bias is None:
+        assert_close(gpu_prefill(case), oracle_prefill(case), BF, what)
+        return
+    # decoder self-attention buckets (one direction), as a T5 decoder's prompt
+    nb, md = 32, 128
+    table = torch.from_numpy(
+        np.random.default_rng(D + 7).standard_normal((2, nb)).astype(np.float32))
+    out = pa.paged_attn_prefill_relpos(case.q, case.k_cache, case.v_cache, case.block_tables,
+                                       case.context_lens, case.query_start_loc, table.to(DEV),
+                                       nb, md, 0, -1, True, case.scale, max_seq_len=msl)
+    h = to_host(case)
+    ref = oracle.prefill_relpos(h.q, h.k_cache, h.v_cache, h.block_tables, h.context_lens,
+                                h.query_start_loc, table, nb, md, 0, -1, 1, h.scale, msl)
+    assert_close(out, ref, BF, what)
 
 
 def _pack_rows(dense, lens, q_lens):
