@@ -812,12 +812,22 @@ pa_prefill_bf16_32(PrefillArgs a) {
         }
       }
       if constexpr (BIAS == 2) {
+        // the tile's relative positions j - p run from c0 - pw0 - 31 to
+        // c0 + 31 - pw0; all at or beyond the maximum distance on one side
+        // (uniform), they share that side's end bucket (at head_dim 64: at
+        // 128 the branch would cost a resident wave)
+        if (D == 64 && (c0 + kKT - 1 - pw0 <= -rel_md || c0 - pw0 - 31 >= rel_md)) {
+          const float bend = rel_lds[c0 < pw0 ? 0 : 2 * rel_md];
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          const int j0 = c0 + 8 * u + 4 * hh;
+          for (int i = 0; i < 16; ++i) s[i] += bend;
+        } else {
 #pragma unroll
-          for (int r = 0; r < 4; ++r)
-            s[4 * u + r] += rel_lds[min(max(j0 + r - p_row, -rel_md), rel_md) + rel_md];
+          for (int u = 0; u < 4; ++u) {
+            const int j0 = c0 + 8 * u + 4 * hh;
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+              s[4 * u + r] += rel_lds[min(max(j0 + r - p_row, -rel_md), rel_md) + rel_md];
+          }
         }
       }
       if constexpr (CAUSAL) {

@@ -123,6 +123,7 @@ pa_prefill_f32x3(PrefillArgs a) {
   const int p_row = pos0 + t_row;
   const int dq = p_row - 4 * g;
   const int dlo = p_row - L;
+  const int pr0 = pos0 + w_first;   // position of the wave's first row
   const float cs = a.scale_log2;
 
   // q * scale * log2(e) in fp32, split into three bf16 planes: dims
@@ -356,9 +357,19 @@ pa_prefill_f32x3(PrefillArgs a) {
         const int c0 = base + ch * 16;
         const int j0 = c0 + 4 * g;
         if constexpr (BIAS == 2) {
+          // the chunk's relative positions j - p run from c0 - pr0 - 15 to
+          // c0 + 15 - pr0 (pr0: the wave's first row); all at or beyond the
+          // maximum distance on one side (uniform), they share that side's
+          // end bucket
+          if (c0 + 15 - pr0 <= -rel_md || c0 - pr0 - 15 >= rel_md) {
+            const float bend = rel_lds[c0 < pr0 ? 0 : 2 * rel_md];
 #pragma unroll
-          for (int r = 0; r < 4; ++r)
-            s[ch][r] = s[ch][r] + rel_lds[min(max(j0 + r - p_row, -rel_md), rel_md) + rel_md];
+            for (int r = 0; r < 4; ++r) s[ch][r] = s[ch][r] + bend;
+          } else {
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+              s[ch][r] = s[ch][r] + rel_lds[min(max(j0 + r - p_row, -rel_md), rel_md) + rel_md];
+          }
         }
         if (LAST && c0 + 16 > L) {
 #pragma unroll
@@ -523,6 +534,7 @@ pa_prefill_f32x3_band(PrefillArgs a) {
   const bool row_ok = t_row < nq;
   const int p_row = pos0 + t_row;
   const int dq = p_row - 4 * g;
+  const int pr0 = pos0 + w_first;   // position of the wave's first row
   int dlo, dhi;
   if constexpr (BAND == 0) {
     dlo = max(p_row - L, -1);
@@ -751,9 +763,17 @@ pa_prefill_f32x3_band(PrefillArgs a) {
       const int c0 = base + ch * 16;
       const int j0 = c0 + 4 * g;
       if constexpr (BIAS == 2) {
+        // as in the kernel above: one end bucket for a chunk wholly at or
+        // beyond the maximum distance from every row of the wave
+        if (c0 + 15 - pr0 <= -rel_md || c0 - pr0 - 15 >= rel_md) {
+          const float bend = rel_lds[c0 < pr0 ? 0 : 2 * rel_md];
 #pragma unroll
-        for (int r = 0; r < 4; ++r)
-          s[ch][r] = s[ch][r] + rel_lds[min(max(j0 + r - p_row, -rel_md), rel_md) + rel_md];
+          for (int r = 0; r < 4; ++r) s[ch][r] = s[ch][r] + bend;
+        } else {
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            s[ch][r] = s[ch][r] + rel_lds[min(max(j0 + r - p_row, -rel_md), rel_md) + rel_md];
+        }
       }
       if (chunk_whole(c0)) {   // uniform
         if constexpr (BIAS == 1) {

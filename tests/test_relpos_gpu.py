@@ -93,3 +93,34 @@ def test_prefill_relpos(bidir, causal, window):
     dense = table.cpu()[:, torch.from_numpy(buckets.astype(np.int64))]
     dense = dense[None].expand(case.num_seqs, -1, -1, -1).contiguous().to(DEV)
     assert torch.equal(gpu_prefill(case, bias=dense), out)
+
+
+@pytest.mark.parametrize("nb,bidir,causal", [(8, 0, True), (16, 1, False), (16, 1, True)])
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+def test_prefill_relpos_end_bucket_edge(nb, bidir, causal, dtype):
+    # max distance one past the exact buckets (4 per direction here): distance
+    # 4 keeps bucket 4, distance 5 and beyond fall in the end bucket 7, so a
+    # tile the kernels treat as wholly beyond the maximum distance one key too
+    # early changes the result. Query sets starting at positions 3 and 29 put
+    # a wave's first row exactly 4 keys past the end of a 32-key tile (and of
+    # a 16-key chunk), and 4 keys before the start of one; lengths span many
+    # tiles on both sides of each row
+    md = 5
+    case = to_device(workloads.prefill_case(760 + nb + causal, num_seqs=4, num_heads=2,
+                                            head_dim=64, lens=[1, 40, 130, 300],
+                                            q_lens=[1, 37, 101, 263], max_seq_len=304,
+                                            dtype=dtype, causal=causal))
+    table = (torch.randn(2, nb, generator=torch.Generator().manual_seed(nb)) * 2.0).to(DEV)
+    half = nb // 2 if bidir else nb
+    b_in = oracle.t5_bucket(np.array([-(md - 1), -md]), bidir, nb, md)
+    assert b_in[0] != b_in[1] and b_in[1] == half - 1       # the edge is visible
+    out = pa.paged_attn_prefill_relpos(case.q, case.k_cache, case.v_cache, case.block_tables,
+                                       case.context_lens, case.query_start_loc, table, nb, md,
+                                       bidir, -1, causal, case.scale,
+                                       max_seq_len=case.max_seq_len)
+    h = to_host(case)
+    ref = oracle.prefill_relpos(h.q, h.k_cache, h.v_cache, h.block_tables, h.context_lens,
+                                h.query_start_loc, table.cpu(), nb, md, bidir, -1, int(causal),
+                                h.scale, h.max_seq_len)
+    assert_close(out, ref, dtype, "prefill relpos end bucket nb=%d bidir=%d causal=%s %s"
+                 % (nb, bidir, causal, dtype))
