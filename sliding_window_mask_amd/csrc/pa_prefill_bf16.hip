@@ -189,12 +189,18 @@ pa_prefill_bf16(PrefillArgs a) {
 
   __shared__ uint16_t k_lds[2][kKT * kKRow];   // K tile, row-major [key][dim]
   __shared__ uint16_t v_lds[2][kKT * kVRow];   // V tile, row-major [key][dim]
-  __shared__ float rel_lds[BIAS == 2 ? 2 * kMaxRelDistance + 1 : 1];
+  // T5 bias of relative position r = j - p at rel_lds[r + md + 3] for r in
+  // [-md - 3, md + 3]; distances past md repeat the end buckets, so a lane's
+  // four consecutive keys clamp their first distance once and read four
+  // neighbouring entries
+  __shared__ float rel_lds[BIAS == 2 ? 2 * kMaxRelDistance + 7 : 1];
   const int rel_md = BIAS == 2 ? a.rel.max_distance : 0;
   if constexpr (BIAS == 2) {
     const float* head_row = a.rel.table + (int64_t)h * a.rel.num_buckets;
-    for (int i = tid; i <= 2 * rel_md; i += kThreads)
-      rel_lds[i] = bmul == 0.0f ? 0.0f : rel_bias(i - rel_md, a.rel, head_row) * bmul;
+    for (int i = tid; i <= 2 * rel_md + 6; i += kThreads)
+      rel_lds[i] = bmul == 0.0f ? 0.0f
+                                : rel_bias(min(max(i - 3 - rel_md, -rel_md), rel_md), a.rel,
+                                           head_row) * bmul;
   }
 
   const uint16_t* kc = static_cast<const uint16_t*>(a.k_cache);
@@ -403,9 +409,9 @@ pa_prefill_bf16(PrefillArgs a) {
             continue;
           }
           if constexpr (BIAS == 2) {
+            const int e0 = min(max(j0 - p_row[sb], -rel_md - 3), rel_md) + rel_md + 3;
 #pragma unroll
-            for (int r = 0; r < 4; ++r)
-              s[sb][ch][r] += rel_lds[min(max(j0 + r - p_row[sb], -rel_md), rel_md) + rel_md];
+            for (int r = 0; r < 4; ++r) s[sb][ch][r] += rel_lds[e0 + r];
           }
           // per-element mask only where some existing row of the sub-tile
           // does not see the whole chunk; a materialised bias is read only
@@ -627,12 +633,18 @@ pa_prefill_bf16_32(PrefillArgs a) {
 
   __shared__ __attribute__((aligned(16))) uint16_t k_lds[2][kKT * kKRow];
   __shared__ __attribute__((aligned(16))) uint16_t v_lds[2][kKT * kVRow];
-  __shared__ float rel_lds[BIAS == 2 ? 2 * kMaxRelDistance + 1 : 1];
+  // T5 bias of relative position r = j - p at rel_lds[r + md + 3] for r in
+  // [-md - 3, md + 3]; distances past md repeat the end buckets, so a lane's
+  // four consecutive keys clamp their first distance once and read four
+  // neighbouring entries
+  __shared__ float rel_lds[BIAS == 2 ? 2 * kMaxRelDistance + 7 : 1];
   const int rel_md = BIAS == 2 ? a.rel.max_distance : 0;
   if constexpr (BIAS == 2) {
     const float* head_row = a.rel.table + (int64_t)h * a.rel.num_buckets;
-    for (int i = tid; i <= 2 * rel_md; i += kThreads)
-      rel_lds[i] = bmul == 0.0f ? 0.0f : rel_bias(i - rel_md, a.rel, head_row) * bmul;
+    for (int i = tid; i <= 2 * rel_md + 6; i += kThreads)
+      rel_lds[i] = bmul == 0.0f ? 0.0f
+                                : rel_bias(min(max(i - 3 - rel_md, -rel_md), rel_md), a.rel,
+                                           head_row) * bmul;
   }
 
   const uint16_t* kc = static_cast<const uint16_t*>(a.k_cache);
@@ -817,16 +829,15 @@ pa_prefill_bf16_32(PrefillArgs a) {
         // (uniform), they share that side's end bucket (at head_dim 64: at
         // 128 the branch would cost a resident wave)
         if (D == 64 && (c0 + kKT - 1 - pw0 <= -rel_md || c0 - pw0 - 31 >= rel_md)) {
-          const float bend = rel_lds[c0 < pw0 ? 0 : 2 * rel_md];
+          const float bend = rel_lds[c0 < pw0 ? 3 : 2 * rel_md + 3];
 #pragma unroll
           for (int i = 0; i < 16; ++i) s[i] += bend;
         } else {
 #pragma unroll
           for (int u = 0; u < 4; ++u) {
-            const int j0 = c0 + 8 * u + 4 * hh;
+            const int e0 = min(max(c0 + 8 * u + 4 * hh - p_row, -rel_md - 3), rel_md) + rel_md + 3;
 #pragma unroll
-            for (int r = 0; r < 4; ++r)
-              s[4 * u + r] += rel_lds[min(max(j0 + r - p_row, -rel_md), rel_md) + rel_md];
+            for (int r = 0; r < 4; ++r) s[4 * u + r] += rel_lds[e0 + r];
           }
         }
       }

@@ -153,16 +153,19 @@ pa_prefill_f32x3(PrefillArgs a) {
 
   __shared__ __attribute__((aligned(16))) uint16_t k_lds[2][3][kKT * kKRow];
   __shared__ __attribute__((aligned(16))) uint16_t v_lds[2][3][kKT * kVRow];
-  // T5 bias of relative position r = j - p for r in [-max_distance,
-  // max_distance] (longer distances share the end buckets), multiplied by
-  // scale * log2(e) as a materialised bias entry is; gfx950 gives a workgroup
-  // up to 160 KiB of LDS, and two of these workgroups (65 KiB each) fit a CU
-  __shared__ float rel_lds[BIAS == 2 ? 2 * kMaxRelDistance + 1 : 1];
+  // T5 bias of relative position r = j - p at rel_lds[r + md + 3] for r in
+  // [-md - 3, md + 3] (longer distances share the end buckets, so the three
+  // entries past each end repeat them: a lane's four consecutive keys clamp
+  // their first distance once and read four neighbouring entries),
+  // multiplied by scale * log2(e) as a materialised bias entry is; gfx950
+  // gives a workgroup up to 160 KiB of LDS, and two of these workgroups
+  // (65 KiB each) fit a CU
+  __shared__ float rel_lds[BIAS == 2 ? 2 * kMaxRelDistance + 7 : 1];
   const int rel_md = BIAS == 2 ? a.rel.max_distance : 0;
   if constexpr (BIAS == 2) {
     const float* head_row = a.rel.table + (int64_t)h * a.rel.num_buckets;
-    for (int i = tid; i <= 2 * rel_md; i += kThreads)
-      rel_lds[i] = rel_bias(i - rel_md, a.rel, head_row) * cs;
+    for (int i = tid; i <= 2 * rel_md + 6; i += kThreads)
+      rel_lds[i] = rel_bias(min(max(i - 3 - rel_md, -rel_md), rel_md), a.rel, head_row) * cs;
   }
 
   const float* kc = static_cast<const float*>(a.k_cache);
@@ -362,13 +365,13 @@ pa_prefill_f32x3(PrefillArgs a) {
           // maximum distance on one side (uniform), they share that side's
           // end bucket
           if (c0 + 15 - pr0 <= -rel_md || c0 - pr0 - 15 >= rel_md) {
-            const float bend = rel_lds[c0 < pr0 ? 0 : 2 * rel_md];
+            const float bend = rel_lds[c0 < pr0 ? 3 : 2 * rel_md + 3];
 #pragma unroll
             for (int r = 0; r < 4; ++r) s[ch][r] = s[ch][r] + bend;
           } else {
+            const int e0 = min(max(j0 - p_row, -rel_md - 3), rel_md) + rel_md + 3;
 #pragma unroll
-            for (int r = 0; r < 4; ++r)
-              s[ch][r] = s[ch][r] + rel_lds[min(max(j0 + r - p_row, -rel_md), rel_md) + rel_md];
+            for (int r = 0; r < 4; ++r) s[ch][r] = s[ch][r] + rel_lds[e0 + r];
           }
         }
         if (LAST && c0 + 16 > L) {
@@ -601,12 +604,12 @@ pa_prefill_f32x3_band(PrefillArgs a) {
 
   __shared__ __attribute__((aligned(16))) uint16_t k_lds[2][3][kKT * kKRow];
   __shared__ __attribute__((aligned(16))) uint16_t v_lds[2][3][kKT * kVRow];
-  __shared__ float rel_lds[BIAS == 2 ? 2 * kMaxRelDistance + 1 : 1];
+  __shared__ float rel_lds[BIAS == 2 ? 2 * kMaxRelDistance + 7 : 1];   // as above
   const int rel_md = BIAS == 2 ? a.rel.max_distance : 0;
   if constexpr (BIAS == 2) {
     const float* head_row = a.rel.table + (int64_t)h * a.rel.num_buckets;
-    for (int i = tid; i <= 2 * rel_md; i += kThreads)
-      rel_lds[i] = rel_bias(i - rel_md, a.rel, head_row) * cs;
+    for (int i = tid; i <= 2 * rel_md + 6; i += kThreads)
+      rel_lds[i] = rel_bias(min(max(i - 3 - rel_md, -rel_md), rel_md), a.rel, head_row) * cs;
   }
 
   const float* kc = static_cast<const float*>(a.k_cache);
@@ -766,13 +769,13 @@ pa_prefill_f32x3_band(PrefillArgs a) {
         // as in the kernel above: one end bucket for a chunk wholly at or
         // beyond the maximum distance from every row of the wave
         if (c0 + 15 - pr0 <= -rel_md || c0 - pr0 - 15 >= rel_md) {
-          const float bend = rel_lds[c0 < pr0 ? 0 : 2 * rel_md];
+          const float bend = rel_lds[c0 < pr0 ? 3 : 2 * rel_md + 3];
 #pragma unroll
           for (int r = 0; r < 4; ++r) s[ch][r] = s[ch][r] + bend;
         } else {
+          const int e0 = min(max(j0 - p_row, -rel_md - 3), rel_md) + rel_md + 3;
 #pragma unroll
-          for (int r = 0; r < 4; ++r)
-            s[ch][r] = s[ch][r] + rel_lds[min(max(j0 + r - p_row, -rel_md), rel_md) + rel_md];
+          for (int r = 0; r < 4; ++r) s[ch][r] = s[ch][r] + rel_lds[e0 + r];
         }
       }
       if (chunk_whole(c0)) {   // uniform
