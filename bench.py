@@ -742,6 +742,16 @@ def bench_prefill(args, dtype_name="f32"):
                      % (bias_bytes // 4),
         "bias_GBps": bias_bytes / (msb * 1e-3) / 1e9,
         "slowdown_vs_no_bias": msb / var["full_attention_layer"]["ms_per_layer"] - 1.0}
+    # the same bias under a causal mask (a T5 decoder's prompt with a
+    # materialised bias): only the entries j <= i are read
+    mscb = time_steps(lambda: lib.paged_attn_prefill(
+        c.q, c.k_cache, c.v_cache, c.block_tables, c.context_lens, c.query_start_loc, bias, -1,
+        True, c.scale, max_seq_len=c.max_seq_len, out=o), args.steps, args.warmup)
+    cbias_bytes = 4 * 12 * int(np.sum(c.lens.astype(np.int64) * (c.lens + 1) // 2))
+    var["causal_layer_with_bias"] = {
+        "ms_per_layer": mscb,
+        "TFLOPs": prefill_flops(c.lens, 12, 64, -1, causal=True) / (mscb * 1e-3) / 1e12,
+        "bias_GBps": cbias_bytes / (mscb * 1e-3) / 1e9}
     del bias
     # the same layer under a causal mask (decoder-style prefill: the queries
     # see the keys at or before their own position)

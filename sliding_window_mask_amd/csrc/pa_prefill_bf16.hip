@@ -17,9 +17,9 @@
 // and multiplier 1.
 //
 // Two kernels share this design. Bidirectional launches without a window,
-// and causal ones without a window or a materialised bias at head_dim 64, go
-// to a 32-query-per-wave kernel on v_mfma_f32_32x32x16_bf16 (second half of
-// this file); other causal launches and windowed ones to the kernel below.
+// and causal ones without a window at head_dim 64, go to a 32-query-per-wave
+// kernel on v_mfma_f32_32x32x16_bf16 (second half of this file); other causal
+// launches and windowed ones to the kernel below.
 //
 // One workgroup per (64-query tile, head, sequence), numbered so that all
 // query tiles of a (sequence, head) share an XCD, longest sequences first
@@ -524,13 +524,14 @@ pa_prefill_bf16(PrefillArgs a) {
 // many queries). Measured on ModernBERT-shaped layers it is 6-9% faster than
 // the kernel above for these launches, and slower for windowed ones (a longer
 // band per workgroup, fewer resident waves), which stay on the kernel above.
-// With CAUSAL (head_dim 64, no bias or the in-kernel T5 bias) it also takes
-// causal launches without a window: the workgroup stages keys up to its last
-// row, each wave stops after the tile holding its own last row and masks only
-// the tiles crossing its diagonal; a ModernBERT-shaped causal layer runs 12%
-// faster than on the kernel above, with or without the T5 bias. A
-// materialised bias stays on the kernel above: the coalesced walk below would
-// read entries past a row's diagonal.
+// With CAUSAL (head_dim 64) it also takes causal launches without a window:
+// the workgroup stages keys up to its last row, each wave stops after the
+// tile holding its own last row and masks only the tiles crossing its
+// diagonal; a materialised bias is read by the coalesced walk below only on
+// tiles every row of the wave sees whole, and per entry, clamped to the row's
+// own diagonal, on the others. A ModernBERT-shaped causal layer runs 8-12%
+// faster than on the kernel above, with no bias, a T5 bias or a materialised
+// one.
 //
 // Operand layout (32x32x16, lane l, j = l % 32, hh = l / 32; A[i][k] comes
 // from lane i + 32 (k/8) element k%8, B[k][j] from lane j + 32 (k/8) element
@@ -571,7 +572,6 @@ constexpr int min_waves32() { return D == 64 && BIAS == 0 ? 5 : 1; }
 template <int D, int BIAS, bool CAUSAL>
 __global__ void __launch_bounds__(kThreads32, (min_waves32<D, BIAS>()))
 pa_prefill_bf16_32(PrefillArgs a) {
-  static_assert(!CAUSAL || BIAS != 1, "causal launches here carry no materialised bias");
   constexpr int kThreads = kThreads32;
   constexpr int kKRow = D + 8;                 // K row stride in LDS (bf16)
   constexpr int kVRow = D + 32;                // V row stride in LDS (bf16)
@@ -716,8 +716,11 @@ pa_prefill_bf16_32(PrefillArgs a) {
   float lsum = 0.0f;                      // this lane's half of the row sum
   float m_ref = -INFINITY, neg_m = 0.0f;  // running reference (base 2), -m_ref once finite
   const float* bias_row = nullptr;
+  // causal: a row reads entries of keys j <= p_bias only (rows past the
+  // query set read the last query's row, which sees every key below L)
+  const int p_bias = row_ok ? p_row : L - 1;
   if (BIAS == 1) {
-    const int tb_row = row_ok ? t_row : t_first;
+    const int tb_row = row_ok ? t_row : (CAUSAL ? nq - 1 : t_first);
     bias_row = a.bias_start
                    ? a.attn_bias + a.bias_start[b] + ((int64_t)h * nq + tb_row) * L
                    : a.attn_bias +
@@ -727,8 +730,10 @@ pa_prefill_bf16_32(PrefillArgs a) {
   // loads on tiles that lie wholly inside the sequence, if every lane's row
   // is 16-byte aligned (uniform)
   const bf16x2_t one2 = __builtin_bit_cast(bf16x2_t, 0x3f803f80u);
-  // Bias entries of tiles lying wholly inside the sequence are read with
-  // whole 128-byte row segments per 8 lanes: load q of a tile takes rows
+  // Bias entries of tiles lying wholly inside the sequence (causal: and
+  // wholly at or before the wave's first row, so that every row of the wave
+  // sees every key of the tile) are read with whole 128-byte row segments
+  // per 8 lanes: load q of a tile takes rows
   // lane/8 + 8q of the wave's 32 (a row past the last query repeats the
   // last query's row), 16 bytes per lane, one tile ahead; the wave then
   // passes them through its own LDS block (rows padded to 36 floats, so the
@@ -760,7 +765,7 @@ pa_prefill_bf16_32(PrefillArgs a) {
   float4_t bnext[4];
 #pragma unroll
   for (int q = 0; q < 4; ++q) bnext[q] = float4_t{0, 0, 0, 0};
-  if (BIAS == 1 && bias_vec && kKT <= L) {
+  if (BIAS == 1 && bias_vec && kKT <= L && (!CAUSAL || kKT - 1 <= pw0)) {
 #pragma unroll
     for (int q = 0; q < 4; ++q) bnext[q] = *reinterpret_cast<const float4_t*>(bbase + boff[q]);
   }
@@ -781,7 +786,7 @@ pa_prefill_bf16_32(PrefillArgs a) {
     constexpr int buf = decltype(buf_c)::value;
     const int c0 = tk * kKT;
     if (wave_active && (!CAUSAL || c0 <= pw0 + 31)) {
-      const bool bias_whole = bias_vec && c0 + kKT <= L;
+      const bool bias_whole = bias_vec && c0 + kKT <= L && (!CAUSAL || c0 + kKT - 1 <= pw0);
       // ---- S^T for the tile's 32 keys ----
       float16_t s;
 #pragma unroll
@@ -809,7 +814,7 @@ pa_prefill_bf16_32(PrefillArgs a) {
             for (int r = 0; r < 4; ++r) s[4 * u + r] = fmaf(bv[r], bmul, s[4 * u + r]);
           }
           // the next tile's entries, a whole tile of work ahead of their use
-          if (c0 + 2 * kKT <= L) {
+          if (c0 + 2 * kKT <= L && (!CAUSAL || c0 + 2 * kKT - 1 <= pw0)) {
 #pragma unroll
             for (int q = 0; q < 4; ++q)
               bnext[q] = *reinterpret_cast<const float4_t*>(bbase + boff[q] + c0 + kKT);
@@ -820,7 +825,8 @@ pa_prefill_bf16_32(PrefillArgs a) {
 #pragma unroll
             for (int r = 0; r < 4; ++r)
               s[4 * u + r] =
-                  fmaf(bias_row[min(c0 + 8 * u + 4 * hh + r, L - 1)], bmul, s[4 * u + r]);
+                  fmaf(bias_row[min(c0 + 8 * u + 4 * hh + r, CAUSAL ? p_bias : L - 1)], bmul,
+                       s[4 * u + r]);
         }
       }
       if constexpr (BIAS == 2) {
@@ -1304,20 +1310,19 @@ pa_prefill_bf16_32p(PrefillArgs a) {
 }
 
 // Bidirectional launches without a window or chunks take the
-// 32-query-per-wave kernel, and so do causal ones without a window, chunks or
-// materialised bias at head_dim 64 (switch below); other causal, windowed and
-// chunked ones the 16-query-per-wave kernel.
+// 32-query-per-wave kernel, and so do causal ones without a window or chunks
+// at head_dim 64 (switch below); other causal, windowed and chunked ones the
+// 16-query-per-wave kernel.
 #ifndef PA_PREFILL_BF16_CAUSAL32
 #define PA_PREFILL_BF16_CAUSAL32 1
 #endif
 
 template <int D, int BIAS>
-constexpr bool causal_on_32() { return PA_PREFILL_BF16_CAUSAL32 && D == 64 && BIAS != 1; }
+constexpr bool causal_on_32() { return PA_PREFILL_BF16_CAUSAL32 && D == 64; }
 
-bool wide_tiles(const PrefillArgs& a, int D, int bias) {
+bool wide_tiles(const PrefillArgs& a, int D) {
   if (a.window > 0 || a.chunk > 0) return false;
-  if (!a.causal) return true;
-  return PA_PREFILL_BF16_CAUSAL32 && D == 64 && bias != 1;
+  return !a.causal || (PA_PREFILL_BF16_CAUSAL32 && D == 64);
 }
 
 template <int D, int BIAS>
@@ -1347,7 +1352,7 @@ template <int D>
 hipError_t launch_d(PrefillArgs a, hipStream_t stream) {
   const int bias = a.rel.table ? 2 : (a.attn_bias ? 1 : 0);
   // queries per workgroup
-  const int qt = wide_tiles(a, D, bias) ? kQT32 : kQT;
+  const int qt = wide_tiles(a, D) ? kQT32 : kQT;
   a.num_qtiles = (a.max_seq_len + qt - 1) / qt;
   const int64_t pairs = (int64_t)a.num_seqs * a.num_heads;
   const int64_t nwg = (pairs + kXcds - 1) / kXcds * kXcds * a.num_qtiles;

@@ -8,7 +8,8 @@ past a sequence's length are NaN already. The outputs must be finite and
 match the float64 oracle, which itself reads only visible entries (so a mask
 below that poisoned a visible entry would show as a NaN oracle result).
 Padded and ragged layouts, fp32 and bf16 (both bf16 kernels: bidirectional
-launches without a window take the 32-query-per-wave one)."""
+launches without a window, and causal ones without a window at head_dim 64,
+take the 32-query-per-wave one)."""
 import numpy as np
 import pytest
 import torch
@@ -23,7 +24,7 @@ pytestmark = pytest.mark.gpu
 DEV = "cuda"
 
 MASKS = [  # (window, chunk, causal, partial query sets)
-    (-1, 0, False, False), (-1, 0, False, True), (-1, 0, True, True),
+    (-1, 0, False, False), (-1, 0, False, True), (-1, 0, True, False), (-1, 0, True, True),
     (1, 0, False, False), (5, 0, False, True), (16, 0, False, False), (17, 0, True, True),
     (64, 0, False, False), (-1, 8, False, False), (-1, 16, True, True), (-1, 33, False, True),
 ]
