@@ -180,32 +180,34 @@ def _pack_rows(dense, lens, q_lens):
 
 @pytest.mark.parametrize("D", [64, 128])
 @pytest.mark.parametrize("partial", [False, True])
-def test_prefill_bf16_bias_read_paths_agree(D, partial):
-    # bidirectional launches without a window read the bias of whole 32-key
-    # tiles as 128-byte row segments passed between lanes through LDS when
-    # every row is 16-byte aligned, and entry by entry otherwise: a padded
-    # bias with row pitch 320 (aligned), the same values with pitch 306 (not
-    # aligned) and the ragged layout (rows of L entries, aligned or not) must
-    # give bit-identical outputs, and match the oracle
+@pytest.mark.parametrize("causal", [False, True])
+def test_prefill_bf16_bias_read_paths_agree(D, partial, causal):
+    # launches without a window read the bias of whole 32-key tiles (causal:
+    # tiles every row of the wave sees whole) as 128-byte row segments passed
+    # between lanes through LDS when every row is 16-byte aligned, and entry
+    # by entry otherwise: a padded bias with row pitch 320 (aligned), the same
+    # values with pitch 306 (not aligned) and the ragged layout (rows of L
+    # entries, aligned or not) must give bit-identical outputs, and match the
+    # oracle
     lens = [31, 32, 64, 100, 129, 256, 257, 300]
     q_lens = lens if not partial else [1, 32, 33, 99, 2, 200, 129, 300]
-    log("bf16 bias read paths D=%d partial=%s" % (D, partial))
+    what = "bf16 bias read paths D=%d partial=%s causal=%s" % (D, partial, causal)
+    log(what)
     case = to_device(workloads.prefill_case(1600 + D + partial, num_seqs=len(lens), num_heads=2,
                                             head_dim=D, lens=lens, max_seq_len=320, dtype=BF,
-                                            bias="normal", q_lens=q_lens))
+                                            bias="normal", q_lens=q_lens, causal=causal))
     out_a = gpu_prefill(case)
     bias_b = case.attn_bias[:, :, :306, :306].contiguous()
     out_b = pa.paged_attn_prefill(case.q, case.k_cache, case.v_cache, case.block_tables,
-                                  case.context_lens, case.query_start_loc, bias_b, -1, False,
+                                  case.context_lens, case.query_start_loc, bias_b, -1, causal,
                                   case.scale, max_seq_len=306)
     packed, starts = _pack_rows(case.attn_bias.cpu(), case.lens, case.q_lens)
     out_c = pa.paged_attn_prefill_ragged_bias(case.q, case.k_cache, case.v_cache,
                                               case.block_tables, case.context_lens,
                                               case.query_start_loc, packed.to(DEV),
-                                              starts.to(DEV), -1, False, case.scale,
+                                              starts.to(DEV), -1, causal, case.scale,
                                               max_seq_len=320)
     torch.cuda.synchronize()
-    assert_close(out_a, oracle_prefill(case), BF,
-                 "bf16 bias read paths D=%d partial=%s" % (D, partial))
+    assert_close(out_a, oracle_prefill(case), BF, what)
     assert torch.equal(out_a.view(torch.int16), out_b.view(torch.int16))
     assert torch.equal(out_a.view(torch.int16), out_c.view(torch.int16))
