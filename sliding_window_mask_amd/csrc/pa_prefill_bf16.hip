@@ -733,14 +733,15 @@ pa_prefill_bf16_32(PrefillArgs a) {
   // Bias entries of tiles lying wholly inside the sequence (causal: and
   // wholly at or before the wave's first row, so that every row of the wave
   // sees every key of the tile) are read with whole 128-byte row segments
-  // per 8 lanes: load q of a tile takes rows
-  // lane/8 + 8q of the wave's 32 (a row past the last query repeats the
-  // last query's row), 16 bytes per lane, one tile ahead; the wave then
-  // passes them through its own LDS block (rows padded to 36 floats, so the
-  // reads of 16 lanes cover all banks once) to the lanes that own the rows.
-  // Reading a lane's own 4 runs of 4 entries directly would touch 32 rows in
-  // every load instruction, 32 bytes each. The block is the wave's alone and
-  // its LDS operations complete in order, so no barrier is involved.
+  // per 8 lanes: load q of a tile takes rows lane/8 + 8q of the wave's 32 (a
+  // row past the last query repeats the last query's row), 16 bytes per
+  // lane, one tile ahead, as non-temporal loads (each entry is read once,
+  // and whole lines at a time); the wave then passes them through its own
+  // LDS block (rows padded to 36 floats, so the reads of 16 lanes cover all
+  // banks once) to the lanes that own the rows. Reading a lane's own 4 runs
+  // of 4 entries directly would touch 32 rows in every load instruction, 32
+  // bytes each. The block is the wave's alone and its LDS operations
+  // complete in order, so no barrier is involved.
   constexpr int kBRow = 36;
   __shared__ __attribute__((aligned(16))) float b_lds[BIAS == 1 ? (kQT32 / 32) * 32 * kBRow : 4];
   float* bw = &b_lds[BIAS == 1 ? wave * 32 * kBRow : 0];
@@ -767,7 +768,8 @@ pa_prefill_bf16_32(PrefillArgs a) {
   for (int q = 0; q < 4; ++q) bnext[q] = float4_t{0, 0, 0, 0};
   if (BIAS == 1 && bias_vec && kKT <= L && (!CAUSAL || kKT - 1 <= pw0)) {
 #pragma unroll
-    for (int q = 0; q < 4; ++q) bnext[q] = *reinterpret_cast<const float4_t*>(bbase + boff[q]);
+    for (int q = 0; q < 4; ++q)
+      bnext[q] = __builtin_nontemporal_load(reinterpret_cast<const float4_t*>(bbase + boff[q]));
   }
 
   if (ntiles > 0) {
@@ -817,7 +819,8 @@ pa_prefill_bf16_32(PrefillArgs a) {
           if (c0 + 2 * kKT <= L && (!CAUSAL || c0 + 2 * kKT - 1 <= pw0)) {
 #pragma unroll
             for (int q = 0; q < 4; ++q)
-              bnext[q] = *reinterpret_cast<const float4_t*>(bbase + boff[q] + c0 + kKT);
+              bnext[q] = __builtin_nontemporal_load(
+                  reinterpret_cast<const float4_t*>(bbase + boff[q] + c0 + kKT));
           }
         } else {
 #pragma unroll

@@ -259,7 +259,8 @@ pa_prefill_f32x3(PrefillArgs a) {
   };
 
   // a lane's 4 bias entries of each 16-key chunk of a tile, loaded a step
-  // ahead (whole chunks, when the rows are 16-byte aligned)
+  // ahead (whole chunks, when the rows are 16-byte aligned), non-temporal:
+  // each entry is read once
   float4_t bcur[2];
   auto load_bias = [&](int tk) {
 #pragma unroll
@@ -267,7 +268,7 @@ pa_prefill_f32x3(PrefillArgs a) {
       const int c0 = tk * kKT + ch * 16;
       bcur[ch] = float4_t{0, 0, 0, 0};
       if (bias_vec && c0 + 16 <= L)
-        bcur[ch] = *reinterpret_cast<const float4_t*>(bias_row + c0 + 4 * g);
+        bcur[ch] = __builtin_nontemporal_load(reinterpret_cast<const float4_t*>(bias_row + c0 + 4 * g));
     }
   };
 
@@ -674,7 +675,7 @@ pa_prefill_f32x3_band(PrefillArgs a) {
       BIAS == 1 &&
       __builtin_amdgcn_ballot_w64((reinterpret_cast<uintptr_t>(bias_row) & 15) != 0) == 0;
   // a lane's 4 bias entries of each chunk inside every row's range (16-byte
-  // loads, when the rows are 16-byte aligned)
+  // non-temporal loads, when the rows are 16-byte aligned)
   float4_t bcur[2];
   auto load_bias = [&](int tk) {
 #pragma unroll
@@ -682,7 +683,7 @@ pa_prefill_f32x3_band(PrefillArgs a) {
       const int c0 = kstart + tk * kKT + ch * 16;
       bcur[ch] = float4_t{0, 0, 0, 0};
       if (bias_vec && chunk_whole(c0))
-        bcur[ch] = *reinterpret_cast<const float4_t*>(bias_row + c0 + 4 * g);
+        bcur[ch] = __builtin_nontemporal_load(reinterpret_cast<const float4_t*>(bias_row + c0 + 4 * g));
     }
   };
 
