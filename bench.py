@@ -752,6 +752,16 @@ def bench_prefill(args, dtype_name="f32"):
         "ms_per_layer": mscb,
         "TFLOPs": prefill_flops(c.lens, 12, 64, -1, causal=True) / (mscb * 1e-3) / 1e12,
         "bias_GBps": cbias_bytes / (mscb * 1e-3) / 1e9}
+    # a window-64 layer with the same bias (sliding window and bias together):
+    # only the entries |i - j| < 64 are read
+    cw, ow = layers[win[0]], outs[win[0]]
+    mswb = time_steps(lambda: run_layer(cw, ow, bias), args.steps, args.warmup)
+    fw = prefill_flops(cw.lens, 12, 64, cw.sliding_window)
+    wpairs = fw // (4 * 64 * 12)   # visible (query, key) pairs per head
+    var["window_64_layer_with_bias"] = {
+        "ms_per_layer": mswb, "TFLOPs": fw / (mswb * 1e-3) / 1e12,
+        "bias_GBps": 4 * 12 * wpairs / (mswb * 1e-3) / 1e9,
+        "slowdown_vs_no_bias": mswb / var["window_64_layer"]["ms_per_layer"] - 1.0}
     del bias
     # the same layer under a causal mask (decoder-style prefill: the queries
     # see the keys at or before their own position)

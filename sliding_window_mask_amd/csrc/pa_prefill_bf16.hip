@@ -167,6 +167,20 @@ pa_prefill_bf16(PrefillArgs a) {
     }
     if (!row_ok[sb]) dlo[sb] = 0x7fffffff;
   }
+  // the keys [bjlo, bjhi] a row sees (empty for rows past n_q): partly seen
+  // chunks read their bias entries with the key clamped into this range, so
+  // that they can be requested with the whole chunks, before the products,
+  // and still read only visible entries
+  int bjlo[kSub], bjhi[kSub];
+#pragma unroll
+  for (int sb = 0; sb < kSub; ++sb) {
+    bjlo[sb] = 0;
+    bjhi[sb] = -1;
+    if (BIAS == 1 && row_ok[sb]) {
+      bjhi[sb] = p_row[sb] - dlo[sb] - 1;
+      if constexpr (WINDOW) bjlo[sb] = max(p_row[sb] - dhi[sb] + 1, 0);
+    }
+  }
 
   // Q operands: kSteps x 8 bf16 per sub-tile (rows past n_q, and every row
   // under a zero scale, are zero; a negative scale flips the sign bits)
@@ -339,7 +353,9 @@ pa_prefill_bf16(PrefillArgs a) {
           live |= (c0 < wv_hi && c0 + 16 > wv_lo) ? 1 << ch : 0;
         }
       }
-      // bias of the chunks seen whole, requested before the products
+      // bias of the tile's live chunks, requested before the products:
+      // chunks seen whole in one 16-byte load when the rows are aligned,
+      // otherwise entry by entry with the key clamped into the row's range
       float4_t bpre[kSub][2];
       if constexpr (BIAS == 1) {
 #pragma unroll
@@ -347,9 +363,17 @@ pa_prefill_bf16(PrefillArgs a) {
 #pragma unroll
           for (int ch = 0; ch < 2; ++ch) {
             const int c0 = base + ch * 16;
+            const int j0 = c0 + 4 * g;
             bpre[sb][ch] = float4_t{0, 0, 0, 0};
-            if (bias_vec[sb] && ((live >> ch) & 1) && chunk_whole(sb, c0))
-              bpre[sb][ch] = *reinterpret_cast<const float4_t*>(bias_row[sb] + c0 + 4 * g);
+            if ((live >> ch) & 1) {
+              if (bias_vec[sb] && chunk_whole(sb, c0)) {
+                bpre[sb][ch] = *reinterpret_cast<const float4_t*>(bias_row[sb] + j0);
+              } else if (bjlo[sb] <= bjhi[sb]) {
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                  bpre[sb][ch][r] = bias_row[sb][min(max(j0 + r, bjlo[sb]), bjhi[sb])];
+              }
+            }
           }
       }
       // ---- S^T for the two 16-key chunks of every sub-tile ----
@@ -418,15 +442,9 @@ pa_prefill_bf16(PrefillArgs a) {
           // for visible keys
           if (chunk_whole(sb, c0)) {
             if constexpr (BIAS == 1) {
-              if (bias_vec[sb]) {
 #pragma unroll
-                for (int r = 0; r < 4; ++r)
-                  s[sb][ch][r] = fmaf(bpre[sb][ch][r], bmul, s[sb][ch][r]);
-              } else {
-#pragma unroll
-                for (int r = 0; r < 4; ++r)
-                  s[sb][ch][r] = fmaf(bias_row[sb][j0 + r], bmul, s[sb][ch][r]);
-              }
+              for (int r = 0; r < 4; ++r)
+                s[sb][ch][r] = fmaf(bpre[sb][ch][r], bmul, s[sb][ch][r]);
             }
           } else {
             const int d0 = dq[sb] - c0;
@@ -436,9 +454,7 @@ pa_prefill_bf16(PrefillArgs a) {
               bool vis = d > dlo[sb];
               if constexpr (WINDOW) vis = vis && d < dhi[sb];
               if constexpr (BIAS == 1) {
-                float x = -INFINITY;
-                if (vis) x = fmaf(bias_row[sb][j0 + r], bmul, s[sb][ch][r]);
-                s[sb][ch][r] = x;
+                s[sb][ch][r] = vis ? fmaf(bpre[sb][ch][r], bmul, s[sb][ch][r]) : -INFINITY;
               } else {
                 s[sb][ch][r] = vis ? s[sb][ch][r] : -INFINITY;
               }

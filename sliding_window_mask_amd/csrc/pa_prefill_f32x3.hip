@@ -547,6 +547,18 @@ pa_prefill_f32x3_band(PrefillArgs a) {
     prefill_row_bounds(p_row, L, window, chunk, CAUSAL, dlo, dhi);
   }
   if (!row_ok) dlo = 0x7fffffff;
+  // with a window or chunks, the keys [bjlo, bjhi] the row sees (empty for
+  // rows past the query set): chunks some row sees only in part read their
+  // bias entries with the key clamped into this range, so that they are
+  // requested a step ahead with the whole chunks and still only visible
+  // entries are read (causal launches read them when they are used: the
+  // registers held across the step would cost spills there)
+  constexpr bool kEarly = BIAS == 1 && BAND != 0;
+  int bjlo = 0, bjhi = -1;
+  if (kEarly && row_ok) {
+    bjhi = p_row - dlo - 1;
+    bjlo = max(p_row - dhi + 1, 0);
+  }
   const float cs = a.scale_log2;
 
   // keys [lo, hi) the workgroup's rows may see, walked in 32-key tiles from
@@ -674,16 +686,23 @@ pa_prefill_f32x3_band(PrefillArgs a) {
   const bool bias_vec =
       BIAS == 1 &&
       __builtin_amdgcn_ballot_w64((reinterpret_cast<uintptr_t>(bias_row) & 15) != 0) == 0;
-  // a lane's 4 bias entries of each chunk inside every row's range (16-byte
-  // non-temporal loads, when the rows are 16-byte aligned)
+  // a lane's 4 bias entries of each chunk of a tile: chunks inside every
+  // row's range in one 16-byte non-temporal load when the rows are 16-byte
+  // aligned, others (with a window or chunks) entry by entry with the key
+  // clamped into the row's range
   float4_t bcur[2];
   auto load_bias = [&](int tk) {
 #pragma unroll
     for (int ch = 0; ch < 2; ++ch) {
       const int c0 = kstart + tk * kKT + ch * 16;
+      const int j0 = c0 + 4 * g;
       bcur[ch] = float4_t{0, 0, 0, 0};
-      if (bias_vec && chunk_whole(c0))
-        bcur[ch] = __builtin_nontemporal_load(reinterpret_cast<const float4_t*>(bias_row + c0 + 4 * g));
+      if (bias_vec && chunk_whole(c0)) {
+        bcur[ch] = __builtin_nontemporal_load(reinterpret_cast<const float4_t*>(bias_row + j0));
+      } else if (kEarly && chunk_live(c0) && bjlo <= bjhi) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) bcur[ch][r] = bias_row[min(max(j0 + r, bjlo), bjhi)];
+      }
     }
   };
 
@@ -781,7 +800,7 @@ pa_prefill_f32x3_band(PrefillArgs a) {
       }
       if (chunk_whole(c0)) {   // uniform
         if constexpr (BIAS == 1) {
-          if (bias_vec) {
+          if (kEarly || bias_vec) {
 #pragma unroll
             for (int r = 0; r < 4; ++r) s[ch][r] = s[ch][r] + bcur[ch][r] * cs;
           } else {
@@ -797,7 +816,7 @@ pa_prefill_f32x3_band(PrefillArgs a) {
           float x = -INFINITY;
           if (d > dlo && d < dhi) {
             x = s[ch][r];
-            if constexpr (BIAS == 1) x = x + bias_row[j0 + r] * cs;
+            if constexpr (BIAS == 1) x = x + (kEarly ? bcur[ch][r] : bias_row[j0 + r]) * cs;
           }
           s[ch][r] = x;
         }
