@@ -917,29 +917,41 @@ def bench_prefill_layer(args):
 
 def bench_prefill_window_sweep(args):
     """One ModernBERT-shaped layer (32 sequences, lengths U[64, 1024], 12
-    heads, head_dim 64, no bias) through the product prefill call at a range
-    of sliding windows, in both dtypes."""
+    heads, head_dim 64) through the product prefill call at a range of
+    sliding windows, in both dtypes, without a bias and with a materialised
+    fp32 bias [32, 12, 1024, 1024] N(0, 1) (its visible entries read)."""
     import torch
     import sliding_window_mask_amd as pa
     lib = pa.lib()
     rows = []
+    bias = None
     for dtype_name, dtype, esize in (("f32", torch.float32, 4), ("bf16", torch.bfloat16, 2)):
         c = modernbert_layers(dtype)[0]
         o = torch.empty_like(c.q)
+        if bias is None:
+            bias = torch.randn(c.num_seqs, 12, c.max_seq_len, c.max_seq_len, device="cuda",
+                               generator=torch.Generator(device="cuda").manual_seed(12))
         torch.cuda.synchronize()
         by = prefill_bytes(c.lens, 12, 64, esize)
         for w in (1, 16, 32, 64, 128, 256, 512, -1):
-            msl = time_steps(lambda: lib.paged_attn_prefill(
-                c.q, c.k_cache, c.v_cache, c.block_tables, c.context_lens, c.query_start_loc,
-                None, w, False, c.scale, max_seq_len=c.max_seq_len, out=o),
-                args.steps, args.warmup)
             fl = prefill_flops(c.lens, 12, 64, w)
-            rows.append({"dtype": dtype_name, "sliding_window": w, "us_per_layer": msl * 1e3,
-                         "TFLOPs": fl / (msl * 1e-3) / 1e12,
-                         "GBps": by / (msl * 1e-3) / 1e9})
+            row = {"dtype": dtype_name, "sliding_window": w}
+            for tag, bb in (("", None), ("_with_bias", bias)):
+                msl = time_steps(lambda: lib.paged_attn_prefill(
+                    c.q, c.k_cache, c.v_cache, c.block_tables, c.context_lens,
+                    c.query_start_loc, bb, w, False, c.scale, max_seq_len=c.max_seq_len, out=o),
+                    args.steps, args.warmup)
+                row["us_per_layer" + tag] = msl * 1e3
+                row["TFLOPs" + tag] = fl / (msl * 1e-3) / 1e12
+            row["GBps"] = by / (row["us_per_layer"] * 1e-6) / 1e9
+            # visible bias entries: one per visible (query, key) pair and head
+            row["bias_GBps"] = fl // (4 * 64) * 4 / (row["us_per_layer_with_bias"] * 1e-6) / 1e9
+            rows.append(row)
+        del c, o
     return {"metric": "prefill layer time by sliding window", "rows": rows,
             "note": "one layer of the 12-layer ModernBERT-shaped step; GBps counts q, K, V "
-                    "read once and the output written once"}
+                    "read once and the output written once; bias_GBps the visible bias "
+                    "entries over the biased layer's time"}
 
 
 # ----------------------------------------------------------------------------
