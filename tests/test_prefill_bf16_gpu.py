@@ -82,20 +82,23 @@ def test_prefill_bf16_deterministic():
     assert torch.equal(gpu_prefill(case).view(torch.int16), a.view(torch.int16))
 
 
-@pytest.mark.parametrize("layer,causal", [(0, False), (1, False), (0, True)])
-def test_modernbert_shaped_bf16_layer_every_sequence(layer, causal):
+@pytest.mark.parametrize("layer,causal,bias", [(0, False, None), (1, False, None),
+                                               (0, True, None), (0, False, "normal"),
+                                               (0, True, "normal"), (1, False, "normal")])
+def test_modernbert_shaped_bf16_layer_every_sequence(layer, causal, bias):
     """A full-attention (0) and a window-64 (1) layer of the bf16 ModernBERT-
-    shaped prefill, and the full-attention one under a causal mask, as the
-    benchmark launches them, with every one of the 32 sequences (all heads and
-    queries) against the oracle."""
-    log("bf16 modernbert-shaped layer %d causal=%s, all sequences" % (layer, causal))
+    shaped prefill, the full-attention one under a causal mask, and each with
+    a materialised fp32 bias [32, 12, 1024, 1024], as the benchmark launches
+    them, with every one of the 32 sequences (all heads and queries) against
+    the oracle."""
+    what = "bf16 layer %d causal=%s bias=%s all sequences" % (layer, causal, bias)
+    log(what)
     case = workloads.prefill_case(4, num_seqs=32, num_heads=12, head_dim=64, lens=(64, 1024),
-                                  max_seq_len=1024, dtype=BF,
+                                  max_seq_len=1024, dtype=BF, bias=bias,
                                   sliding_window=workloads.modernbert_window(layer),
                                   causal=causal, device=DEV, layer_seed=[4, layer])
     out = gpu_prefill(case)
-    assert_close(out, oracle_prefill(case), BF,
-                 "bf16 layer %d causal=%s all sequences" % (layer, causal))
+    assert_close(out, oracle_prefill(case), BF, what)
 
 
 @pytest.mark.parametrize("D", [64, 128])

@@ -140,6 +140,20 @@ def test_modernbert_prefill_layer_every_sequence(layer):
     assert_close(out, ref, torch.float32, "layer %d all sequences" % layer)
 
 
+@pytest.mark.parametrize("layer,causal", [(0, False), (0, True), (1, False)])
+def test_modernbert_prefill_layer_with_bias_every_sequence(layer, causal):
+    """The same layers with a materialised fp32 bias [32, 12, 1024, 1024]
+    (and the full-attention one also under a causal mask), as the benchmark's
+    biased variants launch them: every sequence against the oracle."""
+    what = "layer %d causal=%s with bias, all sequences" % (layer, causal)
+    log(what)
+    case = workloads.prefill_case(4, num_seqs=32, num_heads=12, head_dim=64, lens=(64, 1024),
+                                  max_seq_len=1024, dtype=torch.float32, bias="normal",
+                                  sliding_window=workloads.modernbert_window(layer),
+                                  causal=causal, device=DEV, layer_seed=[4, layer])
+    assert_close(gpu_prefill(case), oracle_prefill(case), torch.float32, what)
+
+
 def fp32_reference(h, window, chunk, causal):
     """The same attention in plain fp32 on the CPU (torch), from host copies:
     K/V gathered through the block table, scores (q.k) * scale with the
