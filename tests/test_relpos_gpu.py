@@ -124,3 +124,28 @@ def test_prefill_relpos_end_bucket_edge(nb, bidir, causal, dtype):
                                 h.scale, h.max_seq_len)
     assert_close(out, ref, dtype, "prefill relpos end bucket nb=%d bidir=%d causal=%s %s"
                  % (nb, bidir, causal, dtype))
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+@pytest.mark.parametrize("bidir,causal,window", [(1, False, -1), (0, True, -1), (1, False, 64)])
+def test_prefill_relpos_full_size_every_sequence(dtype, bidir, causal, window):
+    # the ModernBERT-shaped layer (32 sequences of U[64, 1024] tokens, 12
+    # heads, head_dim 64) with a T5 bias of 32 buckets and maximum distance
+    # 128 as the benchmark times it: encoder buckets (bidirectional, with and
+    # without a 64-token window) and decoder buckets (causal); every sequence
+    # against the oracle
+    what = "full-size relpos %s bidir=%d causal=%s W=%d" % (dtype, bidir, causal, window)
+    log(what)
+    case = workloads.prefill_case(4, num_seqs=32, num_heads=12, head_dim=64, lens=(64, 1024),
+                                  max_seq_len=1024, dtype=dtype, sliding_window=window,
+                                  causal=causal, device=DEV, layer_seed=[4, 0])
+    table = (torch.randn(12, 32, generator=torch.Generator().manual_seed(5)) * 0.5).to(DEV)
+    out = pa.paged_attn_prefill_relpos(case.q, case.k_cache, case.v_cache, case.block_tables,
+                                       case.context_lens, case.query_start_loc, table, 32, 128,
+                                       bidir, window, causal, case.scale,
+                                       max_seq_len=case.max_seq_len)
+    h = to_host(case)
+    ref = oracle.prefill_relpos(h.q, h.k_cache, h.v_cache, h.block_tables, h.context_lens,
+                                h.query_start_loc, table.cpu(), 32, 128, bidir, window,
+                                int(causal), h.scale, h.max_seq_len)
+    assert_close(out, ref, dtype, what)
